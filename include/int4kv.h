@@ -1,0 +1,154 @@
+/*
+ * int4kv: INT4 per-token-head paged KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI.  Pointers are DEVICE pointers unless marked "host".  `stream`
+ * is a hipStream_t passed as void* (NULL = the legacy null stream).  Every call
+ * validates its host-side arguments first and returns a status without
+ * enqueuing anything when they are invalid; on success the work is enqueued on
+ * `stream` and the call returns at once (no synchronisation).  The library
+ * allocates no memory and keeps no global mutable state apart from a
+ * thread-local error string, so it is re-entrant; buffers are owned by the
+ * caller.  Device-resident metadata (slot numbers, block ids, lengths) is the
+ * caller's contract and is not checked: out-of-range values there are
+ * undefined behaviour.
+ *
+ * Citations name the page and the section that defines each operation:
+ *   [report]   PR #40835 report: "[Feature] Triton INT4 per-token-head KV cache
+ *              quantization" (prhub.com.cn)
+ *   [pr40633]  vLLM Pull Request #40633: "[Feature] Triton INT4 / INT2
+ *              per-token-head KV cache quantization"
+ *   [testfile] tests/quantization/test_per_token_kv_cache.py (vLLM fork page),
+ *              by its numbered sections.
+ *
+ * Cache layout ([report], key snippets: get_kv_cache_shape):
+ *   uint8 [num_blocks][2][block_size][num_kv_heads][R],  R = head_size/2 + 4.
+ *   Index 0 of dim 1 holds K rows, index 1 holds V rows.  A row holds the
+ *   head_size 4-bit codes of one (token, head), two per byte with the even
+ *   element in the low nibble ([testfile] §2 and §6), followed by one
+ *   little-endian fp32 scale word whose low 4 mantissa bits carry the zero
+ *   point ([pr40633] description; [testfile] §6 steganography step).
+ *   Rows are 4-byte aligned; the cache base must be 16-byte aligned.
+ */
+#ifndef INT4KV_H_
+#define INT4KV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  INT4KV_OK = 0,
+  INT4KV_ERR_INVALID_ARG = 1, /* a host argument is out of range or inconsistent */
+  INT4KV_ERR_UNSUPPORTED = 2, /* valid but not implemented (head size, block size, GQA ratio) */
+  INT4KV_ERR_WORKSPACE = 3,   /* split-K requested without segment buffers */
+  INT4KV_ERR_LAUNCH = 4       /* the HIP runtime reported an error at launch */
+} int4kv_status_t;
+
+typedef enum { INT4KV_F16 = 0, INT4KV_BF16 = 1 } int4kv_dtype_t;
+
+/* Bytes of a cache of the given shape, or -1 if a dimension is < 1 or
+ * head_size is odd.  R = head_size/2 + 4 bytes per (token, head, K|V) row. */
+int64_t int4kv_cache_bytes(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_size);
+
+/*
+ * int4_kv_write: quantize and store K and V of `num_tokens` tokens.
+ * ([report] implementation breakdown, item 2 and item 4: the INT4 write
+ *  kernel; [pr40633] description: random Hadamard pre-rotation, asymmetric
+ *  16-level quantization with one fp32 scale per (token, head) and the zero
+ *  point hidden in the scale; [testfile] §4: negative slots are skipped.)
+ *
+ * For each token t with slot = slot_mapping[t] >= 0 and each KV head h, for
+ * K (kv = 0) and V (kv = 1):
+ *   x = input row (converted exactly to fp32); y = H (signs * x), the
+ *   unnormalised Walsh-Hadamard transform in natural order, evaluated in fp32
+ *   as butterflies of span 1, 2, 4, ..., d/2;
+ *   s = max(fl((max y - min y) / 15), 1e-6f); s_t = s with its low 4 bits
+ *   cleared; inv = fl(1 / s_t); zp = clamp(rint(-min y * inv), 0, 15);
+ *   code_i = clamp(rint(fl(y_i * inv) + zp), 0, 15);
+ *   row bytes j = code_{2j} | code_{2j+1} << 4; scale word = bits(s_t) | zp;
+ *   the row goes to block slot / block_size, offset slot % block_size.
+ * The result is bit-for-bit reproducible (no FMA contraction, no flush to zero).
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_size] of `dtype`; the
+ *                     token stride (in elements) is given; heads are
+ *                     contiguous.  Base 16-byte aligned, stride a multiple of 8.
+ *   slot_mapping      int64 [num_tokens]; slot < 0 leaves the cache untouched.
+ *   kv_cache          the packed cache (layout above), written in place.
+ *   rht_signs         fp32 [head_size], each exactly +1.0f or -1.0f.
+ * Supported: head_size 64 or 128, block_size 16.  num_tokens == 0 is a no-op.
+ * Slots of one call must be distinct (two tokens to one slot race).
+ */
+int4kv_status_t int4_kv_write(const void* key, int64_t key_token_stride, const void* value,
+                              int64_t value_token_stride, int4kv_dtype_t dtype,
+                              const int64_t* slot_mapping, int32_t num_tokens, uint8_t* kv_cache,
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_size, const float* rht_signs, void* stream);
+
+/*
+ * int4_paged_attention: causal attention of a varlen batch of queries over
+ * the packed cache.
+ * ([report] implementation breakdown, item 2 and item 5: the INT4 read
+ *  kernel behind unified_attention, and risks: causal attention only;
+ *  [pr40633] description: Q split into interleaved streams matching the
+ *  nibble order, split-dot score with a sum(Q)*zp correction, per-stream
+ *  accumulators, online softmax and segment reduction shared with the common
+ *  kernel; [testfile] §6: argument list of unified_attention.)
+ *
+ * Sequence b has q_len_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] query rows and
+ * L_b = seqused_k[b] keys (its new tokens included).  Query row i sits at
+ * position L_b - q_len_b + i and attends to keys [0, that position].  Query
+ * head g reads KV head g / (num_q_heads / num_kv_heads).  Key j of sequence b
+ * is row (j % block_size) of block block_table[b * block_table_stride +
+ * j / block_size].  The result equals softmax(softmax_scale * q . k_hat) . v_hat,
+ * where k_hat, v_hat are the dequantised, inverse-rotated cache rows
+ * (signs * H ((code - zp) * s_t) / head_size); internally the score is taken
+ * in the rotated domain and the output rotated back.  fp32 accumulation;
+ * `out` has the dtype of q.
+ *
+ *   q                 [Tq, num_q_heads, head_size], token stride given (elements,
+ *                     multiple of 8), heads contiguous, 16-byte aligned base.
+ *   out               [Tq, num_q_heads, head_size] contiguous, same dtype as q.
+ *   cu_seqlens_q      int32 [num_seqs + 1];  seqused_k int32 [num_seqs].
+ *   max_seqlen_q      host: max q_len_b.  1 selects the decode path, which
+ *                     may split each sequence's keys into `num_segments`
+ *                     segments of whole blocks (ceil(ceil(L_b/16)/NS) blocks
+ *                     each) merged by a reduction pass.  > 1 selects the
+ *                     prefill/mixed path (no split-K; segments ignored).
+ *   max_seqlen_k      host: >= every L_b.
+ *   block_table       int32 [num_seqs, block_table_stride], entries < num_blocks.
+ *   rht_signs         fp32 [head_size], the signs used by int4_kv_write.
+ *   num_segments      >= 1.  When > 1 on the decode path, segm_output fp32
+ *                     [num_seqs, num_q_heads, num_segments, head_size],
+ *                     segm_max and segm_expsum fp32 [num_seqs, num_q_heads,
+ *                     num_segments] are required scratch (contents on return
+ *                     unspecified: per-segment accumulator, running maximum in
+ *                     base-2 logit units, and exp-sum).
+ * Supported: head_size 64 or 128, block_size 16, num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8, 16}.  A sequence with L_b == 0 gets zero output rows.
+ */
+int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void* out,
+                                     int4kv_dtype_t dtype, const uint8_t* kv_cache,
+                                     int32_t num_blocks, int32_t block_size,
+                                     int32_t num_kv_heads, int32_t head_size,
+                                     int32_t num_q_heads, const int32_t* cu_seqlens_q,
+                                     const int32_t* seqused_k, int32_t num_seqs,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     const int32_t* block_table, int32_t block_table_stride,
+                                     float softmax_scale, const float* rht_signs,
+                                     int32_t num_segments, float* segm_output, float* segm_max,
+                                     float* segm_expsum, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* int4kv_status_string(int4kv_status_t s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* int4kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT4KV_H_ */

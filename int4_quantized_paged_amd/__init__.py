@@ -1,0 +1,179 @@
+"""INT4 per-token-head paged KV cache on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI of ``include/int4kv.h``.  It only marshals
+arguments (device pointers, sizes, the current HIP stream); every step of the
+write and the attention runs in the HIP kernels of ``libint4kv.so``.  If the
+library is missing, every call raises: there is no CPU fallback.
+
+Exports the C entry points under the same names:
+    int4_kv_write(...)          quantize + pack K/V rows into the paged cache
+    int4_paged_attention(...)   causal attention over the packed cache
+plus small helpers to size and allocate the buffers those calls take.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "int4_kv_write", "int4_paged_attention", "int4kv_cache_bytes", "int4kv_status_string",
+    "int4kv_last_error", "Int4KVError", "cache_shape", "empty_cache", "segment_buffers",
+    "library_path", "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libint4kv.so")
+_lib = None
+
+INT4KV_F16, INT4KV_BF16 = 0, 1
+_STATUS = {0: "INT4KV_OK", 1: "INT4KV_ERR_INVALID_ARG", 2: "INT4KV_ERR_UNSUPPORTED",
+           3: "INT4KV_ERR_WORKSPACE", 4: "INT4KV_ERR_LAUNCH"}
+
+
+class Int4KVError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libint4kv.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                           "(run python -m int4_quantized_paged_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.int4kv_cache_bytes.argtypes = [i32, i32, i32, i32]
+    lib.int4kv_cache_bytes.restype = i64
+    lib.int4kv_status_string.argtypes = [ctypes.c_int]
+    lib.int4kv_status_string.restype = ctypes.c_char_p
+    lib.int4kv_last_error.argtypes = []
+    lib.int4kv_last_error.restype = ctypes.c_char_p
+    lib.int4_kv_write.argtypes = [P, i64, P, i64, ctypes.c_int, P, i32, P, i32, i32, i32, i32, P, P]
+    lib.int4_kv_write.restype = ctypes.c_int
+    lib.int4_paged_attention.argtypes = [P, i64, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P, P,
+                                         i32, i32, i32, P, i32, ctypes.c_float, P, i32, P, P, P, P]
+    lib.int4_paged_attention.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float16:
+        return INT4KV_F16
+    if dt == torch.bfloat16:
+        return INT4KV_BF16
+    raise TypeError(f"unsupported dtype {dt}: float16 or bfloat16")
+
+
+def _check(status: int):
+    if status != 0:
+        raise Int4KVError(status, load_library().int4kv_last_error().decode())
+
+
+def int4kv_cache_bytes(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int) -> int:
+    return int(load_library().int4kv_cache_bytes(num_blocks, block_size, num_kv_heads, head_size))
+
+
+def int4kv_status_string(status: int) -> str:
+    return load_library().int4kv_status_string(status).decode()
+
+
+def int4kv_last_error() -> str:
+    return load_library().int4kv_last_error().decode()
+
+
+def cache_shape(num_blocks: int, num_kv_heads: int, head_size: int, block_size: int = 16):
+    """[num_blocks, 2, block_size, num_kv_heads, head_size/2 + 4] uint8."""
+    return (num_blocks, 2, block_size, num_kv_heads, head_size // 2 + 4)
+
+
+def empty_cache(num_blocks: int, num_kv_heads: int, head_size: int, device="cuda",
+                block_size: int = 16) -> torch.Tensor:
+    return torch.empty(cache_shape(num_blocks, num_kv_heads, head_size, block_size),
+                       dtype=torch.uint8, device=device)
+
+
+def segment_buffers(num_seqs: int, num_q_heads: int, num_segments: int, head_size: int,
+                    device="cuda"):
+    """Split-K scratch: (output [S, Hq, NS, d], max [S, Hq, NS], expsum [S, Hq, NS]) fp32."""
+    o = torch.empty((num_seqs, num_q_heads, num_segments, head_size), dtype=torch.float32,
+                    device=device)
+    m = torch.empty((num_seqs, num_q_heads, num_segments), dtype=torch.float32, device=device)
+    s = torch.empty((num_seqs, num_q_heads, num_segments), dtype=torch.float32, device=device)
+    return o, m, s
+
+
+def int4_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                  kv_cache: torch.Tensor, rht_signs: torch.Tensor) -> None:
+    """Quantize and store ``key``/``value`` [T, Hkv, d] at ``slot_mapping`` (int64 [T]).
+
+    ``kv_cache`` is uint8 [num_blocks, 2, block_size, Hkv, d/2 + 4] on the same
+    device; ``rht_signs`` fp32 [d] of +-1.  Enqueued on the current stream."""
+    lib = load_library()
+    T = key.shape[0]
+    if key.dim() != 3 or value.shape != key.shape or key.dtype != value.dtype:
+        raise ValueError("key and value must both be [T, Hkv, d] of one dtype")
+    if key.stride(2) != 1 or key.stride(1) != key.shape[2] or value.stride(2) != 1 or \
+            value.stride(1) != value.shape[2]:
+        raise ValueError("key/value heads must be contiguous ([T, Hkv, d] with a token stride)")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 5 or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous uint8 [NB, 2, B, Hkv, d/2+4] tensor")
+    nb, two, bs, hkv, _ = kv_cache.shape
+    signs = rht_signs.contiguous()
+    _check(lib.int4_kv_write(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
+                             _dtype_code(key.dtype), _ptr(slot_mapping.contiguous()), T,
+                             _ptr(kv_cache), nb, bs, hkv, key.shape[2], _ptr(signs),
+                             _stream(key.device)))
+
+
+def int4_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         seqused_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                         block_table: torch.Tensor, softmax_scale: float,
+                         rht_signs: torch.Tensor, out: torch.Tensor | None = None,
+                         num_segments: int = 1, segm_output: torch.Tensor | None = None,
+                         segm_max: torch.Tensor | None = None,
+                         segm_expsum: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal attention of ``q`` [Tq, Hq, d] over the packed cache; returns ``out``."""
+    lib = load_library()
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [Tq, Hq, d] with contiguous heads")
+    Tq, hq, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, hq, d), dtype=q.dtype, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous with q's shape and dtype")
+    nb, two, bs, hkv, _ = kv_cache.shape
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k),
+                    ("block_table", block_table)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [S, max_blocks] with unit column stride")
+    S = seqused_k.shape[0]
+    _check(lib.int4_paged_attention(
+        _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype), _ptr(kv_cache), nb, bs, hkv, d, hq,
+        _ptr(cu_seqlens_q.contiguous()), _ptr(seqused_k.contiguous()), S, int(max_seqlen_q),
+        int(max_seqlen_k), _ptr(block_table), block_table.stride(0), float(softmax_scale),
+        _ptr(rht_signs.contiguous()), int(num_segments), _ptr(segm_output), _ptr(segm_max),
+        _ptr(segm_expsum), _stream(q.device)))
+    return out

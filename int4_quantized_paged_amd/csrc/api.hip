@@ -1,0 +1,154 @@
+// C ABI of the INT4 paged KV-cache library: argument validation and dispatch.
+// Every host-checkable problem is reported before anything is enqueued.
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+
+#include "../../include/int4kv.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int4kv_status_t fail(int4kv_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+int4kv_status_t ok() {
+  g_last_error[0] = '\0';
+  return INT4KV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int4kv_status_t check_common(const void* cache, int32_t num_blocks, int32_t block_size,
+                             int32_t num_kv_heads, int32_t head_size, const float* signs) {
+  if (!cache || !signs) return fail(INT4KV_ERR_INVALID_ARG, "null cache or rht_signs pointer");
+  if (num_blocks < 1 || num_kv_heads < 1)
+    return fail(INT4KV_ERR_INVALID_ARG, "num_blocks (%d) and num_kv_heads (%d) must be >= 1",
+                num_blocks, num_kv_heads);
+  if (head_size != 64 && head_size != 128)
+    return fail(INT4KV_ERR_UNSUPPORTED, "head_size %d: supported sizes are 64 and 128", head_size);
+  if (block_size != 16)
+    return fail(INT4KV_ERR_UNSUPPORTED, "block_size %d: only 16 is supported", block_size);
+  if (!aligned16(cache) || !aligned16(signs))
+    return fail(INT4KV_ERR_INVALID_ARG, "cache and rht_signs must be 16-byte aligned");
+  return INT4KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t int4kv_cache_bytes(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_size) {
+  if (num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_size < 2 || (head_size & 1))
+    return -1;
+  return (int64_t)num_blocks * 2 * block_size * num_kv_heads * (head_size / 2 + 4);
+}
+
+const char* int4kv_status_string(int4kv_status_t s) {
+  switch (s) {
+    case INT4KV_OK: return "INT4KV_OK";
+    case INT4KV_ERR_INVALID_ARG: return "INT4KV_ERR_INVALID_ARG";
+    case INT4KV_ERR_UNSUPPORTED: return "INT4KV_ERR_UNSUPPORTED";
+    case INT4KV_ERR_WORKSPACE: return "INT4KV_ERR_WORKSPACE";
+    case INT4KV_ERR_LAUNCH: return "INT4KV_ERR_LAUNCH";
+  }
+  return "INT4KV_ERR_UNKNOWN";
+}
+
+const char* int4kv_last_error(void) { return g_last_error; }
+
+int4kv_status_t int4_kv_write(const void* key, int64_t key_token_stride, const void* value,
+                              int64_t value_token_stride, int4kv_dtype_t dtype,
+                              const int64_t* slot_mapping, int32_t num_tokens, uint8_t* kv_cache,
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_size, const float* rht_signs, void* stream) {
+  int4kv_status_t s =
+      check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
+  if (s != INT4KV_OK) return s;
+  if (dtype != INT4KV_F16 && dtype != INT4KV_BF16)
+    return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
+  if (num_tokens < 0) return fail(INT4KV_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !slot_mapping)
+    return fail(INT4KV_ERR_INVALID_ARG, "null key, value or slot_mapping pointer");
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_token_stride < row || value_token_stride < row)
+    return fail(INT4KV_ERR_INVALID_ARG, "token strides (%lld, %lld) smaller than heads*head_size %lld",
+                (long long)key_token_stride, (long long)value_token_stride, (long long)row);
+  if ((key_token_stride % 8) || (value_token_stride % 8) || !aligned16(key) || !aligned16(value))
+    return fail(INT4KV_ERR_INVALID_ARG,
+                "key/value must be 16-byte aligned with token strides a multiple of 8 elements");
+  hipError_t e = int4kv::launch_write(key, key_token_stride, value, value_token_stride,
+                                      dtype == INT4KV_BF16, slot_mapping, num_tokens, kv_cache,
+                                      num_kv_heads, head_size, rht_signs,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void* out,
+                                     int4kv_dtype_t dtype, const uint8_t* kv_cache,
+                                     int32_t num_blocks, int32_t block_size,
+                                     int32_t num_kv_heads, int32_t head_size,
+                                     int32_t num_q_heads, const int32_t* cu_seqlens_q,
+                                     const int32_t* seqused_k, int32_t num_seqs,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     const int32_t* block_table, int32_t block_table_stride,
+                                     float softmax_scale, const float* rht_signs,
+                                     int32_t num_segments, float* segm_output, float* segm_max,
+                                     float* segm_expsum, void* stream) {
+  int4kv_status_t s =
+      check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
+  if (s != INT4KV_OK) return s;
+  if (dtype != INT4KV_F16 && dtype != INT4KV_BF16)
+    return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
+  if (num_seqs == 0 || max_seqlen_q == 0) return ok();
+  if (!q || !out || !cu_seqlens_q || !seqused_k || !block_table)
+    return fail(INT4KV_ERR_INVALID_ARG, "null q, out, cu_seqlens_q, seqused_k or block_table");
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(INT4KV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(INT4KV_ERR_UNSUPPORTED, "query heads per KV head %d: supported 1, 2, 4, 8, 16", G);
+  if (q_token_stride < (int64_t)num_q_heads * head_size || (q_token_stride % 8) || !aligned16(q) ||
+      !aligned16(out))
+    return fail(INT4KV_ERR_INVALID_ARG,
+                "q token stride %lld must be >= heads*head_size and a multiple of 8; q and out "
+                "16-byte aligned", (long long)q_token_stride);
+  if (block_table_stride < (max_seqlen_k + block_size - 1) / block_size)
+    return fail(INT4KV_ERR_INVALID_ARG, "block_table_stride %d < ceil(max_seqlen_k / block_size)",
+                block_table_stride);
+  if (num_segments < 1) return fail(INT4KV_ERR_INVALID_ARG, "num_segments %d < 1", num_segments);
+  if (!std::isfinite(softmax_scale))
+    return fail(INT4KV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const bool decode = max_seqlen_q == 1;
+  if (decode && num_segments > 1 && (!segm_output || !segm_max || !segm_expsum))
+    return fail(INT4KV_ERR_WORKSPACE, "num_segments %d > 1 needs the three segment buffers",
+                num_segments);
+  if (num_segments > 65535) return fail(INT4KV_ERR_INVALID_ARG, "num_segments too large");
+  if (num_seqs > 65535 || num_kv_heads > 65535)
+    return fail(INT4KV_ERR_UNSUPPORTED, "num_seqs and num_kv_heads are limited to 65535");
+
+  int4kv::AttnArgs a{q, q_token_stride, out, dtype == INT4KV_BF16, kv_cache, num_kv_heads,
+                     head_size, num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q,
+                     max_seqlen_k, block_table, block_table_stride, softmax_scale, rht_signs,
+                     decode ? num_segments : 1, segm_output, segm_max, segm_expsum};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = decode ? int4kv::launch_decode(a, st) : int4kv::launch_prefill(a, st);
+  if (e != hipSuccess)
+    return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

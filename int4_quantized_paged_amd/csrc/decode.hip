@@ -1,0 +1,572 @@
+// INT4 paged decode attention (one query row per sequence), gfx950.
+//
+// Read half of the method as PR #40633's description lays it out: Q is brought
+// into the cache's rotated domain and split into two interleaved streams that
+// match the nibble order; the score is a split dot product over the codes with
+// the asymmetry corrected on the score side by a sum(Q) * zp term; separate
+// accumulators per stream; online softmax; split-K segments merged by a
+// segment reduction (reduce.hip).  The PR #40835 report lists the INT4 mode as
+// causal only.  The test file's section 6 fixes the argument list
+// (cu_seqlens_q, seqused_k, block_table, segment buffers).
+//
+// Work decomposition: one workgroup per (sequence, split-K segment, group of
+// HPW KV heads); one wave per KV head.  A wave keeps the G query heads of its
+// KV head on the rows of 16x16x32 f16 MFMA tiles and walks its segment two
+// cache blocks (32 keys) at a time:
+//   S  = Q' . K^T    A = rotated Q (f16 hi + lo parts), B = K codes
+//   O += W  . V      A = softmax weights times the V scale (f16), B = V codes
+// Codes are expanded to f16 in registers (exact for 0..15).  The zero points
+// enter as scalar corrections: score - zp_K * sum(Q') and O - sum(W * zp_V).
+// Query head qh sits on MFMA row 4 * (qh / RPG) + qh % RPG, so the score and
+// output accumulators of a query head live in one register of one 16-lane
+// group: the softmax touches ceil(G/4) registers per 16 keys, not 4.
+#include "device_common.h"
+#include "launch.h"
+
+namespace int4kv {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One dword of 8 codes (elements e0..e7) to the f16 operand order
+// [e0, e4, e1, e5, e2, e6, e3, e7]: operand slot j holds element
+// (j >> 1) + 4 * (j & 1).
+__device__ __forceinline__ half8_t unpack8(uint32_t w) {
+  u32x4_t r;
+  r.x = nib_pair_f16(w);
+  r.y = nib_pair_f16(w >> 4);
+  r.z = nib_pair_f16(w >> 8);
+  r.w = nib_pair_f16(w >> 12);
+  return __builtin_bit_cast(half8_t, r);
+}
+
+__device__ __forceinline__ uint32_t ld32(const uint8_t* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+
+template <int D>
+struct Tile {
+  static constexpr int NCH = D / 32;  // QK k-chunks
+  uint32_t kd[2][NCH];                // K codes, this lane's dwords, per 16-key half
+  uint32_t ks[2];                     // K scale word of key (lane & 15) of each half
+  uint32_t vd[8];                     // V codes: dword (lane & 15) % (D/8) of 8 keys
+  uint32_t vs[2];                     // V scale word of key (lane & 15) of each half
+};
+
+// Tile-local key of V operand slot j for lane group g (slots 8g..8g+7):
+// pairs (2i, 2i+1) hold keys (4g + i, 16 + 4g + i).
+__device__ __forceinline__ int vslot_key(int g, int j) { return ((j & 1) << 4) + 4 * g + (j >> 1); }
+
+// Loop-invariant per-lane byte offsets inside a block pair [K half | V half]
+// of one cache block; a tile adds the (wave-uniform) block base.
+template <int D>
+struct LaneOffsets {
+  uint32_t k;      // this lane's NCH code dwords of K row (lane & 15)
+  uint32_t ks;     // K scale word of key (lane & 15)
+  uint32_t vs;     // V scale word of key (lane & 15)
+  uint32_t v[8];   // V code dword (lane & 15) % (D/8) of the key in operand slot j
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(uint32_t tok_stride, uint32_t head_off,
+                                                       int lane) {
+  constexpr int NCH = D / 32;
+  constexpr int DW = D / 8;
+  const int col = lane & 15, g = lane >> 4;
+  const uint32_t blk_bytes = (uint32_t)kBlockSize * tok_stride;
+  LaneOffsets<D> o;
+  o.k = col * tok_stride + head_off + 4 * NCH * g;
+  o.ks = col * tok_stride + head_off + D / 2;
+  o.vs = blk_bytes + o.ks;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    o.v[j] = blk_bytes + (vslot_key(g, j) & 15) * tok_stride + head_off + 4 * (col % DW);
+  return o;
+}
+
+// Loads of one tile = blocks (p0, p1).  base = cache + phys * 2 * blk_bytes
+// is uniform across the wave, so the address is SGPR base + VGPR offset.
+template <int D>
+__device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* __restrict__ base0,
+                                          const uint8_t* __restrict__ base1,
+                                          const LaneOffsets<D>& o) {
+  constexpr int NCH = D / 32;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const uint8_t* base = n ? base1 : base0;
+    if constexpr (NCH == 4) {
+      const u32x4a4_t v = *reinterpret_cast<const u32x4a4_t*>(base + o.k);
+      t.kd[n][0] = v.x;
+      t.kd[n][1] = v.y;
+      t.kd[n][2] = v.z;
+      t.kd[n][3] = v.w;
+    } else {
+      const u32x2a4_t v = *reinterpret_cast<const u32x2a4_t*>(base + o.k);
+      t.kd[n][0] = v.x;
+      t.kd[n][1] = v.y;
+    }
+    t.ks[n] = ld32(base + o.ks);
+    t.vs[n] = ld32(base + o.vs);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t.vd[j] = ld32(((j & 1) ? base1 : base0) + o.v[j]);
+}
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(512) void decode_kernel(
+    const uint16_t* __restrict__ q, int64_t q_stride, uint16_t* __restrict__ out,
+    const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
+    const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
+    const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
+    const float* __restrict__ signs, int32_t num_segments, float* __restrict__ segm_out,
+    float* __restrict__ segm_max, float* __restrict__ segm_sum) {
+  constexpr int NCH = D / 32;
+  constexpr int NCOL = D / 16;
+  constexpr int R = D / 2 + 4;
+  constexpr int RPG = G <= 4 ? 1 : G / 4;
+  constexpr int EPL = G * D / 64;   // prologue: elements of Q per lane
+  constexpr int LPQ = 64 / G;       // prologue: lanes per query head
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hpw = blockDim.x >> 6;
+  const int b = blockIdx.y;
+  const int seg = blockIdx.x;
+  const int h = blockIdx.z * hpw + wave;
+
+  const int q0 = cu_seqlens_q[b];
+  const int qlen = cu_seqlens_q[b + 1] - q0;
+  if (qlen <= 0) return;  // uniform over the workgroup
+  const int L = seqused_k[b];
+  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  const int per = (nblk + num_segments - 1) / num_segments;
+  const int b0 = seg * per;
+  const int b1 = min(b0 + per, nblk);
+
+  // ---- prologue: q' = H (signs * q), split into f16 hi + lo parts
+  _Float16* qhi = reinterpret_cast<_Float16*>(smem) + (size_t)wave * 2 * G * D;
+  _Float16* qlo = qhi + G * D;
+  float* qinfo = reinterpret_cast<float*>(reinterpret_cast<_Float16*>(smem) + (size_t)hpw * 2 * G * D) +
+                 wave * 2 * G;
+  {
+    const int i = lane / LPQ, s = lane % LPQ;
+    const uint16_t* qp = q + (int64_t)q0 * q_stride + (int64_t)(h * G + i) * D + s * EPL;
+    float x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = to_f32<BF16>(qp[e]) * signs[s * EPL + e];
+#pragma unroll
+    for (int span = 1; span < EPL; span <<= 1) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        if (e & span) continue;
+        float u = x[e], v = x[e + span];
+        x[e] = u + v;
+        x[e + span] = u - v;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPQ; m <<= 1) {
+      const bool upper = (s & m) != 0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float p = shfl_xor_rt(x[e], m);
+        x[e] = upper ? p - x[e] : x[e] + p;
+      }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) mx = fmaxf(mx, fabsf(x[e]));
+#pragma unroll
+    for (int m = 1; m < LPQ; m <<= 1) mx = fmaxf(mx, shfl_xor_rt(mx, m));
+    // power-of-two normalisation keeps q'' in (-1, 1) for the f16 split
+    const int ex = mx > 0.f ? ilogbf(mx) + 1 : 0;
+    const float nrm = ldexpf(1.0f, -ex);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float v = x[e] * nrm;
+      const _Float16 hv = (_Float16)v;
+      const _Float16 lv = (_Float16)(v - (float)hv);
+      qhi[i * D + s * EPL + e] = hv;
+      qlo[i * D + s * EPL + e] = lv;
+      sum += (float)hv + (float)lv;
+    }
+#pragma unroll
+    for (int m = 1; m < LPQ; m <<= 1) sum += shfl_xor_rt(sum, m);
+    if (s == 0) {
+      qinfo[2 * i] = sum;
+      qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex);
+    }
+  }
+  __syncthreads();
+
+  const int col = lane & 15, g = lane >> 4;
+  // A operands of the score MFMAs (row r = lane & 15 -> query head)
+  half8_t qa_hi[NCH], qa_lo[NCH];
+  {
+    const int r = col, grp = r >> 2, v = r & 3;
+    const int qh = grp * RPG + v;
+    const bool ok = v < RPG && qh < G;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 8 * (g * NCH + c) + (j >> 1) + 4 * (j & 1);
+        qa_hi[c][j] = ok ? qhi[qh * D + d] : (_Float16)0.0f;
+        qa_lo[c][j] = ok ? qlo[qh * D + d] : (_Float16)0.0f;
+      }
+    }
+  }
+  // per query head constants in the accumulator layout (lane group g, register v)
+  float qsum[RPG], c0[RPG];
+  bool qok[RPG];
+#pragma unroll
+  for (int v = 0; v < RPG; ++v) {
+    const int qh = g * RPG + v;
+    qok[v] = qh < G;
+    qsum[v] = qok[v] ? qinfo[2 * qh] : 0.f;
+    c0[v] = qok[v] ? qinfo[2 * qh + 1] : 0.f;
+  }
+
+  float m_run[RPG], l_run[RPG], corr[RPG];
+  float4_t oacc[NCOL];
+#pragma unroll
+  for (int v = 0; v < RPG; ++v) {
+    m_run[v] = -INFINITY;
+    l_run[v] = 0.f;
+    corr[v] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t tok_stride = (int64_t)num_kv_heads * R;
+  const int64_t head_off = (int64_t)h * R;
+  const int32_t* bt = block_table + (int64_t)b * bt_stride;
+
+  // Register pipeline: tiles of 2 blocks are loaded P-1 tiles ahead of the one
+  // being processed.  Loads are unconditional (block ids clamped to the
+  // segment's last block) so the compiler keeps them in flight across tiles.
+  constexpr int P = 3;
+  Tile<D> buf[P];
+  const LaneOffsets<D> loff = lane_offsets<D>((uint32_t)tok_stride, (uint32_t)head_off, lane);
+  const int64_t pair_bytes = 2 * (int64_t)kBlockSize * tok_stride;
+  auto issue = [&](Tile<D>& t, int tb) {
+    const int i0 = min(tb, b1 - 1), i1 = min(tb + 1, b1 - 1);
+    load_tile<D>(t, cache + (int64_t)bt[i0] * pair_bytes, cache + (int64_t)bt[i1] * pair_bytes,
+                 loff);
+  };
+  auto process = [&](const Tile<D>& cur, int tb) {
+
+      // ---- scores S = Q' K^T for the two 16-key halves
+      float4_t sacc[2];
+  #pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const half8_t kb = unpack8(cur.kd[n][c]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], kb, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], kb, acc, 0, 0, 0);
+        }
+        sacc[n] = acc;
+      }
+
+      // ---- online softmax (base 2), per query head in register v of group g
+      bool kval[2];
+      float sK[2], zK[2], sV[2], zV[2];
+  #pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int key = tb * kBlockSize + 16 * n + col;
+        kval[n] = (tb + n < b1) && key < L;
+        sK[n] = as_float(cur.ks[n] & 0xFFFFFFF0u);
+        zK[n] = (float)(cur.ks[n] & 0xFu);
+        sV[n] = as_float(cur.vs[n] & 0xFFFFFFF0u);
+        zV[n] = (float)(cur.vs[n] & 0xFu);
+      }
+      uint32_t wpk[RPG];
+  #pragma unroll
+      for (int v = 0; v < RPG; ++v) {
+        float z[2];
+  #pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const float t = sacc[n][v] - zK[n] * qsum[v];
+          z[n] = kval[n] ? t * (sK[n] * c0[v]) : -INFINITY;
+        }
+        float tmax = fmaxf(z[0], z[1]);
+        tmax = fmaxf(tmax, shfl_xor<1>(tmax));
+        tmax = fmaxf(tmax, shfl_xor<2>(tmax));
+        tmax = fmaxf(tmax, shfl_xor<4>(tmax));
+        tmax = fmaxf(tmax, shfl_xor<8>(tmax));
+        const float mnew = fmaxf(m_run[v], tmax);
+        const float alpha = exp2f(m_run[v] - mnew);
+        m_run[v] = mnew;
+        const float p0 = exp2f(z[0] - mnew), p1 = exp2f(z[1] - mnew);
+        const _Float16 w0 = (_Float16)(kval[0] ? p0 * sV[0] : 0.f);
+        const _Float16 w1 = (_Float16)(kval[1] ? p1 * sV[1] : 0.f);
+        l_run[v] = l_run[v] * alpha + (p0 + p1);
+        corr[v] = corr[v] * alpha + ((float)w0 * zV[0] + (float)w1 * zV[1]);
+  #pragma unroll
+        for (int c = 0; c < NCOL; ++c) oacc[c][v] *= alpha;
+        wpk[v] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+      }
+
+      // ---- weights to the A-operand layout: lane (row r, group g) takes slot
+      // pair i = (W[qh][4g + i], W[qh][16 + 4g + i]) from lane 16*(r/4) + 4g + i
+      u32x4_t wa;
+      {
+        const int r = col, grp = r >> 2, vv = r & 3;
+        const bool ok = vv < RPG && grp * RPG + vv < G;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int src = 16 * grp + 4 * g + i;
+          uint32_t val = 0;
+  #pragma unroll
+          for (int v = 0; v < RPG; ++v) {
+            const uint32_t t = lane_read(wpk[v], src);
+            val = (vv == v) ? t : val;
+          }
+          wa[i] = ok ? val : 0u;
+        }
+      }
+      const half8_t wop = __builtin_bit_cast(half8_t, wa);
+
+      // ---- V operands and O += W V
+      {
+        const int noff = (D == 64) ? 4 * (col >> 3) : 0;
+        uint32_t ylo[4], yhi[4];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t a = cur.vd[2 * i], bb = cur.vd[2 * i + 1];
+          ylo[i] = (a & 0xFFFFu) | (bb << 16);         // nibbles 0..3 of a | of b
+          yhi[i] = (a >> 16) | (bb & 0xFFFF0000u);     // nibbles 4..7
+        }
+  #pragma unroll
+        for (int c = 0; c < NCOL; ++c) {
+          const int nib = c + noff;  // nibble of the lane's dword used by column tile c
+          u32x4_t vb;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t y = (nib < 4) ? ylo[i] : yhi[i];
+            vb[i] = nib_pair_f16(y >> (4 * (nib & 3)));
+          }
+          oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
+                                                           oacc[c], 0, 0, 0);
+        }
+      }
+  };
+  // The loop body is straight-line: tiles past the segment end (at most P-1
+  // per segment) are processed with every key masked, which leaves the
+  // softmax state unchanged.
+  if (b0 < b1) {
+#pragma unroll
+    for (int s = 0; s < P - 1; ++s) issue(buf[s], b0 + 2 * s);
+    const int ntile = (b1 - b0 + 1) / 2;
+    for (int tb = b0; tb < b0 + 2 * ntile; tb += 2 * P) {
+#pragma unroll
+      for (int s = 0; s < P; ++s) {
+        issue(buf[(s + P - 1) % P], tb + 2 * (s + P - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this tile's math
+        process(buf[s], tb + 2 * s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- finalise: sums over the 16 lanes of a group
+#pragma unroll
+  for (int v = 0; v < RPG; ++v) {
+    l_run[v] += shfl_xor<1>(l_run[v]);
+    l_run[v] += shfl_xor<2>(l_run[v]);
+    l_run[v] += shfl_xor<4>(l_run[v]);
+    l_run[v] += shfl_xor<8>(l_run[v]);
+    corr[v] += shfl_xor<1>(corr[v]);
+    corr[v] += shfl_xor<2>(corr[v]);
+    corr[v] += shfl_xor<4>(corr[v]);
+    corr[v] += shfl_xor<8>(corr[v]);
+  }
+
+  // d held by column tile c of this lane
+  auto dof = [&](int c) -> int {
+    return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
+  };
+
+  if (num_segments > 1) {
+#pragma unroll
+    for (int v = 0; v < RPG; ++v) {
+      if (!qok[v]) continue;
+      const int qg = h * G + g * RPG + v;
+      const int64_t base = ((int64_t)b * num_q_heads + qg) * num_segments + seg;
+      float* dst = segm_out + base * D;
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) dst[dof(c)] = oacc[c][v] - corr[v];
+      if (col == 0) {
+        segm_max[base] = m_run[v];
+        segm_sum[base] = l_run[v];
+      }
+    }
+    return;
+  }
+
+  // ---- direct epilogue: normalise, rotate back (signs * H o / D), store
+#pragma unroll
+  for (int v = 0; v < RPG; ++v) {
+    const float inv_l = l_run[v] > 0.f ? 1.0f / l_run[v] : 0.f;
+    float o[NCOL];
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) o[c] = (oacc[c][v] - corr[v]) * inv_l;
+    // in-lane spans over c
+#pragma unroll
+    for (int span = 1; span < (D == 128 ? 8 : 4); span <<= 1) {
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) {
+        if (c & span) continue;
+        float a = o[c], bb = o[c + span];
+        o[c] = a + bb;
+        o[c + span] = a - bb;
+      }
+    }
+    // across lanes of the 16-lane group: lane xor 1, 2, 4, 8
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const bool upper = (col & m) != 0;
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) {
+        const float p = shfl_xor_rt(o[c], m);
+        o[c] = upper ? p - o[c] : o[c] + p;
+      }
+    }
+    if (!qok[v]) continue;
+    const int qg = h * G + g * RPG + v;
+    uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D;
+    const float invD = 1.0f / (float)D;
+    if constexpr (D == 128) {
+      u32x4_t pk;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int d0 = dof(2 * k), d1 = dof(2 * k + 1);
+        const uint16_t lo = from_f32<BF16>(o[2 * k] * signs[d0] * invD);
+        const uint16_t hi = from_f32<BF16>(o[2 * k + 1] * signs[d1] * invD);
+        pk[k] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(dst + dof(0)) = pk;
+    } else {
+      uint32_t pk[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int d0 = dof(2 * k), d1 = dof(2 * k + 1);
+        const uint16_t lo = from_f32<BF16>(o[2 * k] * signs[d0] * invD);
+        const uint16_t hi = from_f32<BF16>(o[2 * k + 1] * signs[d1] * invD);
+        pk[k] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + dof(0));
+      d32[0] = pk[0];
+      d32[1] = pk[1];
+    }
+  }
+}
+
+// Segment reduction: one wave per (sequence, query head).  O = sum_k O_k
+// 2^(m_k - M) / sum_k l_k 2^(m_k - M), then the inverse rotation.
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void reduce_kernel(
+    uint16_t* __restrict__ out, int32_t num_q_heads, const int32_t* __restrict__ cu_seqlens_q,
+    const float* __restrict__ signs, int32_t num_segments, const float* __restrict__ segm_out,
+    const float* __restrict__ segm_max, const float* __restrict__ segm_sum) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / num_q_heads;
+  const int qg = blockIdx.x % num_q_heads;
+  const int q0 = cu_seqlens_q[b];
+  if (cu_seqlens_q[b + 1] - q0 <= 0) return;
+  const int64_t base = ((int64_t)b * num_q_heads + qg) * num_segments;
+  float M = -INFINITY;
+  for (int k = 0; k < num_segments; ++k) M = fmaxf(M, segm_max[base + k]);
+  float Lsum = 0.f;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  if (M != -INFINITY) {
+    for (int k = 0; k < num_segments; ++k) {
+      const float mk = segm_max[base + k];
+      if (mk == -INFINITY) continue;
+      const float f = exp2f(mk - M);
+      Lsum += segm_sum[base + k] * f;
+      const float* src = segm_out + (base + k) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] += src[e] * f;
+    }
+  }
+  const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] *= inv;
+#pragma unroll
+  for (int span = 1; span < EPL; span <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      if (e & span) continue;
+      float a = o[e], bb = o[e + span];
+      o[e] = a + bb;
+      o[e + span] = a - bb;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float p = shfl_xor_rt(o[e], m);
+      o[e] = upper ? p - o[e] : o[e] + p;
+    }
+  }
+  uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e] * signs[lane * EPL + e] / (float)D);
+}
+
+template <bool BF16, int D, int G>
+hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
+  const int hkv = a.num_kv_heads;
+  const size_t lds_per_wave = 2 * G * D * sizeof(_Float16) + 2 * G * sizeof(float);
+  int hpw = 8;
+  while (hkv % hpw || hpw * lds_per_wave > 65536) hpw >>= 1;
+  const int ns = a.num_segments;
+  dim3 grid(ns, a.num_seqs, hkv / hpw), block(64 * hpw);
+  const size_t lds = (size_t)hpw * lds_per_wave;
+  const float scale_log2 = a.softmax_scale * kLog2e / (float)D;
+  hipLaunchKernelGGL((decode_kernel<BF16, D, G>), grid, block, lds, stream,
+                     reinterpret_cast<const uint16_t*>(a.q), a.q_stride,
+                     reinterpret_cast<uint16_t*>(a.out), a.cache, hkv, a.num_q_heads,
+                     a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs,
+                     ns, a.segm_out, a.segm_max, a.segm_sum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  hipLaunchKernelGGL((reduce_kernel<BF16, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
+                     stream, reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, a.cu_seqlens_q,
+                     a.signs, ns, a.segm_out, a.segm_max, a.segm_sum);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_decode_t<BF16, D, 1>(a, stream);
+    case 2: return launch_decode_t<BF16, D, 2>(a, stream);
+    case 4: return launch_decode_t<BF16, D, 4>(a, stream);
+    case 8: return launch_decode_t<BF16, D, 8>(a, stream);
+    default: return launch_decode_t<BF16, D, 16>(a, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.head_size == 128 ? launch_decode_d<true, 128>(a, stream)
+                                        : launch_decode_d<true, 64>(a, stream);
+  return a.head_size == 128 ? launch_decode_d<false, 128>(a, stream)
+                            : launch_decode_d<false, 64>(a, stream);
+}
+
+}  // namespace int4kv

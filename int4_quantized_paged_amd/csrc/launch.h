@@ -1,0 +1,37 @@
+// Host-side launchers of the INT4 KV-cache kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace int4kv {
+
+hipError_t launch_write(const void* key, int64_t key_stride, const void* value,
+                        int64_t value_stride, bool bf16, const int64_t* slot_mapping,
+                        int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
+                        int32_t head_size, const float* signs, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  int64_t q_stride;
+  void* out;
+  bool bf16;
+  const uint8_t* cache;
+  int32_t num_kv_heads, head_size, num_q_heads;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqused_k;
+  int32_t num_seqs, max_seqlen_q, max_seqlen_k;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  float softmax_scale;
+  const float* signs;
+  int32_t num_segments;
+  float* segm_out;
+  float* segm_max;
+  float* segm_sum;
+};
+
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace int4kv

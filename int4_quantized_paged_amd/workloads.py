@@ -172,7 +172,7 @@ def gqa_decode(device="cpu", seed: int = 1) -> Workload:
     S, Hq, Hkv, d, NB = 8, 32, 8, 128, 1024
     kv_lens = torch.randint(1, 1025, (S,), generator=gc).tolist()
     perm = torch.randperm(NB, generator=gc).to(torch.int32)
-    bt = perm.view(S, 64).clone()
+    bt = perm[:S * 64].view(S, 64).clone()
     g = gc if str(device) == "cpu" else _gen(seed, device)
     N = sum(kv_lens)
     key = _normal((N, Hkv, d), g, torch.bfloat16, device)

@@ -1,0 +1,112 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function that include/int4kv.h declares,
+size caches by the closed form, and reject invalid host arguments before
+anything is enqueued (these calls never reach the GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_quantized_paged_amd as ik
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "int4kv.h")
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(int4[a-z_0-9]*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ik.load_library()
+    names = declared_functions()
+    assert {"int4_kv_write", "int4_paged_attention", "int4kv_cache_bytes",
+            "int4kv_status_string", "int4kv_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    raw = ctypes.CDLL(ik.library_path())
+    for n in names:
+        assert ctypes.cast(getattr(raw, n), ctypes.c_void_p).value
+
+
+@pytest.mark.parametrize("nb,bs,h,d", [(3, 16, 1, 64), (16384, 16, 8, 128), (1, 16, 8, 64)])
+def test_cache_bytes_closed_form(nb, bs, h, d):
+    assert ik.int4kv_cache_bytes(nb, bs, h, d) == nb * 2 * bs * h * (d // 2 + 4)
+
+
+def test_cache_bytes_rejects_bad_dims():
+    assert ik.int4kv_cache_bytes(0, 16, 1, 64) == -1
+    assert ik.int4kv_cache_bytes(1, 16, 1, 63) == -1
+
+
+def test_memory_ratio_vs_int8_and_bf16():
+    # packed row d/2 + 4 bytes vs d + 4 (int8 per-token-head) and 2d (bf16)
+    for d, r8 in [(128, 0.515), (64, 0.529)]:
+        r = ik.int4kv_cache_bytes(1, 16, 1, d) / (2 * 16 * (d + 4))
+        assert abs(r - r8) < 1e-3
+    assert abs(ik.int4kv_cache_bytes(1, 16, 1, 128) / (2 * 16 * 256) - 0.2656) < 1e-3
+
+
+def test_status_strings():
+    for code, name in [(0, "INT4KV_OK"), (1, "INT4KV_ERR_INVALID_ARG"), (2, "INT4KV_ERR_UNSUPPORTED"),
+                       (3, "INT4KV_ERR_WORKSPACE"), (4, "INT4KV_ERR_LAUNCH")]:
+        assert ik.int4kv_status_string(code) == name
+
+
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def _write(**kw):
+    a = dict(key=FAKE, ks=1024, value=FAKE, vs=1024, dtype=1, slots=FAKE, T=4, cache=FAKE, nb=4,
+             bs=16, hkv=8, d=128, signs=FAKE, stream=None)
+    a.update(kw)
+    lib = ik.load_library()
+    return lib.int4_kv_write(a["key"], a["ks"], a["value"], a["vs"], a["dtype"], a["slots"], a["T"],
+                             a["cache"], a["nb"], a["bs"], a["hkv"], a["d"], a["signs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cache=None), 1), (dict(signs=None), 1), (dict(d=96), 2), (dict(d=256), 2),
+    (dict(bs=32), 2), (dict(dtype=7), 1), (dict(T=-1), 1), (dict(key=None), 1),
+    (dict(ks=1000), 1), (dict(vs=512), 1), (dict(key=FAKE + 2), 1), (dict(nb=0), 1),
+])
+def test_write_rejects_invalid_host_arguments(kw, status):
+    assert _write(**kw) == status
+    assert ik.int4kv_last_error() != ""
+
+
+def test_write_zero_tokens_is_a_no_op():
+    assert _write(T=0) == 0
+    assert ik.int4kv_last_error() == ""
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, qs=4096, out=FAKE, dtype=1, cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32,
+             cu=FAKE, su=FAKE, S=4, mq=1, mk=1024, bt=FAKE, bts=64, scale=0.088, signs=FAKE, ns=1,
+             so=None, sm=None, ss=None, stream=None)
+    a.update(kw)
+    lib = ik.load_library()
+    return lib.int4_paged_attention(a["q"], a["qs"], a["out"], a["dtype"], a["cache"], a["nb"],
+                                    a["bs"], a["hkv"], a["d"], a["hq"], a["cu"], a["su"], a["S"],
+                                    a["mq"], a["mk"], a["bt"], a["bts"], a["scale"], a["signs"],
+                                    a["ns"], a["so"], a["sm"], a["ss"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=30), 1), (dict(hq=24, hkv=8), 2), (dict(hq=256, hkv=8, qs=32768), 2),
+    (dict(d=80), 2), (dict(bs=8), 2), (dict(ns=0), 1), (dict(ns=16), 3), (dict(bts=10), 1),
+    (dict(qs=100), 1), (dict(out=None), 1), (dict(scale=float("inf")), 1), (dict(S=-1), 1),
+    (dict(cache=FAKE + 4), 1),
+])
+def test_attention_rejects_invalid_host_arguments(kw, status):
+    assert _attn(**kw) == status
+    assert ik.int4kv_last_error() != ""
+
+
+def test_attention_empty_batch_is_a_no_op():
+    assert _attn(S=0) == 0
+    assert _attn(mq=0) == 0

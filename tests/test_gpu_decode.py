@@ -1,0 +1,129 @@
+"""GPU parity of decode attention (one query per sequence), split-K included.
+
+The GPU runs int4_kv_write then int4_paged_attention; the oracle encodes the
+same raw K/V itself and evaluates textbook attention in fp64.  Bound:
+|gpu - ref| <= 2e-3 + 1e-2 |ref| elementwise."""
+import numpy as np
+import pytest
+import torch
+
+from int4_quantized_paged_amd import workloads as wl
+from tests.gpu_helpers import (assert_attention_close, gpu_attention, gpu_cache, gpu_write, header,
+                               oracle_attention, oracle_cache, sub_workload, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_both(oracle_mod, w, ns_list):
+    t = to_dev(w)
+    c = gpu_cache(w)
+    gpu_write(w, t, c, "all")
+    ref_cache = oracle_cache(oracle_mod, w, "all")
+    ref = oracle_attention(oracle_mod, w, ref_cache)
+    outs = {}
+    for ns in ns_list:
+        header(f"decode {w.name} NS={ns}")
+        outs[ns] = gpu_attention(w, t, c, ns)
+        torch.cuda.synchronize()
+        assert_attention_close(outs[ns], ref, f"{w.name} NS={ns}")
+    return outs, ref
+
+
+def test_tiny_causal_case(oracle_mod):
+    _run_both(oracle_mod, wl.tiny(), [1, 3])
+
+
+def test_gqa_decode(oracle_mod):
+    _run_both(oracle_mod, wl.gqa_decode(), [1, 16])
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_ragged_lengths(oracle_mod, G, d):
+    lens = [(1, 1), (1, 15), (1, 16), (1, 17), (1, 33), (1, 100), (1, 517)]
+    hkv = 2 if G <= 8 else 1
+    w = wl.custom(lens, G * hkv, hkv, d, dtype=torch.bfloat16, seed=G * 7 + d, write_all=True,
+                  extra_blocks=3)
+    _run_both(oracle_mod, w, [1, 2, 5, 64])
+
+
+def test_decode_fp16_and_scaled_inputs(oracle_mod):
+    for scale in (1e-3, 30.0):
+        w = wl.custom([(1, 70), (1, 250)], 8, 2, 128, dtype=torch.float16, seed=3,
+                      write_all=True, scale=scale)
+        _run_both(oracle_mod, w, [1, 4])
+
+
+def test_decode_empty_and_zero_length_sequences(oracle_mod):
+    # sequence 1 has no query (q_len 0); sequence 2 has no keys (output zero)
+    w = wl.custom([(1, 40), (0, 20), (1, 0), (1, 9)], 8, 2, 128, seed=4, write_all=True)
+    outs, ref = _run_both(oracle_mod, w, [1, 3])
+    assert np.all(ref[1] == 0.0)
+    for o in outs.values():
+        assert torch.all(o[1].float() == 0.0)
+
+
+def test_decode_outlier_channels(oracle_mod):
+    w = wl.custom([(1, 300), (1, 64)], 32, 8, 128, seed=12, write_all=True)
+    w.key[:, :, [3, 40, 77, 120]] *= 20
+    _run_both(oracle_mod, w, [1, 8])
+
+
+def test_batch_invariance(oracle_mod):
+    """A sequence's output bits do not depend on the rest of the batch."""
+    w = wl.gqa_decode()
+    t = to_dev(w)
+    c = gpu_cache(w)
+    gpu_write(w, t, c, "all")
+    for ns in (1, 16):
+        full = gpu_attention(w, t, c, ns)
+        for seqs in ([3], [0, 5], [7, 2, 6]):
+            ws = sub_workload(w, seqs)
+            ts = to_dev(ws)
+            part = gpu_attention(ws, ts, c, ns)
+            torch.cuda.synchronize()
+            assert torch.equal(part, full[seqs]), (ns, seqs)
+
+
+def test_split_count_agreement(oracle_mod):
+    w = wl.custom([(1, 2000), (1, 777)], 32, 8, 128, seed=21, write_all=True)
+    t = to_dev(w)
+    c = gpu_cache(w)
+    gpu_write(w, t, c, "all")
+    ref = oracle_attention(oracle_mod, w, oracle_cache(oracle_mod, w, "all"))
+    for ns in (1, 3, 16, 125, 200):
+        header(f"split count NS={ns}")
+        assert_attention_close(gpu_attention(w, t, c, ns), ref, f"NS={ns}")
+
+
+@pytest.mark.parametrize("ns", [8])
+def test_llama3_decode_full_size_sampled(oracle_mod, ns):
+    """64 x 4096, 32 q / 8 KV heads, outlier K channels: GPU at full size in the
+    benchmark's launch configuration; 3 sampled sequences checked against the
+    oracle (which encodes those sequences' raw K/V itself)."""
+    header(f"Llama-3-8B-shaped decode full size NS={ns}")
+    w = wl.llama3_8b_decode(device="cuda")
+    t = to_dev(w)
+    c = gpu_cache(w)
+    gpu_write(w, t, c, "all")
+    out = gpu_attention(w, t, c, ns)
+    torch.cuda.synchronize()
+    for seqs in ([0], [37], [63]):
+        ws = sub_workload(w, seqs)
+        ref = oracle_attention(oracle_mod, ws, oracle_cache(oracle_mod, ws, "all"))
+        assert_attention_close(out[seqs], ref, f"seq {seqs}")
+
+
+@pytest.mark.parametrize("ns", [64])
+def test_long_context_decode_full_size_sampled(oracle_mod, ns):
+    """4 x 131072, 64 q / 8 KV heads: split-K at full size; one sequence checked."""
+    header(f"long-context decode full size NS={ns}")
+    w = wl.long_context_decode(device="cuda")
+    t = to_dev(w)
+    c = gpu_cache(w)
+    gpu_write(w, t, c, "all")
+    out = gpu_attention(w, t, c, ns)
+    torch.cuda.synchronize()
+    ws = sub_workload(w, [2])
+    ref = oracle_attention(oracle_mod, ws, oracle_cache(oracle_mod, ws, "all"))
+    assert_attention_close(out[[2]], ref, "seq 2")

@@ -1,0 +1,124 @@
+"""GPU parity of the cache write: packed bytes and scale words must equal the
+oracle's bit for bit, over the whole cache buffer (sentinel bytes included)."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import int4_quantized_paged_amd as ik
+from int4_quantized_paged_amd import workloads as wl
+from tests.gpu_helpers import SENTINEL, dt_name, gpu_cache, gpu_write, header, oracle_cache, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _write_both(oracle_mod, key, value, slots, nb, hkv, d, signs, key_dev=None, value_dev=None):
+    dev = "cuda"
+    c = torch.full(ik.cache_shape(nb, hkv, d), SENTINEL, dtype=torch.uint8, device=dev)
+    ik.int4_kv_write(key.to(dev) if key_dev is None else key_dev,
+                     value.to(dev) if value_dev is None else value_dev,
+                     slots.to(dev), c, signs.to(dev))
+    ref = np.full(oracle_mod.cache_shape(nb, 16, hkv, d), SENTINEL, np.uint8)
+    oracle_mod.kv_write(wl.bits16(key), wl.bits16(value), "bf16" if key.dtype == torch.bfloat16
+                        else "f16", slots.numpy(), ref, signs.numpy())
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hkv", [1, 4, 8])
+@pytest.mark.parametrize("T", [1, 7, 42])
+def test_write_page_grid_bit_exact(oracle_mod, T, hkv, d, dtype):
+    header(f"write grid T={T} hkv={hkv} d={d} {dtype}")
+    random.seed(0)
+    g = torch.Generator().manual_seed(T * 100 + hkv * 10 + d)
+    nb = (T + 15) // 16 + 4
+    slots = torch.tensor(random.sample(range(nb * 16), T), dtype=torch.int64)
+    key = torch.randn((T, hkv, d), generator=g).to(dtype)
+    value = torch.randn((T, hkv, d), generator=g).to(dtype)
+    got, ref = _write_both(oracle_mod, key, value, slots, nb, hkv, d, wl.rht_signs(d))
+    assert np.array_equal(got, ref)
+
+
+def test_write_negative_slots(oracle_mod):
+    header("write negative slots")
+    g = torch.Generator().manual_seed(5)
+    key = torch.randn((4, 2, 64), generator=g).to(torch.bfloat16)
+    value = torch.randn((4, 2, 64), generator=g).to(torch.bfloat16)
+    slots = torch.tensor([0, -1, 1, -1], dtype=torch.int64)
+    got, ref = _write_both(oracle_mod, key, value, slots, 2, 2, 64, wl.rht_signs(64))
+    assert np.array_equal(got, ref)
+    assert (got[0, :, 2:] == SENTINEL).all() and (got[1] == SENTINEL).all()
+    assert not (got[0, 0, 0] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_write_degenerate_rows(oracle_mod, d):
+    """Zero rows (scale floor), constants, one-hot rows (rotated row constant
+    up to sign), all-positive rotated rows (zp clamp), huge and tiny
+    magnitudes, exact ties, fp16 subnormals."""
+    header(f"write degenerate rows d={d}")
+    rows = [torch.zeros(d), torch.full((d,), 3.0), torch.full((d,), -0.5),
+            torch.nn.functional.one_hot(torch.tensor(0), d).float() * 7,
+            torch.nn.functional.one_hot(torch.tensor(5), d).float() * -2,
+            torch.arange(d).float() / 8, torch.randn(d) * 1e4, torch.randn(d) * 1e-5,
+            torch.round(torch.randn(d) * 4) / 2, torch.full((d,), 6e-8)]
+    x = torch.stack(rows)[:, None, :]
+    for dtype in (torch.float16, torch.bfloat16):
+        xx = x.to(dtype)
+        T = xx.shape[0]
+        slots = torch.arange(T, dtype=torch.int64) * 3
+        got, ref = _write_both(oracle_mod, xx, -xx, slots, (3 * T) // 16 + 1, 1, d, wl.rht_signs(d))
+        assert np.array_equal(got, ref), dtype
+
+
+def test_write_strided_token_layout(oracle_mod):
+    """key/value as slices of a fused qkv tensor (token stride > heads * d)."""
+    header("write strided qkv")
+    g = torch.Generator().manual_seed(11)
+    T, hq, hkv, d = 37, 32, 8, 128
+    qkv = torch.randn((T, hq + 2 * hkv, d), generator=g).to(torch.bfloat16)
+    qkv_d = qkv.cuda()
+    key, value = qkv[:, hq:hq + hkv], qkv[:, hq + hkv:]
+    key_d, value_d = qkv_d[:, hq:hq + hkv], qkv_d[:, hq + hkv:]
+    slots = torch.randperm(64 * 16, generator=g)[:T].to(torch.int64)
+    got, ref = _write_both(oracle_mod, key.contiguous(), value.contiguous(), slots, 64, hkv, d,
+                           wl.rht_signs(d), key_dev=key_d, value_dev=value_d)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("make", [wl.tiny, wl.gqa_decode])
+def test_write_small_workloads_whole_cache(oracle_mod, make):
+    w = make()
+    header(f"write workload {w.name}")
+    t = to_dev(w)
+    c = gpu_cache(w)
+    gpu_write(w, t, c, "all")
+    ref = oracle_cache(oracle_mod, w, "all")
+    assert np.array_equal(c.cpu().numpy(), ref)
+
+
+def test_write_llama3_bulk_fill_sampled(oracle_mod):
+    """Full-size bulk fill (64 x 4096 tokens, 8 KV heads, d 128) in the launch
+    configuration the benchmark times; 3000 sampled tokens checked against the
+    oracle bit for bit, and every row of the cache written."""
+    header("write Llama-3-8B-shaped bulk fill (sampled)")
+    w = wl.llama3_8b_decode(device="cuda")
+    idx, slots = w.token_set("all")
+    c = gpu_cache(w)
+    ik.int4_kv_write(w.key, w.value, slots.cuda(), c, w.signs.cuda())
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(1)
+    pick = torch.randperm(idx.numel(), generator=g)[:3000]
+    ref = np.full(oracle_mod.cache_shape(w.num_blocks, 16, 8, 128), SENTINEL, np.uint8)
+    oracle_mod.kv_write(wl.bits16(w.key[pick.cuda()]), wl.bits16(w.value[pick.cuda()]), "bf16",
+                        slots[pick].numpy(), ref, w.signs.numpy())
+    s = slots[pick]
+    blk, off = (s // 16).numpy(), (s % 16).numpy()
+    got = c.cpu().numpy()
+    assert np.array_equal(got[blk, :, off], ref[blk, :, off])
+    # every (block, kv, offset, head) row was written: its scale word is a valid scale
+    words = got[..., 64:68].copy().view("<u4")[..., 0]
+    assert ((words & 0x7F800000) != 0x7F800000).all() and (words != 0xA5A5A5A5).all()
