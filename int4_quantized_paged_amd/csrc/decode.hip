@@ -468,46 +468,82 @@ __global__ __launch_bounds__(512) void decode_kernel(
   }
 }
 
-// Segment reduction: one wave per (sequence, query head).  O = sum_k O_k
-// 2^(m_k - M) / sum_k l_k 2^(m_k - M), then the inverse rotation.
+// Segment reduction: one 256-thread block per (sequence, query head).
+// M = max_k m_k, L = sum_k l_k 2^(m_k - M), O = sum_k O_k 2^(m_k - M) / L, then
+// the inverse rotation signs * H O / D.  The four waves split the segments and
+// combine through LDS.
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_rt(v, m));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += shfl_xor_rt(v, m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 template <bool BF16, int D>
-__global__ __launch_bounds__(64) void reduce_kernel(
+__global__ __launch_bounds__(256) void reduce_kernel(
     uint16_t* __restrict__ out, int32_t num_q_heads, const int32_t* __restrict__ cu_seqlens_q,
     const float* __restrict__ signs, int32_t num_segments, const float* __restrict__ segm_out,
     const float* __restrict__ segm_max, const float* __restrict__ segm_sum) {
   constexpr int EPL = D / 64;
-  const int lane = threadIdx.x;
+  __shared__ float red[4];
+  __shared__ float part[4][D];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = blockIdx.x / num_q_heads;
   const int qg = blockIdx.x % num_q_heads;
   const int q0 = cu_seqlens_q[b];
-  if (cu_seqlens_q[b + 1] - q0 <= 0) return;
+  if (cu_seqlens_q[b + 1] - q0 <= 0) return;  // uniform over the block
   const int64_t base = ((int64_t)b * num_q_heads + qg) * num_segments;
-  float M = -INFINITY;
-  for (int k = 0; k < num_segments; ++k) M = fmaxf(M, segm_max[base + k]);
-  float Lsum = 0.f;
+
+  float mloc = -INFINITY;
+  for (int k = tid; k < num_segments; k += 256) mloc = fmaxf(mloc, segm_max[base + k]);
+  const float M = block_max(mloc, red);
+  float lloc = 0.f;
+  if (M != -INFINITY)
+    for (int k = tid; k < num_segments; k += 256) {
+      const float mk = segm_max[base + k];
+      if (mk != -INFINITY) lloc += segm_sum[base + k] * exp2f(mk - M);
+    }
+  const float Lsum = block_sum(lloc, red);
+
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
   if (M != -INFINITY) {
-    for (int k = 0; k < num_segments; ++k) {
+#pragma unroll 4
+    for (int k = wv; k < num_segments; k += 4) {
       const float mk = segm_max[base + k];
-      if (mk == -INFINITY) continue;
-      const float f = exp2f(mk - M);
-      Lsum += segm_sum[base + k] * f;
+      const float f = mk == -INFINITY ? 0.f : exp2f(mk - M);
       const float* src = segm_out + (base + k) * D + lane * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] += src[e] * f;
     }
   }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) part[wv][lane * EPL + e] = o[e];
+  __syncthreads();
+  if (wv != 0) return;
   const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] *= inv;
+  for (int e = 0; e < EPL; ++e) {
+    const int d = lane * EPL + e;
+    o[e] = ((part[0][d] + part[1][d]) + (part[2][d] + part[3][d])) * inv;
+  }
 #pragma unroll
   for (int span = 1; span < EPL; span <<= 1) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       if (e & span) continue;
-      float a = o[e], bb = o[e + span];
+      const float a = o[e], bb = o[e + span];
       o[e] = a + bb;
       o[e + span] = a - bb;
     }
@@ -543,9 +579,14 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
                      ns, a.segm_out, a.segm_max, a.segm_sum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL((reduce_kernel<BF16, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
+  return launch_reduce(a, stream);
+}
+
+template <bool BF16, int D>
+hipError_t launch_reduce_t(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((reduce_kernel<BF16, D>), dim3(a.num_seqs * a.num_q_heads), dim3(256), 0,
                      stream, reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, a.cu_seqlens_q,
-                     a.signs, ns, a.segm_out, a.segm_max, a.segm_sum);
+                     a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum);
   return hipGetLastError();
 }
 
@@ -562,7 +603,15 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.head_size == 128 ? launch_reduce_t<true, 128>(a, stream)
+                                        : launch_reduce_t<true, 64>(a, stream);
+  return a.head_size == 128 ? launch_reduce_t<false, 128>(a, stream)
+                            : launch_reduce_t<false, 64>(a, stream);
+}
+
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
+  if (decode_lds_supported(a)) return launch_decode_lds(a, stream);
   if (a.bf16) return a.head_size == 128 ? launch_decode_d<true, 128>(a, stream)
                                         : launch_decode_d<true, 64>(a, stream);
   return a.head_size == 128 ? launch_decode_d<false, 128>(a, stream)

@@ -32,6 +32,9 @@ struct AttnArgs {
 };
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream);
+bool decode_lds_supported(const AttnArgs& a);
+hipError_t launch_decode_lds(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace int4kv
