@@ -53,7 +53,7 @@ def _traffic_from_profiles(kernel_hash: str):
 def _kernel_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode.hip", "device_common.h"):
+    for f in ("decode_lds.hip", "decode.hip", "device_common.h", "launch.h"):
         with open(os.path.join(HERE, "int4_quantized_paged_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -211,7 +211,7 @@ def main():
         "write_tokens_per_s": round(wr_tps, 1),
         "write_bulk": {"tokens": wr_T, "seconds": wr_t,
                        "GB_per_s": round(w.write_bytes("all") / wr_t / 1e9, 1)},
-        "roofline": {"kernel": "decode_kernel + reduce_kernel (one int4_paged_attention call)",
+        "roofline": {"kernel": "decode_lds_kernel + reduce_kernel (one int4_paged_attention call)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kv_bytes,

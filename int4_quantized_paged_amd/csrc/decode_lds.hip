@@ -4,22 +4,25 @@
 // correction, online softmax, split-K segments merged by the reduction pass;
 // PR #40633's description), with a different data path:
 //
-//  * The workgroup owns all HPW <= 8 KV heads of its (sequence, segment), so the
-//    K and V halves of a cache block it reads are whole 16-byte-aligned slabs
+//  * The workgroup owns HPW <= 8 KV heads of its (sequence, segment), so the K
+//    and V halves of a cache block it reads are 16-byte-aligned runs
 //    (16 tokens x HPW x R bytes).  Each 2-block tile is copied HBM -> LDS with
 //    global_load_lds_dwordx4 by all waves together (every 128-byte line is
 //    fetched once) into a 3-stage ring, two tiles ahead of the math.  The copies
 //    are issued from inline assembly and waited for with explicit vmcnt so the
-//    compiler does not drain the ring at every barrier.
+//    compiler does not drain the ring at every barrier.  When a token's run is
+//    a whole number of 16-byte chunks, token rows are re-laid out in LDS with a
+//    stride of 12 dwords mod 32 so the per-lane row reads spread over the banks.
 //  * Q . K^T runs on the int8 MFMA (v_mfma_i32_16x16x64_i8): K codes become
 //    int8 with one mask (low nibbles) and a shift + mask (high nibbles) per
 //    dword; the rotated query is held as a 24-bit fixed-point value split into
-//    three int8 planes (p2 * 65536 + p1 * 256 + p0), so each plane's score and
-//    sum(Q) * zp term are exact integers, combined once in fp32.
-//  * P . V stays on the f16 MFMA (the softmax weights need f16 precision); V
-//    codes are expanded to f16 with (w & mask) | 0x6400 (two masks, no shift for
-//    half of the nibbles: 0x00F0 nibbles come out scaled by 16, undone per
-//    output column in the epilogue).
+//    three int8 planes (p2 * 65536 + p1 * 256 + p0): exact integer products,
+//    planes combined in fp32.
+//  * P . V runs on the f16 MFMA (the softmax weights need f16 precision).  V
+//    codes enter as (w & mask) | 0x6400, i.e. 1024 + code (or 1024 + 16 * code
+//    for the nibbles at bits 4..7, undone per output column); the 1024 * sum(W)
+//    bias is produced by one more MFMA against a constant operand and removed
+//    when the accumulators are flushed to fp32, every 16 tiles.
 #include "device_common.h"
 #include "launch.h"
 
@@ -31,6 +34,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kStages = 3;
+constexpr int kFlush = 16;  // tiles between fp32 flushes of the P.V accumulators
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -53,13 +57,33 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c
   return __builtin_amdgcn_bitop3_b32(a, mask, c, 0xEA);  // (a & mask) | c
 }
 
-// f16 pair (1024 + lo nibble field, 1024 + hi nibble field) - 1024.
-__device__ __forceinline__ uint32_t f16_pair(uint32_t fieldbits) {
-  half2_t h = __builtin_bit_cast(half2_t, fieldbits);
-  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  h = h - k1024;
-  return __builtin_bit_cast(uint32_t, h);
-}
+// Compile-time geometry of the LDS image of one tile (two cache blocks).
+template <int D, int HPW>
+struct Geo {
+  static constexpr uint32_t R = D / 2 + 4;
+  static constexpr uint32_t run = HPW * R;                 // bytes of the group's heads per token
+  static constexpr bool kTokenRows = run % 16 == 0;        // token runs are whole chunks
+  static constexpr uint32_t TS =                           // LDS token stride
+      kTokenRows && ((run / 4) % 8 == 0) ? run + 16 : run;
+  static constexpr uint32_t lhalf = 16 * TS;               // one K or V half
+  static constexpr uint32_t blk_chunks = 2 * lhalf / 16;   // 16-byte chunks per block image
+  static constexpr int UPB = (2 * lhalf + 1023) / 1024;    // 1 KiB DMA units per block
+  static constexpr uint32_t BLK = UPB * 1024;              // LDS offset of block 1
+  static constexpr int NI = (2 * UPB + HPW - 1) / HPW;     // DMA instructions per wave per tile
+  static constexpr uint32_t stage = HPW * NI * 1024;
+  static constexpr uint32_t wtile = 17 * 64;               // per-wave W tile: 16 rows + a zero row
+};
+
+// Whole LDS budget: three ring stages (the third also holds the staged query in
+// the prologue, so it is widened when the query is larger) and the W tiles.
+template <int D, int G, int HPW>
+struct Lay {
+  using GG = Geo<D, HPW>;
+  static constexpr uint32_t qstage = HPW * (G * D * 4 + 2 * G * 4);
+  static constexpr uint32_t third = GG::stage > qstage ? GG::stage : qstage;
+  static constexpr uint32_t wbase = 2 * GG::stage + third;
+  static constexpr uint32_t total = wbase + HPW * GG::wtile;
+};
 
 template <bool BF16, int D, int G, int HPW>
 __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
@@ -69,7 +93,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
     const float* __restrict__ signs, int32_t num_segments, float* __restrict__ segm_out,
     float* __restrict__ segm_max, float* __restrict__ segm_sum) {
-  constexpr int R = D / 2 + 4;
+  using GG = Geo<D, HPW>;
+  constexpr uint32_t R = GG::R;
   constexpr int DW = D / 8;      // code dwords per row
   constexpr int DWG = DW / 4;    // code dwords per lane group in the score operand
   constexpr int NCK = D / 64;    // int8 MFMA k-chunks
@@ -77,20 +102,13 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int RPG = G <= 4 ? 1 : G / 4;
   constexpr int EPL = G * D / 64;
   constexpr int LPQ = 64 / G;
-  // LDS image of a tile: two blocks, each [K half | V half] of 16 x HPW x R bytes,
-  // padded to whole 1 KiB DMA units so that a unit never straddles two blocks.
-  constexpr uint32_t run = HPW * R;                 // bytes of the group's heads per token
-  constexpr uint32_t lhalf = 16 * run;              // one K or V half
-  constexpr int UPB = (2 * lhalf + 1023) / 1024;    // DMA units per block
-  constexpr int NI = (2 * UPB + HPW - 1) / HPW;     // DMA instructions per wave per tile
-  constexpr uint32_t stage_bytes = HPW * NI * 1024;
-  constexpr int hpw = HPW;
+  constexpr int NI = GG::NI;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y, seg = blockIdx.x;
-  const int h0 = blockIdx.z * hpw;
+  const int h0 = blockIdx.z * HPW;
   const int h = h0 + wave;
   const int col = lane & 15, g = lane >> 4;
 
@@ -109,45 +127,49 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   const int64_t pair_g = 2 * (int64_t)half_g;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
   const int32_t* bt = block_table + (int64_t)b * bt_stride;
+  unsigned char* wt = smem + Lay<D, G, HPW>::wbase + wave * GG::wtile;  // this wave's W tile
 
   // ---- per-lane DMA sources (loop invariant).  Instruction i of wave w copies
-  // unit u = i*HPW + w; units [0, UPB) hold block 0, [UPB, 2*UPB) block 1, the
-  // rest is padding that re-reads the last chunk.
+  // unit u = i*HPW + w; units [0, UPB) hold block 0, [UPB, 2*UPB) block 1; the
+  // rest, and the padding chunks of token rows, re-read valid chunks.
   uint32_t goff[NI];
   {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int u = min(i * HPW + wave, 2 * UPB - 1);
-      const int blk = u >= UPB ? 1 : 0;
-      uint32_t cb = (uint32_t)(u - blk * UPB) * 64 + lane;  // chunk inside the block
-      if (cb >= 2 * run) cb = 2 * run - 1;
-      const uint32_t kv = cb >= run ? 1 : 0;
-      const uint32_t within = (cb - kv * run) * 16;
+      const int u = min(i * HPW + wave, 2 * GG::UPB - 1);
+      const int blk = u >= GG::UPB ? 1 : 0;
+      uint32_t pos = (uint32_t)(u - blk * GG::UPB) * 64 + lane;  // chunk in the block image
+      if (pos >= GG::blk_chunks) pos = GG::blk_chunks - 1;
       uint32_t off;
-      if (HPW == num_kv_heads) {
-        off = within;  // the half is one contiguous slab
-      } else {
-        const uint32_t tok = within / run, bb = within - tok * run;
-        off = tok * tok_g + (uint32_t)h0 * R + bb;
+      if constexpr (GG::kTokenRows) {
+        constexpr uint32_t TSC = GG::TS / 16, RC = GG::run / 16;
+        const uint32_t kv = pos / (16 * TSC), r = pos - kv * 16 * TSC;
+        const uint32_t tok = r / TSC;
+        uint32_t cc = r - tok * TSC;
+        if (cc >= RC) cc = RC - 1;
+        off = kv * half_g + tok * tok_g + (uint32_t)h0 * R + 16 * cc;
+      } else {  // only when the group holds every head: the half is one slab
+        const uint32_t kv = pos / GG::run;
+        off = kv * half_g + (pos - kv * GG::run) * 16;
       }
-      goff[i] = kv * half_g + off;
+      goff[i] = off;
     }
   }
   auto issue = [&](int tile) {
     const int i0 = min(b0 + 2 * tile, b1 - 1), i1 = min(b0 + 2 * tile + 1, b1 - 1);
     const uint8_t* p0 = cache + (int64_t)bt[i0] * pair_g;
     const uint8_t* p1 = cache + (int64_t)bt[i1] * pair_g;
-    const uint32_t sb = lds0 + (uint32_t)(tile % kStages) * stage_bytes + (uint32_t)wave * 1024;
+    const uint32_t sb = lds0 + (uint32_t)(tile % kStages) * GG::stage + (uint32_t)wave * 1024;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int u = min(i * HPW + wave, 2 * UPB - 1);
-      dma16(u >= UPB ? p1 : p0, goff[i], sb + (uint32_t)(i * HPW) * 1024);
+      const int u = min(i * HPW + wave, 2 * GG::UPB - 1);
+      dma16(u >= GG::UPB ? p1 : p0, goff[i], sb + (uint32_t)(i * HPW) * 1024);
     }
   };
 
   // ---- prologue: q' = H (signs * q) as 24-bit fixed point, staged in stage 2
-  int32_t* q24 = reinterpret_cast<int32_t*>(smem + 2 * stage_bytes) + wave * G * D;
-  float* qinfo = reinterpret_cast<float*>(smem + 2 * stage_bytes + HPW * G * D * 4) + wave * 4 * G;
+  int32_t* q24 = reinterpret_cast<int32_t*>(smem + 2 * GG::stage) + wave * G * D;
+  float* qinfo = reinterpret_cast<float*>(smem + 2 * GG::stage + HPW * G * D * 4) + wave * 2 * G;
   {
     const int i = lane / LPQ, s = lane % LPQ;
     const uint16_t* qp = q + (int64_t)q0 * q_stride + (int64_t)(h * G + i) * D + s * EPL;
@@ -180,37 +202,33 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int m = 1; m < LPQ; m <<= 1) mx = fmaxf(mx, shfl_xor_rt(mx, m));
     const int ex = mx > 0.f ? ilogbf(mx) + 1 : 0;  // |q'| * 2^-ex < 1
     const float nrm = ldexpf(1.0f, 23 - ex);
-    float ps[3] = {0.f, 0.f, 0.f};
+    float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       // |v| <= 2^23 - 2^16 keeps the top plane in [-128, 127] after carries
-      const int v = (int)fminf(fmaxf(rintf(x[e] * nrm), -8323072.f), 8323072.f);
-      q24[i * D + s * EPL + e] = v;
-      const int p0 = ((v + 128) & 0xFF) - 128, r1 = (v - p0) >> 8;
-      const int p1 = ((r1 + 128) & 0xFF) - 128, p2 = (r1 - p1) >> 8;
-      ps[0] += (float)p0;
-      ps[1] += (float)p1;
-      ps[2] += (float)p2;
+      const float v = fminf(fmaxf(rintf(x[e] * nrm), -8323072.f), 8323072.f);
+      q24[i * D + s * EPL + e] = (int)v;
+      sum += v;  // < 2^30 in magnitude; its rounding is far below the score's
     }
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int m = 1; m < LPQ; m <<= 1) ps[k] += shfl_xor_rt(ps[k], m);
+    for (int m = 1; m < LPQ; m <<= 1) sum += shfl_xor_rt(sum, m);
     if (s == 0) {
-      qinfo[4 * i + 0] = ps[0];
-      qinfo[4 * i + 1] = ps[1];
-      qinfo[4 * i + 2] = ps[2];
-      qinfo[4 * i + 3] = scale_log2 * ldexpf(1.0f, ex - 23);
+      qinfo[2 * i + 0] = sum;
+      qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - 23);
     }
   }
   if (ntile > 0) {  // always two tiles ahead (clamped), so vmcnt(NI) below is exact
     issue(0);
     issue(1);
   }
+  // zero row of the W tile (MFMA rows that carry no query head read it)
+  if (lane < 16) reinterpret_cast<uint32_t*>(wt + 16 * 64)[lane] = 0u;
   __syncthreads();
 
-  // int8 planes of Q in the score MFMA's A layout: slot (rho, beta) of chunk k
-  // in lane group g holds element 8*(g*DWG + 2k + rho/2) + 2*beta + rho%2.
+  // int8 planes of Q in the score MFMA's A layout.  Lane group g reads its K
+  // segment dwords in the rotated order j = (q + g) % DWG (spreads LDS banks);
+  // slot (rho, beta) of chunk k then holds element
+  // 8 * (g*DWG + (2k + rho/2 + g) % DWG) + 2*beta + rho%2.
   i32x4_t qa[3][NCK];
   {
     const int r = col, grp = r >> 2, vv = r & 3;
@@ -223,7 +241,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         uint32_t pw[3] = {0u, 0u, 0u};
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta) {
-          const int d = 8 * (g * DWG + 2 * k + (rho >> 1)) + 2 * beta + (rho & 1);
+          const int j = (2 * k + (rho >> 1) + g) % DWG;
+          const int d = 8 * (g * DWG + j) + 2 * beta + (rho & 1);
           const int v = ok ? q24[qh * D + d] : 0;
           const int p0 = ((v + 128) & 0xFF) - 128, r1 = (v - p0) >> 8;
           const int p1 = ((r1 + 128) & 0xFF) - 128, p2 = (r1 - p1) >> 8;
@@ -236,47 +255,75 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       }
     }
   }
-  int qs[3][RPG];
-  float c0[RPG];
+  float qsf[RPG], c0[RPG];
   bool qok[RPG];
 #pragma unroll
   for (int v = 0; v < RPG; ++v) {
     const int qh = g * RPG + v;
     qok[v] = qh < G;
-#pragma unroll
-    for (int pl = 0; pl < 3; ++pl) qs[pl][v] = qok[v] ? (int)qinfo[4 * qh + pl] : 0;
-    c0[v] = qok[v] ? qinfo[4 * qh + 3] : 0.f;
+    qsf[v] = qok[v] ? qinfo[2 * qh] : 0.f;
+    c0[v] = qok[v] ? qinfo[2 * qh + 1] : 0.f;
   }
 
   float m_run[RPG], l_run[RPG], corr[RPG];
-  float4_t oacc[NCOL];
+  float ov[NCOL][RPG];      // flushed P.V result (fp32; code - zp applied at the end)
+  float4_t oacc[NCOL];      // MFMA accumulators of W . (1024 + scaled code)
+  float4_t bacc;            // MFMA accumulator of W . 1024
 #pragma unroll
   for (int v = 0; v < RPG; ++v) {
     m_run[v] = -INFINITY;
     l_run[v] = 0.f;
     corr[v] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) ov[c][v] = 0.f;
   }
 #pragma unroll
   for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  bacc = float4_t{0.f, 0.f, 0.f, 0.f};
+  const int noff = (D == 64) ? 4 * (col >> 3) : 0;  // nibble offset of this lane's V dword
+  auto unscale = [&](int c) -> float { return ((c + noff) & 1) ? 0.0625f : 1.0f; };
+  auto flush = [&]() {
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c)
+#pragma unroll
+      for (int v = 0; v < RPG; ++v) ov[c][v] += (oacc[c][v] - bacc[v]) * unscale(c);
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    bacc = float4_t{0.f, 0.f, 0.f, 0.f};
+  };
 
   // per-lane LDS byte offsets inside a stage (loop invariant)
   const uint32_t hoff = (uint32_t)wave * R;
-  constexpr uint32_t blk_lds = UPB * 1024;                  // LDS offset of block 1
-  const uint32_t k_off = col * run + hoff + 4 * (g * DWG);  // + n*blk_lds, + 4*(2k+q)
-  const uint32_t ks_off = col * run + hoff + D / 2;          // + n*blk_lds (+ lhalf for V)
+  const uint32_t row_off = col * GG::TS + hoff;
+  uint32_t k_off[DWG];
+#pragma unroll
+  for (int qq = 0; qq < DWG; ++qq) k_off[qq] = row_off + 4 * (g * DWG + (qq + g) % DWG);
+  const uint32_t ks_off = row_off + D / 2;  // + n*BLK (+ lhalf for V)
   uint32_t v_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int kk = ((j & 1) << 4) + 4 * g + (j >> 1);  // key of P.V slot j (pairs 4g+i, 16+4g+i)
-    v_off[j] = (kk >> 4) * blk_lds + lhalf + (kk & 15) * run + hoff + 4 * (col % DW);
+    v_off[j] = (kk >> 4) * GG::BLK + GG::lhalf + (kk & 15) * GG::TS + hoff + 4 * (col % DW);
   }
-  const int noff = (D == 64) ? 4 * (col >> 3) : 0;  // nibble offset of this lane's V dword
+  // W tile addressing: writer (col, g) -> row qh, dword col; reader (row r, g)
+  // -> 16 bytes at dword 4g of its query head's row (or the zero row)
+  uint32_t wr_off[RPG];
+#pragma unroll
+  for (int v = 0; v < RPG; ++v) wr_off[v] = (uint32_t)min(g * RPG + v, 15) * 64 + 4 * col;
+  uint32_t rd_off;
+  {
+    const int grp = col >> 2, vv = col & 3, qh = grp * RPG + vv;
+    rd_off = (vv < RPG && qh < G ? (uint32_t)qh : 16u) * 64 + 16 * g;
+  }
+  half8_t ones1024;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones1024[j] = (_Float16)1024.0f;
 
   for (int t = 0; t < ntile; ++t) {
     wait_vmem<NI>();  // this wave's copies of tile t have landed (tile t+1 may be in flight)
     __syncthreads();  // ... and everyone's; everyone is done with tile t-1
     issue(t + 2);     // into the stage of tile t-1 (clamped to the segment's last block)
-    const unsigned char* st = smem + (uint32_t)(t % kStages) * stage_bytes;
+    const unsigned char* st = smem + (uint32_t)(t % kStages) * GG::stage;
     const int tb = b0 + 2 * t;
 
     // ---- scores: per plane S_p = Q_p . K (exact int32)
@@ -284,13 +331,15 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     uint32_t kw[2], vw[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const unsigned char* kp = st + n * blk_lds + k_off;
+      uint32_t segw[DWG];
+#pragma unroll
+      for (int qq = 0; qq < DWG; ++qq)
+        segw[qq] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + k_off[qq]);
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl) acc[n][pl] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int k = 0; k < NCK; ++k) {
-        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(kp + 8 * k);
-        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(kp + 8 * k + 4);
+        const uint32_t w0 = segw[2 * k], w1 = segw[2 * k + 1];
         i32x4_t kb;
         kb[0] = (int)(w0 & 0x0F0F0F0Fu);
         kb[1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
@@ -300,22 +349,22 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         for (int pl = 0; pl < 3; ++pl)
           acc[n][pl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[pl][k], kb, acc[n][pl], 0, 0, 0);
       }
-      kw[n] = *reinterpret_cast<const uint32_t*>(st + n * blk_lds + ks_off);
-      vw[n] = *reinterpret_cast<const uint32_t*>(st + n * blk_lds + lhalf + ks_off);
+      kw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + ks_off);
+      vw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + GG::lhalf + ks_off);
     }
 
     // ---- online softmax (base 2) per query head (register v of lane group g)
     bool kval[2];
-    float sK[2], sV[2], zV[2];
+    float sK[2], zK[2], sV[2], zV[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int key = tb * kBlockSize + 16 * n + col;
       kval[n] = (tb + n < b1) && key < L;
       sK[n] = as_float(kw[n] & 0xFFFFFFF0u);
+      zK[n] = (float)(kw[n] & 0xFu);
       sV[n] = as_float(vw[n] & 0xFFFFFFF0u);
       zV[n] = (float)(vw[n] & 0xFu);
     }
-    uint32_t wpk[RPG];
     float alpha[RPG];
     bool moved = false;
 #pragma unroll
@@ -323,13 +372,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       float z[2];
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        // sum_i q_i (code_i - zp) per plane, exact; planes combined in fp32
-        const int zk = (int)(kw[n] & 0xFu);
-        const int t0 = acc[n][0][v] - __mul24(zk, qs[0][v]);
-        const int t1 = acc[n][1][v] - __mul24(zk, qs[1][v]);
-        const int t2 = acc[n][2][v] - __mul24(zk, qs[2][v]);
-        const float tt = fmaf((float)t2, 65536.0f, (float)((t1 << 8) + t0));
-        z[n] = kval[n] ? tt * (sK[n] * c0[v]) : -INFINITY;
+        const float sf = fmaf((float)acc[n][2][v], 65536.0f,
+                              (float)((acc[n][1][v] << 8) + acc[n][0][v]));
+        const float tt = fmaf(-zK[n], qsf[v], sf);  // sum_i q_i (code_i - zp)
+        float zz = tt * (sK[n] * c0[v]);
+        asm volatile("" : "+v"(zz));  // computed by every lane: a select, not a branch
+        z[n] = kval[n] ? zz : -INFINITY;
       }
       float tmax = fmaxf(z[0], z[1]);
       tmax = fmaxf(tmax, shfl_xor<1>(tmax));
@@ -338,42 +386,33 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       tmax = fmaxf(tmax, shfl_xor<8>(tmax));
       const float mnew = fmaxf(m_run[v], tmax);
       moved |= mnew > m_run[v];
-      alpha[v] = exp2f(m_run[v] - mnew);
+      alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - mnew);
       m_run[v] = mnew;
-      const float p0 = exp2f(z[0] - mnew), p1 = exp2f(z[1] - mnew);
+      const float p0 = __builtin_amdgcn_exp2f(z[0] - mnew);
+      const float p1 = __builtin_amdgcn_exp2f(z[1] - mnew);
       const _Float16 w0 = (_Float16)(kval[0] ? p0 * sV[0] : 0.f);
       const _Float16 w1 = (_Float16)(kval[1] ? p1 * sV[1] : 0.f);
       l_run[v] = l_run[v] * alpha[v] + (p0 + p1);
       corr[v] = corr[v] * alpha[v] + ((float)w0 * zV[0] + (float)w1 * zV[1]);
-      wpk[v] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+      const uint32_t wpk = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+      *reinterpret_cast<uint32_t*>(wt + wr_off[v]) = wpk;
     }
     if (__any(moved)) {  // rescale only when some running maximum grew
 #pragma unroll
-      for (int v = 0; v < RPG; ++v)
+      for (int v = 0; v < RPG; ++v) {
 #pragma unroll
-        for (int c = 0; c < NCOL; ++c) oacc[c][v] *= alpha[v];
-    }
-
-    // ---- weights to the A layout: lane (row r, group g) takes slot pair i =
-    // (W[qh][4g + i], W[qh][16 + 4g + i]) from lane 16*(r/4) + 4g + i
-    u32x4_t wa;
-    {
-      const int r = col, grp = r >> 2, vv = r & 3;
-      const bool ok = vv < RPG && grp * RPG + vv < G;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int src = 16 * grp + 4 * g + i;
-        uint32_t val = 0;
-#pragma unroll
-        for (int v = 0; v < RPG; ++v) {
-          const uint32_t tv = lane_read(wpk[v], src);
-          val = (vv == v) ? tv : val;
+        for (int c = 0; c < NCOL; ++c) {
+          oacc[c][v] *= alpha[v];
+          ov[c][v] *= alpha[v];
         }
-        wa[i] = ok ? val : 0u;
+        bacc[v] *= alpha[v];
       }
     }
-    const half8_t wop = __builtin_bit_cast(half8_t, wa);
+
+    // ---- weights in the A layout, read back from this wave's W tile (LDS
+    // operations of one wave complete in order)
+    const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
 
     // ---- V operands and O += W V.  Column tile c uses nibble c (+ noff) of the
     // lane's dword of each slot key; nibbles at odd positions come out x16.
@@ -395,14 +434,17 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
           const uint32_t y = (nib < 4) ? ylo[i] : yhi[i];
           const uint32_t ys = (nib & 2) ? (y >> 8) : y;
           const uint32_t mask = (nib & 1) ? 0x00F000F0u : 0x000F000Fu;
-          vb[i] = f16_pair(and_or(ys, mask, 0x64006400u));
+          vb[i] = and_or(ys, mask, 0x64006400u);
         }
         oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
                                                          oacc[c], 0, 0, 0);
       }
+      bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, ones1024, bacc, 0, 0, 0);
     }
+    if ((t % kFlush) == kFlush - 1) flush();
   }
   wait_vmem<0>();  // drain the clamped look-ahead copies
+  flush();
 
   // ---- finalise: sums over the 16 lanes of a group
 #pragma unroll
@@ -416,11 +458,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     corr[v] += shfl_xor<4>(corr[v]);
     corr[v] += shfl_xor<8>(corr[v]);
   }
-  // column tile c holds element dof(c) of this lane, scaled by 16 for odd nibbles
+  // column tile c holds element dof(c) of this lane
   auto dof = [&](int c) -> int {
     return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
   };
-  auto unscale = [&](int c) -> float { return ((c + noff) & 1) ? 0.0625f : 1.0f; };
 
   if (num_segments > 1) {
 #pragma unroll
@@ -430,7 +471,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       const int64_t base = ((int64_t)b * num_q_heads + qg) * num_segments + seg;
       float* dst = segm_out + base * D;
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) dst[dof(c)] = oacc[c][v] * unscale(c) - corr[v];
+      for (int c = 0; c < NCOL; ++c) dst[dof(c)] = ov[c][v] - corr[v];
       if (col == 0) {
         segm_max[base] = m_run[v];
         segm_sum[base] = l_run[v];
@@ -444,7 +485,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const float inv_l = l_run[v] > 0.f ? 1.0f / l_run[v] : 0.f;
     float o[NCOL];
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) o[c] = (oacc[c][v] * unscale(c) - corr[v]) * inv_l;
+    for (int c = 0; c < NCOL; ++c) o[c] = (ov[c][v] - corr[v]) * inv_l;
 #pragma unroll
     for (int span = 1; span < (D == 128 ? 8 : 4); span <<= 1) {
 #pragma unroll
@@ -475,12 +516,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 
 template <bool BF16, int D, int G, int HPW>
 hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
-  constexpr int R = D / 2 + 4;
-  constexpr int UPB = (2 * 16 * HPW * R + 1023) / 1024;
-  constexpr int NI = (2 * UPB + HPW - 1) / HPW;
-  constexpr size_t stage = (size_t)HPW * NI * 1024;
-  constexpr size_t qstage = (size_t)HPW * (G * D * 4 + 4 * G * sizeof(float));
-  constexpr size_t lds = 2 * stage + (stage > qstage ? stage : qstage);
+  constexpr size_t lds = Lay<D, G, HPW>::total;
+  static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 CU");
   auto kern = decode_lds_kernel<BF16, D, G, HPW>;
   if (lds > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per CU)
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
