@@ -3,7 +3,9 @@
 Each ``csrc/*.hip`` file is compiled to an object in parallel, then linked
 into one shared library exporting the C ABI of ``include/int4kv.h``.
 The cache-write kernel is compiled without FMA contraction so its fp32
-sequence is the one the encoding defines.
+sequence is the one the encoding defines; the LDS-staged decode kernel is
+compiled without NaN semantics (its scores are finite or -inf by construction)
+so its 16-lane maxima are single DPP instructions.
 """
 from __future__ import annotations
 
@@ -23,7 +25,9 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           # packed fp32 ops are never emitted (see the project's design notes)
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I" + os.path.join(HERE, "..", "include")]
-PER_FILE = {"write.hip": ["-ffp-contract=off"]}
+# The LDS-staged decode kernel never produces NaN scores (masked keys are
+# selected as -inf, not computed), so its maxima need no NaN quieting.
+PER_FILE = {"write.hip": ["-ffp-contract=off"], "decode_lds.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -8,7 +8,8 @@
 //    and V halves of a cache block it reads are 16-byte-aligned runs
 //    (16 tokens x HPW x R bytes).  Each 2-block tile is copied HBM -> LDS with
 //    global_load_lds_dwordx4 by all waves together (every 128-byte line is
-//    fetched once) into a 3-stage ring, two tiles ahead of the math.  The copies
+//    fetched once) into a ring of 3 to 6 stages (as deep as the 160 KiB of LDS
+//    allows), all but one stage ahead of the math.  The copies
 //    are issued from inline assembly and waited for with explicit vmcnt so the
 //    compiler does not drain the ring at every barrier.  When a token's run is
 //    a whole number of 16-byte chunks, token rows are re-laid out in LDS with a
@@ -23,6 +24,8 @@
 //    for the nibbles at bits 4..7, undone per output column); the 1024 * sum(W)
 //    bias is produced by one more MFMA against a constant operand and removed
 //    when the accumulators are flushed to fp32, every 16 tiles.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -33,7 +36,6 @@ namespace int4kv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kStages = 3;
 constexpr int kFlush = 16;  // tiles between fp32 flushes of the P.V accumulators
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -57,6 +59,23 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c
   return __builtin_amdgcn_bitop3_b32(a, mask, c, 0xEA);  // (a & mask) | c
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the 16 lanes of a DPP row (rotations by 8 and 4, then the quad
+// swaps): four v_max_f32 with DPP operands.  Scores are finite or -inf (masked
+// keys are selected, never computed), so no NaN handling is needed here.
+__device__ __forceinline__ float max16(float x) {
+  x = fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8
+  x = fmaxf(x, dpp_f32<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+  return x;
+}
+
 // Compile-time geometry of the LDS image of one tile (two cache blocks).
 template <int D, int HPW>
 struct Geo {
@@ -69,19 +88,28 @@ struct Geo {
   static constexpr uint32_t blk_chunks = 2 * lhalf / 16;   // 16-byte chunks per block image
   static constexpr int UPB = (2 * lhalf + 1023) / 1024;    // 1 KiB DMA units per block
   static constexpr uint32_t BLK = UPB * 1024;              // LDS offset of block 1
-  static constexpr int NI = (2 * UPB + HPW - 1) / HPW;     // DMA instructions per wave per tile
-  static constexpr uint32_t stage = HPW * NI * 1024;
+  static constexpr int U = 2 * UPB;                        // units per tile
+  static constexpr int NI = (U + HPW - 1) / HPW;           // DMA instructions of waves [0, NREM)
+  static constexpr int NREM = U % HPW == 0 ? HPW : U % HPW;  // the others issue NI - 1
+  static constexpr uint32_t stage = U * 1024;
   static constexpr uint32_t wtile = 17 * 64;               // per-wave W tile: 16 rows + a zero row
 };
 
-// Whole LDS budget: three ring stages (the third also holds the staged query in
-// the prologue, so it is widened when the query is larger) and the W tiles.
+// Whole LDS budget: S ring stages (the last one also holds the staged query in
+// the prologue, widened when the query is larger) and the W tiles.  S is the
+// deepest ring that fits the 160 KiB of a gfx950 CU, at most 6 for a full
+// 8-head workgroup (one per CU) and at most 4 for smaller ones (several per CU
+// share the LDS).
 template <int D, int G, int HPW>
 struct Lay {
   using GG = Geo<D, HPW>;
   static constexpr uint32_t qstage = HPW * (G * D * 4 + 2 * G * 4);
-  static constexpr uint32_t third = GG::stage > qstage ? GG::stage : qstage;
-  static constexpr uint32_t wbase = 2 * GG::stage + third;
+  static constexpr uint32_t last = GG::stage > qstage ? GG::stage : qstage;
+  static constexpr uint32_t bytes(int s) { return (s - 1) * GG::stage + last + HPW * GG::wtile; }
+  static constexpr bool fits(int s) { return s <= (HPW == 8 ? 6 : 4) && bytes(s) <= 160 * 1024; }
+  static constexpr int S = fits(6) ? 6 : fits(5) ? 5 : fits(4) ? 4 : 3;
+  static constexpr uint32_t qbase = (S - 1) * GG::stage;
+  static constexpr uint32_t wbase = qbase + last;
   static constexpr uint32_t total = wbase + HPW * GG::wtile;
 };
 
@@ -103,6 +131,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int EPL = G * D / 64;
   constexpr int LPQ = 64 / G;
   constexpr int NI = GG::NI;
+  constexpr int S = Lay<D, G, HPW>::S;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
@@ -130,13 +159,14 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   unsigned char* wt = smem + Lay<D, G, HPW>::wbase + wave * GG::wtile;  // this wave's W tile
 
   // ---- per-lane DMA sources (loop invariant).  Instruction i of wave w copies
-  // unit u = i*HPW + w; units [0, UPB) hold block 0, [UPB, 2*UPB) block 1; the
-  // rest, and the padding chunks of token rows, re-read valid chunks.
+  // unit u = i*HPW + w < U; units [0, UPB) hold block 0, [UPB, U) block 1; the
+  // padding chunks of token rows and of the last unit re-read valid chunks.
+  const bool full = wave < GG::NREM;  // this wave issues NI copies per tile, else NI - 1
   uint32_t goff[NI];
   {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int u = min(i * HPW + wave, 2 * GG::UPB - 1);
+      const int u = min(i * HPW + wave, GG::U - 1);
       const int blk = u >= GG::UPB ? 1 : 0;
       uint32_t pos = (uint32_t)(u - blk * GG::UPB) * 64 + lane;  // chunk in the block image
       if (pos >= GG::blk_chunks) pos = GG::blk_chunks - 1;
@@ -159,17 +189,27 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const int i0 = min(b0 + 2 * tile, b1 - 1), i1 = min(b0 + 2 * tile + 1, b1 - 1);
     const uint8_t* p0 = cache + (int64_t)bt[i0] * pair_g;
     const uint8_t* p1 = cache + (int64_t)bt[i1] * pair_g;
-    const uint32_t sb = lds0 + (uint32_t)(tile % kStages) * GG::stage + (uint32_t)wave * 1024;
+    asm volatile("" : "+s"(p0), "+s"(p1));  // keep both bases in SGPRs; select per copy
+    const uint32_t sb = lds0 + (uint32_t)(tile % S) * GG::stage + (uint32_t)wave * 1024;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int u = min(i * HPW + wave, 2 * GG::UPB - 1);
+      if (i == NI - 1 && !full) break;
+      const int u = i * HPW + wave;
       dma16(u >= GG::UPB ? p1 : p0, goff[i], sb + (uint32_t)(i * HPW) * 1024);
     }
   };
+  // wait until at most `ahead` tiles of this wave's copies are in flight
+  auto wait_tiles = [&](auto ahead) {
+    if (full)
+      wait_vmem<decltype(ahead)::value * NI>();
+    else
+      wait_vmem<decltype(ahead)::value * (NI - 1)>();
+  };
 
-  // ---- prologue: q' = H (signs * q) as 24-bit fixed point, staged in stage 2
-  int32_t* q24 = reinterpret_cast<int32_t*>(smem + 2 * GG::stage) + wave * G * D;
-  float* qinfo = reinterpret_cast<float*>(smem + 2 * GG::stage + HPW * G * D * 4) + wave * 2 * G;
+  // ---- prologue: q' = H (signs * q) as 24-bit fixed point, staged in the last stage
+  int32_t* q24 = reinterpret_cast<int32_t*>(smem + Lay<D, G, HPW>::qbase) + wave * G * D;
+  float* qinfo =
+      reinterpret_cast<float*>(smem + Lay<D, G, HPW>::qbase + HPW * G * D * 4) + wave * 2 * G;
   {
     const int i = lane / LPQ, s = lane % LPQ;
     const uint16_t* qp = q + (int64_t)q0 * q_stride + (int64_t)(h * G + i) * D + s * EPL;
@@ -217,9 +257,9 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - 23);
     }
   }
-  if (ntile > 0) {  // always two tiles ahead (clamped), so vmcnt(NI) below is exact
-    issue(0);
-    issue(1);
+  if (ntile > 0) {  // always S - 1 tiles ahead (clamped), so the vmcnt below is exact
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) issue(i);
   }
   // zero row of the W tile (MFMA rows that carry no query head read it)
   if (lane < 16) reinterpret_cast<uint32_t*>(wt + 16 * 64)[lane] = 0u;
@@ -319,16 +359,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) ones1024[j] = (_Float16)1024.0f;
 
-  for (int t = 0; t < ntile; ++t) {
-    wait_vmem<NI>();  // this wave's copies of tile t have landed (tile t+1 may be in flight)
-    __syncthreads();  // ... and everyone's; everyone is done with tile t-1
-    issue(t + 2);     // into the stage of tile t-1 (clamped to the segment's last block)
-    const unsigned char* st = smem + (uint32_t)(t % kStages) * GG::stage;
-    const int tb = b0 + 2 * t;
-
-    // ---- scores: per plane S_p = Q_p . K (exact int32)
-    i32x4_t acc[2][3];
-    uint32_t kw[2], vw[2];
+  // ---- int8 K operands of one tile (low nibbles as is, high nibbles shifted)
+  auto k_operands = [&](const unsigned char* st, i32x4_t (&kb)[2][NCK]) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       uint32_t segw[DWG];
@@ -336,68 +368,120 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       for (int qq = 0; qq < DWG; ++qq)
         segw[qq] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + k_off[qq]);
 #pragma unroll
-      for (int pl = 0; pl < 3; ++pl) acc[n][pl] = i32x4_t{0, 0, 0, 0};
-#pragma unroll
       for (int k = 0; k < NCK; ++k) {
         const uint32_t w0 = segw[2 * k], w1 = segw[2 * k + 1];
-        i32x4_t kb;
-        kb[0] = (int)(w0 & 0x0F0F0F0Fu);
-        kb[1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
-        kb[2] = (int)(w1 & 0x0F0F0F0Fu);
-        kb[3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
-#pragma unroll
-        for (int pl = 0; pl < 3; ++pl)
-          acc[n][pl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[pl][k], kb, acc[n][pl], 0, 0, 0);
+        kb[n][k][0] = (int)(w0 & 0x0F0F0F0Fu);
+        kb[n][k][1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
+        kb[n][k][2] = (int)(w1 & 0x0F0F0F0Fu);
+        kb[n][k][3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
       }
+    }
+  };
+  // score group i (block n = i / NCK, k-chunk k = i % NCK): the three planes
+  // S_p += Q_p . K (exact int32)
+  auto score_group = [&](int i, const i32x4_t (&kb)[2][NCK], i32x4_t (&acc)[2][3]) {
+    const int n = i / NCK, k = i % NCK;
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl)
+      acc[n][pl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          qa[pl][k], kb[n][k], k == 0 ? i32x4_t{0, 0, 0, 0} : acc[n][pl], 0, 0, 0);
+  };
+  constexpr int NGROUP = 2 * NCK;
+  // emits score group `i` of the next tile if it exists, then fences the phase
+  auto phase_end = [&](int i, const i32x4_t (&kb)[2][NCK], i32x4_t (&acc)[2][3]) {
+    if (i < NGROUP) score_group(i, kb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- one pipelined step: the scores of tile t+1 (matrix cores) are
+  // interleaved, phase by phase, with the softmax of tile t (vector ALU); then
+  // O += W V for tile t.
+  auto step = [&](int t, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3]) {
+    wait_tiles(std::integral_constant<int, S - 3>());  // this wave's copies of tile t+1
+    __syncthreads();   // ... and everyone's; everyone is done with tile t-1
+    issue(t + S - 1);  // into the stage of tile t-1 (clamped to the segment's last block)
+    const unsigned char* st = smem + (uint32_t)(t % S) * GG::stage;
+    const int tb = b0 + 2 * t;
+
+    // phase 0: LDS reads (K of tile t+1; scale words and V of tile t).  After
+    // the last tile, tile t+1 is a clamped copy of the last block: its scores
+    // are never used.
+    i32x4_t kb[2][NCK];
+    k_operands(smem + (uint32_t)((t + 1) % S) * GG::stage, kb);
+    uint32_t kw[2], vw[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
       kw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + ks_off);
       vw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + GG::lhalf + ks_off);
     }
+    uint32_t va[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- online softmax (base 2) per query head (register v of lane group g)
+    // phase 1: logits z = c0 sK (S - zK sum(q')) in base-2 units
     bool kval[2];
-    float sK[2], zK[2], sV[2], zV[2];
+    float sV[2], zV[2];
+    float z[RPG][2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int key = tb * kBlockSize + 16 * n + col;
       kval[n] = (tb + n < b1) && key < L;
-      sK[n] = as_float(kw[n] & 0xFFFFFFF0u);
-      zK[n] = (float)(kw[n] & 0xFu);
-      sV[n] = as_float(vw[n] & 0xFFFFFFF0u);
+      const float sK = as_float(kw[n] & 0xFFFFFFF0u);
+      const float zK = (float)(kw[n] & 0xFu);
+      sV[n] = kval[n] ? as_float(vw[n] & 0xFFFFFFF0u) : 0.f;  // masked keys get zero weight
       zV[n] = (float)(vw[n] & 0xFu);
+      const uint32_t keep = kval[n] ? 0xFFFFFFFFu : 0u;
+      const uint32_t ninf = kval[n] ? 0u : 0xFF800000u;
+#pragma unroll
+      for (int v = 0; v < RPG; ++v) {
+        const float sf = fmaf((float)acc[n][2][v], 65536.0f,
+                              (float)((acc[n][1][v] << 8) + acc[n][0][v]));
+        const float tt = fmaf(-zK, qsf[v], sf);  // sum_i q_i (code_i - zp)
+        // masked keys become -inf through a bitwise select (never a branch)
+        z[v][n] = as_float(and_or(as_uint(tt * (sK * c0[v])), keep, ninf));
+      }
     }
-    float alpha[RPG];
+    phase_end(0, kb, nxt);
+
+    // phase 2: running maxima
+    float mnew[RPG], alpha[RPG];
     bool moved = false;
 #pragma unroll
     for (int v = 0; v < RPG; ++v) {
-      float z[2];
+      mnew[v] = fmaxf(m_run[v], max16(fmaxf(z[v][0], z[v][1])));
+      moved |= mnew[v] > m_run[v];
+      alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - mnew[v]);
+      m_run[v] = mnew[v];
+    }
+    phase_end(1, kb, nxt);
+
+    // phase 3: probabilities, weights W = p sV (f16), sums, zero-point term
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const float sf = fmaf((float)acc[n][2][v], 65536.0f,
-                              (float)((acc[n][1][v] << 8) + acc[n][0][v]));
-        const float tt = fmaf(-zK[n], qsf[v], sf);  // sum_i q_i (code_i - zp)
-        float zz = tt * (sK[n] * c0[v]);
-        asm volatile("" : "+v"(zz));  // computed by every lane: a select, not a branch
-        z[n] = kval[n] ? zz : -INFINITY;
-      }
-      float tmax = fmaxf(z[0], z[1]);
-      tmax = fmaxf(tmax, shfl_xor<1>(tmax));
-      tmax = fmaxf(tmax, shfl_xor<2>(tmax));
-      tmax = fmaxf(tmax, shfl_xor<4>(tmax));
-      tmax = fmaxf(tmax, shfl_xor<8>(tmax));
-      const float mnew = fmaxf(m_run[v], tmax);
-      moved |= mnew > m_run[v];
-      alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - mnew);
-      m_run[v] = mnew;
-      const float p0 = __builtin_amdgcn_exp2f(z[0] - mnew);
-      const float p1 = __builtin_amdgcn_exp2f(z[1] - mnew);
-      const _Float16 w0 = (_Float16)(kval[0] ? p0 * sV[0] : 0.f);
-      const _Float16 w1 = (_Float16)(kval[1] ? p1 * sV[1] : 0.f);
+    for (int v = 0; v < RPG; ++v) {
+      const float p0 = __builtin_amdgcn_exp2f(z[v][0] - mnew[v]);
+      const float p1 = __builtin_amdgcn_exp2f(z[v][1] - mnew[v]);
+      const _Float16 w0 = (_Float16)(p0 * sV[0]);
+      const _Float16 w1 = (_Float16)(p1 * sV[1]);
       l_run[v] = l_run[v] * alpha[v] + (p0 + p1);
       corr[v] = corr[v] * alpha[v] + ((float)w0 * zV[0] + (float)w1 * zV[1]);
       const uint32_t wpk = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
                            ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
       *reinterpret_cast<uint32_t*>(wt + wr_off[v]) = wpk;
     }
+    phase_end(2, kb, nxt);
+
+    // phase 4: V operand bytes (pairs of keys per dword); remaining score groups
+    uint32_t ylo[4], yhi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ylo[i] = __builtin_amdgcn_perm(va[2 * i + 1], va[2 * i], 0x05040100u);  // [a.b0 a.b1 b.b0 b.b1]
+      yhi[i] = __builtin_amdgcn_perm(va[2 * i + 1], va[2 * i], 0x07060302u);  // [a.b2 a.b3 b.b2 b.b3]
+    }
+#pragma unroll
+    for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+
     if (__any(moved)) {  // rescale only when some running maximum grew
 #pragma unroll
       for (int v = 0; v < RPG; ++v) {
@@ -410,39 +494,47 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       }
     }
 
-    // ---- weights in the A layout, read back from this wave's W tile (LDS
+    // weights in the A layout, read back from this wave's W tile (LDS
     // operations of one wave complete in order)
     const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
-
-    // ---- V operands and O += W V.  Column tile c uses nibble c (+ noff) of the
-    // lane's dword of each slot key; nibbles at odd positions come out x16.
-    {
-      uint32_t ylo[4], yhi[4];
+    // O += W V.  Column tile c uses nibble c (+ noff) of the lane's dword of
+    // each slot key; nibbles at odd positions come out x16.
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) {
+      const int nib = c + noff;
+      u32x4_t vb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(st + v_off[2 * i]);
-        const uint32_t bb = *reinterpret_cast<const uint32_t*>(st + v_off[2 * i + 1]);
-        ylo[i] = __builtin_amdgcn_perm(bb, a, 0x05040100u);  // [a.b0 a.b1 b.b0 b.b1]
-        yhi[i] = __builtin_amdgcn_perm(bb, a, 0x07060302u);  // [a.b2 a.b3 b.b2 b.b3]
+        const uint32_t y = (nib < 4) ? ylo[i] : yhi[i];
+        const uint32_t ys = (nib & 2) ? (y >> 8) : y;
+        const uint32_t mask = (nib & 1) ? 0x00F000F0u : 0x000F000Fu;
+        vb[i] = and_or(ys, mask, 0x64006400u);
       }
-#pragma unroll
-      for (int c = 0; c < NCOL; ++c) {
-        const int nib = c + noff;
-        u32x4_t vb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t y = (nib < 4) ? ylo[i] : yhi[i];
-          const uint32_t ys = (nib & 2) ? (y >> 8) : y;
-          const uint32_t mask = (nib & 1) ? 0x00F000F0u : 0x000F000Fu;
-          vb[i] = and_or(ys, mask, 0x64006400u);
-        }
-        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
-                                                         oacc[c], 0, 0, 0);
-      }
-      bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, ones1024, bacc, 0, 0, 0);
+      oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
+                                                       oacc[c], 0, 0, 0);
     }
+    bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, ones1024, bacc, 0, 0, 0);
     if ((t % kFlush) == kFlush - 1) flush();
+  };
+
+  // ---- main loop.  Tile t+1 must have landed at the top of step t; tiles
+  // t+2 .. t+S-1 are in flight.  Unrolled by two so the score accumulators
+  // alternate without copies.
+  i32x4_t accA[2][3], accB[2][3];
+  if (ntile > 0) {
+    wait_tiles(std::integral_constant<int, S - 2>());  // tile 0
+    __syncthreads();
+    i32x4_t kb[2][NCK];
+    k_operands(smem, kb);
+#pragma unroll
+    for (int i = 0; i < NGROUP; ++i) score_group(i, kb, accA);
   }
+  int t = 0;
+  for (; t + 1 < ntile; t += 2) {
+    step(t, accA, accB);
+    step(t + 1, accB, accA);
+  }
+  if (t < ntile) step(t, accA, accB);
   wait_vmem<0>();  // drain the clamped look-ahead copies
   flush();
 
@@ -518,6 +610,7 @@ template <bool BF16, int D, int G, int HPW>
 hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
   constexpr size_t lds = Lay<D, G, HPW>::total;
   static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 CU");
+  static_assert((Lay<D, G, HPW>::S - 2) * Geo<D, HPW>::NI <= 63, "vmcnt range");
   auto kern = decode_lds_kernel<BF16, D, G, HPW>;
   if (lds > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per CU)
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

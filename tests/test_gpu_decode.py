@@ -129,10 +129,14 @@ def test_long_context_decode_full_size_sampled(oracle_mod, ns):
     assert_attention_close(out[[2]], ref, "seq 2")
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(6, 3, 128), (32, 16, 128), (32, 16, 64), (12, 12, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(6, 3, 128), (32, 16, 128), (32, 16, 64), (12, 12, 64),
+                                      (16, 4, 128), (16, 4, 64), (64, 4, 128), (8, 8, 64),
+                                      (128, 8, 128), (16, 8, 64)])
 def test_decode_other_kv_head_counts(oracle_mod, hq, hkv, d):
-    """KV-head counts outside {1, 2, 4, 8}: 16 KV heads split into two groups
-    of 8 per workgroup (non-contiguous head runs), and counts that take the
-    register-staged path (3, 12)."""
+    """KV-head counts and group sizes beyond the other cases: 16 KV heads split
+    into two groups of 8 per workgroup (non-contiguous head runs), 4 KV heads per
+    workgroup at group sizes 4 and 16, 8 KV heads at group sizes 1, 2 and 16
+    (the largest staged query), and counts that take the register-staged path
+    (3, 12)."""
     w = wl.custom([(1, 45), (1, 300), (1, 16)], hq, hkv, d, seed=hq + hkv + d, write_all=True)
     _run_both(oracle_mod, w, [1, 4])
