@@ -36,7 +36,8 @@ namespace int4kv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kFlush = 16;  // tiles between fp32 flushes of the P.V accumulators
+constexpr int kFlush = 16;    // tiles between fp32 flushes of the P.V accumulators
+constexpr float kLazy = 4.0f;  // headroom of the softmax reference maximum (log2 units)
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 
   const uint32_t tok_g = (uint32_t)num_kv_heads * R;  // global token stride
   const uint32_t half_g = 16 * tok_g;
-  const int64_t pair_g = 2 * (int64_t)half_g;
+  const uint32_t pair_g = 2 * half_g;  // bytes per cache block (K and V halves)
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
   const int32_t* bt = block_table + (int64_t)b * bt_stride;
   unsigned char* wt = smem + Lay<D, G, HPW>::wbase + wave * GG::wtile;  // this wave's W tile
@@ -185,10 +186,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       goff[i] = off;
     }
   }
-  auto issue = [&](int tile) {
-    const int i0 = min(b0 + 2 * tile, b1 - 1), i1 = min(b0 + 2 * tile + 1, b1 - 1);
-    const uint8_t* p0 = cache + (int64_t)bt[i0] * pair_g;
-    const uint8_t* p1 = cache + (int64_t)bt[i1] * pair_g;
+  // block ids of the next tile to copy, read one step before they are needed
+  // so the scalar loads never stall the copy issue
+  uint32_t nid0 = 0, nid1 = 0;
+  auto load_ids = [&](int tile) {
+    nid0 = (uint32_t)bt[min(b0 + 2 * tile, b1 - 1)];
+    nid1 = (uint32_t)bt[min(b0 + 2 * tile + 1, b1 - 1)];
+  };
+  auto issue = [&](int tile) {  // nid0 / nid1 hold this tile's block ids
+    const uint8_t* p0 = cache + (uint64_t)nid0 * pair_g;
+    const uint8_t* p1 = cache + (uint64_t)nid1 * pair_g;
     asm volatile("" : "+s"(p0), "+s"(p1));  // keep both bases in SGPRs; select per copy
     const uint32_t sb = lds0 + (uint32_t)(tile % S) * GG::stage + (uint32_t)wave * 1024;
 #pragma unroll
@@ -259,7 +266,11 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
   if (ntile > 0) {  // always S - 1 tiles ahead (clamped), so the vmcnt below is exact
 #pragma unroll
-    for (int i = 0; i < S - 1; ++i) issue(i);
+    for (int i = 0; i < S - 1; ++i) {
+      load_ids(i);
+      issue(i);
+    }
+    load_ids(S - 1);
   }
   // zero row of the W tile (MFMA rows that carry no query head read it)
   if (lane < 16) reinterpret_cast<uint32_t*>(wt + 16 * 64)[lane] = 0u;
@@ -389,34 +400,53 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int NGROUP = 2 * NCK;
   // emits score group `i` of the next tile if it exists, then fences the phase
   auto phase_end = [&](int i, const i32x4_t (&kb)[2][NCK], i32x4_t (&acc)[2][3]) {
-    if (i < NGROUP) score_group(i, kb, acc);
+    if (i < NGROUP) {
+      score_group(i, kb, acc);
+      // one MFMA, then a few vector instructions, so the matrix core works
+      // while this wave keeps issuing
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- one pipelined step: the scores of tile t+1 (matrix cores) are
   // interleaved, phase by phase, with the softmax of tile t (vector ALU); then
   // O += W V for tile t.
-  auto step = [&](int t, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3]) {
+  // LDS words of a tile needed after its scores: scale words and V bytes
+  struct TileWords {
+    uint32_t kw[2], vw[2], va[8];
+  };
+  auto tile_words = [&](const unsigned char* st, TileWords& w) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      w.kw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + ks_off);
+      w.vw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + GG::lhalf + ks_off);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
+  };
+
+  auto step = [&](int t, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3], const TileWords& cw,
+                  TileWords& nw) {
     wait_tiles(std::integral_constant<int, S - 3>());  // this wave's copies of tile t+1
     __syncthreads();   // ... and everyone's; everyone is done with tile t-1
     issue(t + S - 1);  // into the stage of tile t-1 (clamped to the segment's last block)
+    load_ids(t + S);
     const unsigned char* st = smem + (uint32_t)(t % S) * GG::stage;
     const int tb = b0 + 2 * t;
 
-    // phase 0: LDS reads (K of tile t+1; scale words and V of tile t).  After
-    // the last tile, tile t+1 is a clamped copy of the last block: its scores
-    // are never used.
+    // phase 0: LDS reads of tile t+1 (K, scale words, V); tile t's words were
+    // read one step earlier, so the softmax below starts from registers.
+    // After the last tile, tile t+1 is a clamped copy of the last block: its
+    // words and scores are never used.
     i32x4_t kb[2][NCK];
-    k_operands(smem + (uint32_t)((t + 1) % S) * GG::stage, kb);
-    uint32_t kw[2], vw[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      kw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + ks_off);
-      vw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + GG::lhalf + ks_off);
-    }
-    uint32_t va[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
+    const unsigned char* sn = smem + (uint32_t)((t + 1) % S) * GG::stage;
+    k_operands(sn, kb);
+    tile_words(sn, nw);
     __builtin_amdgcn_sched_barrier(0);
 
     // phase 1: logits z = c0 sK (S - zK sum(q')) in base-2 units
@@ -427,10 +457,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int n = 0; n < 2; ++n) {
       const int key = tb * kBlockSize + 16 * n + col;
       kval[n] = (tb + n < b1) && key < L;
-      const float sK = as_float(kw[n] & 0xFFFFFFF0u);
-      const float zK = (float)(kw[n] & 0xFu);
-      sV[n] = kval[n] ? as_float(vw[n] & 0xFFFFFFF0u) : 0.f;  // masked keys get zero weight
-      zV[n] = (float)(vw[n] & 0xFu);
+      const float sK = as_float(cw.kw[n] & 0xFFFFFFF0u);
+      const float zK = (float)(cw.kw[n] & 0xFu);
+      sV[n] = kval[n] ? as_float(cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked keys get zero weight
+      zV[n] = (float)(cw.vw[n] & 0xFu);
       const uint32_t keep = kval[n] ? 0xFFFFFFFFu : 0u;
       const uint32_t ninf = kval[n] ? 0u : 0xFF800000u;
 #pragma unroll
@@ -444,13 +474,18 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     }
     phase_end(0, kb, nxt);
 
-    // phase 2: running maxima
+    // phase 2: reference maxima.  The reference m only moves when a logit
+    // exceeds it by more than kLazy (base-2 units), so p = 2^(z - m) <= 2^kLazy
+    // and the accumulators are rescaled rarely; m, l and O always share the
+    // same reference, which is all the merge and the normalisation need.
     float mnew[RPG], alpha[RPG];
     bool moved = false;
 #pragma unroll
     for (int v = 0; v < RPG; ++v) {
-      mnew[v] = fmaxf(m_run[v], max16(fmaxf(z[v][0], z[v][1])));
-      moved |= mnew[v] > m_run[v];
+      const float tmax = max16(fmaxf(z[v][0], z[v][1]));
+      const bool up = tmax > m_run[v] + kLazy;
+      moved |= up;
+      mnew[v] = up ? tmax : m_run[v];
       alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - mnew[v]);
       m_run[v] = mnew[v];
     }
@@ -469,17 +504,19 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
                            ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
       *reinterpret_cast<uint32_t*>(wt + wr_off[v]) = wpk;
     }
+    // weights in the A layout, read back from this wave's W tile right away
+    // (LDS operations of one wave complete in order); the latency is covered
+    // by the work up to the P.V products
+    const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
     phase_end(2, kb, nxt);
 
     // phase 4: V operand bytes (pairs of keys per dword); remaining score groups
     uint32_t ylo[4], yhi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ylo[i] = __builtin_amdgcn_perm(va[2 * i + 1], va[2 * i], 0x05040100u);  // [a.b0 a.b1 b.b0 b.b1]
-      yhi[i] = __builtin_amdgcn_perm(va[2 * i + 1], va[2 * i], 0x07060302u);  // [a.b2 a.b3 b.b2 b.b3]
+      ylo[i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], 0x05040100u);  // a.b01 b.b01
+      yhi[i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], 0x07060302u);  // a.b23 b.b23
     }
-#pragma unroll
-    for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
     __builtin_amdgcn_sched_barrier(0);
 
     if (__any(moved)) {  // rescale only when some running maximum grew
@@ -494,9 +531,6 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       }
     }
 
-    // weights in the A layout, read back from this wave's W tile (LDS
-    // operations of one wave complete in order)
-    const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
     // O += W V.  Column tile c uses nibble c (+ noff) of the lane's dword of
     // each slot key; nibbles at odd positions come out x16.
 #pragma unroll
@@ -514,6 +548,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
                                                        oacc[c], 0, 0, 0);
     }
     bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, ones1024, bacc, 0, 0, 0);
+    // the remaining score groups of tile t+1 share this region: one MFMA per
+    // four vector instructions of the V operand expansion
+#pragma unroll
+    for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
+#pragma unroll
+    for (int j = 0; j < NCOL + 1 + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if ((t % kFlush) == kFlush - 1) flush();
   };
 
@@ -521,20 +565,22 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // t+2 .. t+S-1 are in flight.  Unrolled by two so the score accumulators
   // alternate without copies.
   i32x4_t accA[2][3], accB[2][3];
+  TileWords wA, wB;
   if (ntile > 0) {
     wait_tiles(std::integral_constant<int, S - 2>());  // tile 0
     __syncthreads();
     i32x4_t kb[2][NCK];
     k_operands(smem, kb);
+    tile_words(smem, wA);
 #pragma unroll
     for (int i = 0; i < NGROUP; ++i) score_group(i, kb, accA);
   }
   int t = 0;
   for (; t + 1 < ntile; t += 2) {
-    step(t, accA, accB);
-    step(t + 1, accB, accA);
+    step(t, accA, accB, wA, wB);
+    step(t + 1, accB, accA, wB, wA);
   }
-  if (t < ntile) step(t, accA, accB);
+  if (t < ntile) step(t, accA, accB, wA, wB);
   wait_vmem<0>();  // drain the clamped look-ahead copies
   flush();
 
