@@ -4,15 +4,18 @@ Workload: long-context decode, 4 sequences x 131072 tokens, 64 query heads,
 8 KV heads, head_size 128, bf16 inputs, split-K over 64 segments.  One step =
 write the new token of every sequence into the packed cache (int4_kv_write),
 then one decode step of causal paged attention over the full context
-(int4_paged_attention: split-K kernel + segment reduction).  Several
-independent caches are rotated between steps so that no step reads a cache
-still resident in the 256 MB Infinity Cache.
+(int4_paged_attention: split-K kernel + segment reduction).  Two independent
+caches alternate between steps so that no step reads a cache still resident
+in the 256 MB Infinity Cache.
 
-Prints one JSON line: decode effective KV GB/s (packed K+V bytes of every key
-attended, once per KV head, over the step time), the bulk cache-write rate
-(tokens/s, from a timed full-cache fill), the roofline of the decode kernels
-(HIP events on the launch stream), and the CPU oracle timed on a bounded
-sample on this host.
+Each step is captured once per cache in a HIP graph (the same library calls,
+recorded on the capturing stream) and replayed, so the host never throttles
+the GPU; `--eager` times plain calls instead.  Prints one JSON line: decode
+effective KV GB/s (packed K+V bytes of every key attended, once per KV head,
+over the step time), the bulk cache-write rate (tokens/s, from a timed
+full-cache fill), the roofline of the attention call (HIP events on the
+launch stream around back-to-back calls), and the CPU oracle timed on the
+same workload on this host.
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ import os
 import sys
 import time
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +35,7 @@ import int4_quantized_paged_amd as ik  # noqa: E402
 from int4_quantized_paged_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "decode attn effective KV GB/s (% of HBM peak); int4 cache-write tokens/s"
 NUM_SEGMENTS = 64
 
@@ -85,17 +90,46 @@ def build_buffers(nbufs: int, dev: str):
     return bufs
 
 
-def step(b, ev=None):
+def write_new(b):
     ik.int4_kv_write(b["key_new"], b["value_new"], b["slots_new"], b["cache"], b["signs"])
+
+
+def attend(b):
     w = b["w"]
-    if ev is not None:
-        ev[0].record()
     ik.int4_paged_attention(b["query"], b["cache"], b["cu"], b["su"], 1, w.max_seqlen_k, b["bt"],
                             w.softmax_scale, b["signs"], out=b["out"], num_segments=NUM_SEGMENTS,
                             segm_output=b["segs"][0], segm_max=b["segs"][1],
                             segm_expsum=b["segs"][2])
-    if ev is not None:
-        ev[1].record()
+
+
+def step(b):
+    write_new(b)
+    attend(b)
+
+
+def capture(fn):
+    """Record fn's library calls into a HIP graph (torch.cuda.graph makes the
+    capturing stream current, which is the stream the binding passes)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def check_replay(bufs, graphs):
+    """Replays must reproduce the eager result bit for bit (deterministic kernels)."""
+    for b, g in zip(bufs, graphs):
+        b["out"].zero_()
+        attend(b)
+        torch.cuda.synchronize()
+        ref = b["out"].clone()
+        for _ in range(2):
+            b["out"].zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(b["out"], ref):
+                raise RuntimeError("graph replay differs from the eager attention call")
 
 
 def measure_bulk_write(b, reps: int = 5):
@@ -117,35 +151,105 @@ def measure_bulk_write(b, reps: int = 5):
     return T / t, t, T
 
 
+def _median_event_us(fn, reps):
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def _attention_setup(w, dev, ns, ncaches=1):
+    caches = [ik.empty_cache(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)]
+    _, slots = w.token_set("all")
+    signs = w.signs.to(dev)
+    ik.int4_kv_write(w.key, w.value, slots.to(dev), caches[0], signs)
+    for _ in range(ncaches - 1):
+        caches.append(caches[0].clone())
+    cu, su, bt = w.cu_seqlens_q().to(dev), w.seqused_k().to(dev), w.block_table.to(dev)
+    segs = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns, w.head_size, dev) if ns > 1 else \
+        (None, None, None)
+    out = torch.empty_like(w.query)
+    state = {"i": 0}
+
+    def call():
+        c = caches[state["i"] % len(caches)]
+        state["i"] += 1
+        ik.int4_paged_attention(w.query, c, cu, su, w.max_seqlen_q, w.max_seqlen_k, bt,
+                                w.softmax_scale, signs, out=out, num_segments=ns,
+                                segm_output=segs[0], segm_max=segs[1], segm_expsum=segs[2])
+    return call
+
+
+def other_rows(dev):
+    """The other timed rows of the path, each at its full size: prefill on the
+    chunked-prefill mix (MFMA-bound; TFLOP/s against the dense f16 peak) and
+    decode on the Llama-3-8B-shaped batch (HBM-bound; two cache copies
+    alternate).  Median of hipEvent-timed calls."""
+    rows = {}
+    for d in (128, 64):
+        w = wl.chunked_prefill(device=dev, head_size=d)
+        call = _attention_setup(w, dev, 1)
+        for _ in range(3):
+            call()
+        us = _median_event_us(call, 10)
+        fl = w.attention_flops()
+        rows[f"prefill_d{d}"] = {
+            "workload": f"chunked-prefill mix: 32 seqs, {sum(w.query_lens)} query tokens, "
+                        f"{sum(w.kv_lens)} keys, 32 q / 8 KV heads, d {d}",
+            "us": round(us, 2), "tflops": round(fl / us / 1e6, 1),
+            "mfma_frac": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
+            "algorithmic_gflop": round(fl / 1e9, 2),
+            "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
+        del w, call
+    w = wl.llama3_8b_decode(device=dev)
+    best = None
+    for ns in (1, 2, 4, 8):
+        call = _attention_setup(w, dev, ns, ncaches=2)
+        for _ in range(3):
+            call()
+        us = _median_event_us(call, 20)
+        if best is None or us < best[1]:
+            best = (ns, us)
+        del call
+    kv = w.kv_bytes_attended()
+    rows["llama3_8b_decode"] = {
+        "workload": "64 seqs x 4096 tokens, 32 q / 8 KV heads, d 128 (outlier K channels)",
+        "num_segments": best[0], "us": round(best[1], 2),
+        "GBps": round(kv / best[1] / 1e3, 1), "hbm_frac": round(kv / best[1] / 1e3 / HBM_PEAK_GBS, 4)}
+    return rows
+
+
 def cpu_baseline(b):
-    """The oracle (plain single-threaded C) on a bounded sample of the same
-    workload: one of the 4 sequences, its 131072 tokens encoded, then one
-    decode query of all 64 heads attended over them."""
-    import numpy as np
+    """The oracle (plain single-threaded C) on the same workload: all 524288
+    tokens encoded into the packed cache, then one decode query of all 64
+    heads attended for each of the 4 sequences (textbook fp64 attention)."""
     import oracle
     oracle._load()
     w = b["w"]
     key, value, _ = b["bulk"]
-    L = w.kv_lens[0]
-    sub = wl.Workload(w.name + " seq 0", w.dtype, w.num_q_heads, w.num_kv_heads, w.head_size,
-                      w.num_blocks, [L], [1], [1], w.block_table[:1].clone(), key[:L], value[:L],
-                      w.query[:1], w.signs)
-    kb, vb = wl.bits16(sub.key), wl.bits16(sub.value)
-    qb = wl.bits16(sub.query)
-    _, slots = sub.token_set("all")
+    kb, vb = wl.bits16(key), wl.bits16(value)
+    qb = wl.bits16(w.query)
+    _, slots = w.token_set("all")
     cache = np.zeros(oracle.cache_shape(w.num_blocks, 16, w.num_kv_heads, w.head_size), np.uint8)
     t0 = time.perf_counter()
     oracle.kv_write(kb, vb, "bf16", slots.numpy(), cache, w.signs.numpy())
     t_write = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.attention_plain(qb, "bf16", cache, sub.cu_seqlens_q().numpy(), sub.seqused_k().numpy(),
-                           sub.block_table.numpy(), w.softmax_scale, w.signs.numpy(), w.num_q_heads)
+    oracle.attention_plain(qb, "bf16", cache, w.cu_seqlens_q().numpy(), w.seqused_k().numpy(),
+                           w.block_table.numpy(), w.softmax_scale, w.signs.numpy(), w.num_q_heads)
     t_attn = time.perf_counter() - t0
-    kv = sub.kv_bytes_attended()
-    return {"value": kv / t_attn / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"1 of 4 sequences (131072 keys x 8 KV heads, 64 query heads): plain fp64 "
-                      f"attention {t_attn:.2f} s; its cache write {t_write:.2f} s",
-            "write_tokens_per_s": L / t_write}
+    kv = w.kv_bytes_attended()
+    return {"value": round(kv / t_attn / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload (4 x 131072 keys, 8 KV heads, 64 query heads): plain "
+                      f"fp64 attention {t_attn:.2f} s; its cache write of 524288 tokens "
+                      f"{t_write:.2f} s",
+            "write_tokens_per_s": round(key.shape[0] / t_write, 1)}
 
 
 def main():
@@ -154,6 +258,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-rows", action="store_true",
+                    help="skip the prefill and Llama-3-shaped decode measurements")
+    ap.add_argument("--eager", action="store_true",
+                    help="time plain library calls instead of HIP-graph replays of them")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -181,18 +289,34 @@ def main():
     w = bufs[0]["w"]
     kv_bytes = w.kv_bytes_attended()
 
+    if args.eager:
+        run = [lambda b=b: step(b) for b in bufs]
+        run_attn = [lambda b=b: attend(b) for b in bufs]
+    else:
+        graphs = [capture(lambda b=b: step(b)) for b in bufs]
+        attn_graphs = [capture(lambda b=b: attend(b)) for b in bufs]
+        check_replay(bufs, attn_graphs)
+        run = [g.replay for g in graphs]
+        run_attn = [g.replay for g in attn_graphs]
+
     for i in range(args.warmup):
-        step(bufs[i % nbufs])
+        run[i % nbufs]()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(bufs[i % nbufs], evs[i])
+        run[i % nbufs]()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    attn_s = sum(a.elapsed_time(b) for a, b in evs) / 1e3 / args.steps
+
+    # attention call alone: HIP events on the launch stream around back-to-back calls
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        run_attn[i % nbufs]()
+    e1.record()
+    e1.synchronize()
+    attn_s = e0.elapsed_time(e1) / 1e3 / args.steps
 
     wr_tps, wr_t, wr_T = measure_bulk_write(bufs[0])
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
@@ -206,7 +330,8 @@ def main():
         "config": {"workload": "long-context decode: 4 seqs x 131072 tokens, 64 q / 8 KV heads, "
                                "head_size 128, bf16 K/V/Q N(0,1), block_size 16, split-K 64 "
                                "segments + segment reduction; step = write 4 new tokens + decode",
-                   "global_batch": 4, "seq_len": 131072, "parallelism": "none (1 GPU)"},
+                   "global_batch": 4, "seq_len": 131072, "parallelism": "none (1 GPU)",
+                   "launch": "eager" if args.eager else "hip graph replay"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "write_tokens_per_s": round(wr_tps, 1),
         "write_bulk": {"tokens": wr_T, "seconds": wr_t,
@@ -217,6 +342,8 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": kv_bytes,
                      "avg_launch_us": round(attn_s * 1e6, 2)},
     }
+    if not args.no_other_rows:
+        res["other_rows"] = other_rows(dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(bufs[0])
     else:

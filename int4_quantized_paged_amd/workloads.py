@@ -121,6 +121,15 @@ class Workload:
         R = self.head_size // 2 + 4
         return sum(self.kv_lens) * self.num_kv_heads * 2 * R
 
+    def attention_flops(self) -> int:
+        """Algorithmic flops of causal attention: 2*d for Q.K and 2*d for P.V
+        per (query row, visible key, query head).  Query i of sequence b sees
+        L_b - q_b + i + 1 keys."""
+        pairs = 0
+        for L, q in zip(self.kv_lens, self.query_lens):
+            pairs += q * (L - q) + q * (q + 1) // 2
+        return pairs * self.num_q_heads * 4 * self.head_size
+
     def write_bytes(self, which: str = "new") -> int:
         """Algorithmic bytes of the cache write: K and V inputs read, packed
         rows written, one int64 slot per token."""
