@@ -64,6 +64,10 @@ def _kernel_hash() -> str:
     return h.hexdigest()
 
 
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def build_buffers(nbufs: int, dev: str):
     bufs = []
     for i in range(nbufs):
@@ -286,6 +290,7 @@ def main():
     ik.load_library()
     nbufs = 2  # 2 x 570 MB > 256 MB Infinity Cache
     bufs = build_buffers(nbufs, dev)
+    log("caches filled")
     w = bufs[0]["w"]
     kv_bytes = w.kv_bytes_attended()
 
@@ -318,6 +323,7 @@ def main():
     e1.synchronize()
     attn_s = e0.elapsed_time(e1) / 1e3 / args.steps
 
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_s * 1e6:.2f} us")
     wr_tps, wr_t, wr_T = measure_bulk_write(bufs[0])
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = kv_bytes / attn_s / 1e9
@@ -344,8 +350,10 @@ def main():
     }
     if not args.no_other_rows:
         res["other_rows"] = other_rows(dev)
+        log("other rows measured")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(bufs[0])
+        log("oracle baseline timed")
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
