@@ -25,9 +25,11 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           # packed fp32 ops are never emitted (see the project's design notes)
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I" + os.path.join(HERE, "..", "include")]
-# The LDS-staged decode kernel never produces NaN scores (masked keys are
-# selected as -inf, not computed), so its maxima need no NaN quieting.
-PER_FILE = {"write.hip": ["-ffp-contract=off"], "decode_lds.hip": ["-fno-honor-nans"]}
+# The LDS-staged decode kernel and the prefill kernel never produce NaN
+# logits (masked keys are selected as -inf, not computed), so their maxima
+# need no NaN quieting.
+PER_FILE = {"write.hip": ["-ffp-contract=off"], "decode_lds.hip": ["-fno-honor-nans"],
+            "prefill.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

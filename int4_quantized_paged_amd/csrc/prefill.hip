@@ -1,96 +1,142 @@
 // INT4 paged attention for prefill / mixed batches (query lengths > 1), gfx950.
 //
 // Same method as the decode kernel (PR #40633's description: Q rotated into
-// the cache's domain and split to match the nibble order, split-dot score with
-// a sum(Q) * zp correction, online softmax, per-stream accumulators; causal
-// only per the PR #40835 report's risk list), organised for many query rows:
+// the cache's domain, split-dot score with a sum(Q) * zp correction, online
+// softmax, per-stream accumulators; causal only per the PR #40835 report's
+// risk list), organised for many query rows per key:
 //
-// One workgroup (4 waves) owns one (sequence, KV head, tile of 64/G query
-// tokens); its 64 rows are (token, query head) pairs, 16 per wave, so every
-// 16x16x32 f16 MFMA tile is fully used.  Key tiles of 32 keys (2 cache blocks)
-// are fetched once per workgroup (prefetched into registers one tile ahead),
-// expanded from nibbles to f16 and stored in LDS:
-//   K as [key][d] in the operand order of the score MFMA (padded rows),
-//   V transposed as [d][key slot] for the P.V MFMA (xor-swizzled 16-byte chunks),
-// so all four waves read their MFMA operands from LDS.  Softmax weights go
-// back through a small per-wave LDS tile to become the A operand of P.V.
+//  * One workgroup (8 waves) owns one (sequence, KV head, tile of 128/G query
+//    tokens): 128 rows of (token, query head).  Waves 0-3 take the even key
+//    tiles and waves 4-7 the odd ones (a split of the key range inside the
+//    workgroup, merged through LDS at the end), so the longest contexts run as
+//    two chains and every SIMD holds two waves; each wave owns 32 rows as two
+//    16-row MFMA tiles, so each K/V tile read from LDS feeds two row tiles.
+//  * The K and V rows of the head (R bytes at the cache's token stride) are
+//    copied HBM -> LDS with global_load_lds_dword into an 8-stage ring, six
+//    tiles ahead of the math; wave q of a group copies (block q/2, K|V q%2)
+//    of each of the group's two-block tiles.  Rows land as 17-dword (d = 128) or 9-dword (d = 64)
+//    records, an odd stride, so the per-key reads of 16 lanes hit 16 banks.
+//  * Codes enter the f16 MFMAs as raw bit patterns: (w & 0x000F000F) is a pair
+//    of f16 subnormals code * 2^-24, (w & 0x00F000F0) is 16 * code * 2^-24;
+//    products and sums stay exact in fp32 and the 2^24 (and the 16) are folded
+//    into per-row and per-column constants.  No bias, no subtraction.
+//  * Q . K^T: Q' as f16 hi + lo (22 significant bits), both against the same
+//    K operand.  P . V: softmax weights times the V scale (f16) as the A
+//    operand, through a per-wave LDS tile, against V codes expanded per lane
+//    from one dword of each of 8 keys.
+//  * Workgroups are numbered so that the KV heads of one (sequence, tile) run
+//    on the same XCD (the heads of a token share 128-byte lines in L2), and
+//    later query tiles, which see more keys, are dispatched first.
 #include "device_common.h"
 #include "launch.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace int4kv {
 
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 4.0f;  // headroom of the softmax reference maximum (log2 units)
+constexpr int kStages = 8;
 
-__device__ __forceinline__ half8_t unpack8(uint32_t w) {
-  u32x4_t r;
-  r.x = nib_pair_f16(w);
-  r.y = nib_pair_f16(w >> 4);
-  r.z = nib_pair_f16(w >> 8);
-  r.w = nib_pair_f16(w >> 12);
-  return __builtin_bit_cast(half8_t, r);
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// 4 bytes per lane from global memory (uniform base + 32-bit lane offset)
+// into LDS at M0 + lane * 4.
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
 }
 
-__device__ __forceinline__ uint32_t ld32(const uint8_t* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Slot of tile-local key kk (0..31) in the P.V contraction: slots 8g..8g+7
-// hold keys 4g + i (even slots) and 16 + 4g + i (odd slots), i = 0..3.
-__device__ __forceinline__ int key_slot(int kk) {
-  return 8 * ((kk & 15) >> 2) + 2 * (kk & 3) + (kk >> 4);
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Byte offset of (row d, slot chunk ch) in the transposed V tile: 64-byte rows,
-// the 16-byte chunk index xor-swizzled by bits 3..4 of d.
-__device__ __forceinline__ int vt_off(int d, int ch) { return d * 64 + 16 * (ch ^ ((d >> 3) & 3)); }
+// maximum over the 16 lanes of a DPP row (logits are finite or -inf)
+__device__ __forceinline__ float max16(float x) {
+  x = fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8
+  x = fmaxf(x, dpp_f32<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+  return x;
+}
 
-template <int D>
-struct KVRegs {
-  uint32_t k0, k1, v0, v1;  // dword w of keys kk and kk + 16 (K and V)
-  uint32_t sw;              // a scale word (K or V) of one key, for threads that own one
+template <int D, int G>
+struct PGeo {
+  static constexpr int R = D / 2 + 4;             // packed row bytes
+  static constexpr int RW = R / 4;                // dwords per row (17 or 9)
+  static constexpr int DW = D / 8;                // code dwords per row
+  static constexpr int NIB = (16 * RW + 63) / 64; // copies per (block, K|V) image
+  static constexpr uint32_t HALF = NIB * 256;     // LDS bytes of one (block, K|V) image
+  static constexpr uint32_t STAGE = 4 * HALF;     // two blocks, K and V
+  static constexpr uint32_t RING = kStages * STAGE;
+  static constexpr uint32_t QSTAGE = 128 * D * 2 * 2;  // hi and lo, operand order
+  static constexpr uint32_t WBASE = RING > QSTAGE ? RING : QSTAGE;
+  static constexpr uint32_t WTILE = 2 * 16 * 64;  // per wave: 2 row tiles x 16 rows x 32 keys f16
+  // odd-tile group's state for the final merge: per lane 8 m, 8 l, 8 corr, 16*NCOL/2 O
+  static constexpr uint32_t MERGE = 4 * 64 * (24 + 8 * (D / 16)) * 4;
+  static constexpr uint32_t LOW = WBASE > MERGE ? WBASE : MERGE;
+  static constexpr uint32_t TOTAL = LOW + 8 * WTILE;
+  static constexpr int TQ = 128 / G;              // query tokens per workgroup
 };
 
 template <bool BF16, int D, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(512) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, uint16_t* __restrict__ out,
     const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
-    const float* __restrict__ signs) {
-  constexpr int NCH = D / 32;
-  constexpr int NCOL = D / 16;
-  constexpr int DW = D / 8;
-  constexpr int R = D / 2 + 4;
-  constexpr int TQ = 64 / G;        // query tokens per workgroup
-  constexpr int KROW = D * 2 + 16;  // padded bytes per key row of the K tile
-  constexpr int EPL = D / 4;        // prologue: elements per lane (4 lanes per row)
+    const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq) {
+  using PG = PGeo<D, G>;
+  constexpr int R = PG::R, RW = PG::RW, DW = PG::DW, NIB = PG::NIB;
+  constexpr int NCH = D / 32;   // f16 MFMA k-chunks of the score
+  constexpr int NCOL = D / 16;  // P.V column tiles
+  constexpr int TQ = PG::TQ;
+  constexpr int EPL = D / 2;    // prologue: elements per lane (2 lanes per row)
 
-  __shared__ __align__(16) _Float16 s_qhi[64 * D];
-  __shared__ __align__(16) _Float16 s_qlo[64 * D];
-  __shared__ float s_qinfo[64 * 2];
-  __shared__ __align__(16) unsigned char s_k[32 * KROW];
-  __shared__ __align__(16) unsigned char s_vt[D * 64];
-  __shared__ uint32_t s_kw[32], s_vw[32];
-  __shared__ __align__(16) uint32_t s_w[4][16 * 16];  // per wave: W [16 rows][32 slots] f16
-
+  extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int qt = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave >> 2;  // key-tile group: 0 takes even tiles, 1 odd tiles
+  const int wq = wave & 3;   // row quarter: rows 32 wq .. 32 wq + 31
+  const int col = lane & 15, g = lane >> 4;
+
+  // ---- workgroup -> (sequence, query tile, KV head): the heads of one group
+  // share the XCD (id % 8), and each sequence's last query tile comes first
+  const int id = blockIdx.x;
+  const int rr = id >> 3;
+  const int h = rr % num_kv_heads;
+  const int grp = (rr / num_kv_heads) * 8 + (id & 7);
+  if (grp >= num_seqs * tiles_per_seq) return;
+  const int b = grp / tiles_per_seq;
+  const int qt = tiles_per_seq - 1 - grp % tiles_per_seq;
   const int q0 = cu_seqlens_q[b];
   const int qlen = cu_seqlens_q[b + 1] - q0;
   if (qt * TQ >= qlen) return;  // uniform over the workgroup
   const int L = seqused_k[b];
   const int t_hi = min((qt + 1) * TQ, qlen) - 1;  // last valid token of this tile
-  const int pos_max = L - qlen + t_hi;
-  const int nkeys = pos_max + 1;
+  const int nkeys = L - qlen + t_hi + 1;          // keys the last row sees
   const int ntiles = nkeys > 0 ? (nkeys + 31) / 32 : 0;
   const int nblk = (nkeys + kBlockSize - 1) / kBlockSize;
+  const int pos_lo = L - qlen + qt * TQ;          // position of the first row's token
 
-  // ---- prologue: rotate the 64 rows of Q (4 lanes per row), split into f16 hi + lo
-  {
-    const int row = 16 * wave + (lane >> 2), s = lane & 3;
+  // ---- prologue: q' = H (signs * q), normalised per row to |q'| < 2^10, split
+  // into f16 hi + lo and staged in LDS in the MFMA operand order
+  _Float16* sq = reinterpret_cast<_Float16*>(smem);  // [128 rows][2][NCH][4][8]
+  float* sinfo = reinterpret_cast<float*>(smem + PG::LOW);  // [128 + 4], reuses the W tiles
+  if (kg == 0) {  // the even group rotates Q; both groups read it
+    const int row = 32 * wq + (lane >> 1), s = lane & 1;
     const int tq = min(qt * TQ + row / G, qlen - 1);  // rows past the end repeat the last token
     const int qh = row % G;
     const uint16_t* qp = q + (int64_t)(q0 + tq) * q_stride + (int64_t)(h * G + qh) * D + s * EPL;
@@ -108,268 +154,394 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       }
     }
 #pragma unroll
-    for (int m = 1; m < 4; m <<= 1) {
-      const bool upper = (s & m) != 0;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float p = shfl_xor_rt(x[e], m);
-        x[e] = upper ? p - x[e] : x[e] + p;
-      }
+    for (int e = 0; e < EPL; ++e) {
+      const float p = shfl_xor<1>(x[e]);
+      x[e] = s ? p - x[e] : x[e] + p;
     }
+    // one exponent for the wave's 32 rows, so the logit scale is one constant
+    // per wave (a row far below the wave's maximum keeps fewer significant
+    // bits, but its logits, and their absolute error, are as small)
     float mx = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) mx = fmaxf(mx, fabsf(x[e]));
-    mx = fmaxf(mx, shfl_xor<1>(mx));
-    mx = fmaxf(mx, shfl_xor<2>(mx));
-    const int ex = mx > 0.f ? ilogbf(mx) + 1 : 0;
-    const float nrm = ldexpf(1.0f, -ex);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) mx = fmaxf(mx, shfl_xor_rt(mx, m));
+    const int ex = mx > 0.f ? ilogbf(mx) + 1 : 0;  // |q'| * 2^(10-ex) < 2^10
+    const float nrm = ldexpf(1.0f, 10 - ex);
     float sum = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float v = x[e] * nrm;
-      const _Float16 hv = (_Float16)v;
-      const _Float16 lv = (_Float16)(v - (float)hv);
-      s_qhi[row * D + s * EPL + e] = hv;
-      s_qlo[row * D + s * EPL + e] = lv;
-      sum += (float)hv + (float)lv;
+    for (int e8 = 0; e8 < EPL / 8; ++e8) {
+      // elements el = s*EPL + 8*e8 + j sit in chunk el/32, lane group (el%32)/8
+      // and slot {0,2,4,6,1,3,5,7}[j]; slots of odd j meet codes scaled by 16
+      half8_t hi8, lo8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = x[8 * e8 + j] * nrm;
+        const _Float16 hv = (_Float16)v;
+        const _Float16 lv = (_Float16)(v - (float)hv);
+        sum += (float)hv + (float)lv;
+        const int slot = ((j & 3) << 1) | (j >> 2);
+        hi8[slot] = (j & 1) ? (_Float16)((float)hv * 0.0625f) : hv;
+        lo8[slot] = (j & 1) ? (_Float16)((float)lv * 0.0625f) : lv;
+      }
+      const int el = s * EPL + 8 * e8;
+      const int off = ((row * 2 + 0) * NCH + el / 32) * 32 + ((el % 32) / 8) * 8;
+      *reinterpret_cast<half8_t*>(sq + off) = hi8;
+      *reinterpret_cast<half8_t*>(sq + off + NCH * 32) = lo8;
     }
     sum += shfl_xor<1>(sum);
-    sum += shfl_xor<2>(sum);
-    if (s == 0) {
-      s_qinfo[2 * row] = sum;
-      s_qinfo[2 * row + 1] = scale_log2 * ldexpf(1.0f, ex);
-    }
+    if (s == 0) sinfo[row] = sum * 5.9604644775390625e-08f;  // sum(q') in 2^-24 code units
+    if (lane == 0) sinfo[128 + wq] = scale_log2 * ldexpf(1.0f, ex - 10 + 24);
   }
   __syncthreads();
 
-  const int col = lane & 15, g = lane >> 4;
-  half8_t qa_hi[NCH], qa_lo[NCH];
-  {
-    const int row = 16 * wave + col;
+  // A operands of the score: row tile i = rows 32w + 16i + col
+  half8_t qa_hi[2][NCH], qa_lo[2][NCH];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * wq + 16 * i + col;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = 8 * (g * NCH + c) + (j >> 1) + 4 * (j & 1);
-        qa_hi[c][j] = s_qhi[row * D + d];
-        qa_lo[c][j] = s_qlo[row * D + d];
-      }
+      qa_hi[i][c] = *reinterpret_cast<const half8_t*>(sq + ((row * 2 + 0) * NCH + c) * 32 + g * 8);
+      qa_lo[i][c] = *reinterpret_cast<const half8_t*>(sq + ((row * 2 + 1) * NCH + c) * 32 + g * 8);
     }
   }
-  // per-row constants in the accumulator layout: register v <-> row 16*wave + 4g + v
-  float qsum[4], c0[4];
-  int pos[4];
+  // per-row constants in the accumulator layout: register v of row tile i is
+  // row 32w + 16i + 4g + v
+  float qsum[2][4];
+  int pos[2][4];
+  const float c0 = sinfo[128 + wq];  // logit units (base 2) per unit of S
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int row = 16 * wave + 4 * g + v;
-    qsum[v] = s_qinfo[2 * row];
-    c0[v] = s_qinfo[2 * row + 1];
-    const int tq = min(qt * TQ + row / G, qlen - 1);
-    pos[v] = L - qlen + tq;
-  }
-
-  float m_run[4], l_run[4], corr[4];
-  float4_t oacc[NCOL];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    m_run[v] = -INFINITY;
-    l_run[v] = 0.f;
-    corr[v] = 0.f;
-  }
-#pragma unroll
-  for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  // ---- cooperative tile loads: thread -> (key pair kk / kk + 16, dword w)
-  const int64_t tok_stride = (int64_t)num_kv_heads * R;
-  const int64_t blk_bytes = (int64_t)kBlockSize * tok_stride;
-  const int64_t head_off = (int64_t)h * R;
-  const int32_t* bt = block_table + (int64_t)b * bt_stride;
-  const bool has_item = tid < 16 * DW;
-  const int it_kk = tid & 15, it_w = (tid >> 4) % DW;
-  // scale words: threads [0, 32) take K of key tid, [32, 64) V of key tid - 32
-  // when D == 128; with D == 64 the idle threads [128, 192) do it instead.
-  const int sw_base = (D == 128) ? 0 : 128;
-  const bool has_sw = tid >= sw_base && tid < sw_base + 64;
-  const int sw_key = (tid - sw_base) & 31, sw_v = ((tid - sw_base) >> 5) & 1;
-
-  auto load = [&](int tile, KVRegs<D>& r) {
-    const int bi0 = 2 * tile, bi1 = min(2 * tile + 1, nblk - 1);
-    const int64_t p0 = bt[bi0], p1 = bt[bi1];
-    if (has_item) {
-      const uint8_t* r0 = cache + p0 * 2 * blk_bytes + it_kk * tok_stride + head_off + 4 * it_w;
-      const uint8_t* r1 = cache + p1 * 2 * blk_bytes + it_kk * tok_stride + head_off + 4 * it_w;
-      r.k0 = ld32(r0);
-      r.k1 = ld32(r1);
-      r.v0 = ld32(r0 + blk_bytes);
-      r.v1 = ld32(r1 + blk_bytes);
-    }
-    if (has_sw) {
-      const int64_t p = (sw_key >> 4) ? p1 : p0;
-      r.sw = ld32(cache + p * 2 * blk_bytes + sw_v * blk_bytes + (sw_key & 15) * tok_stride +
-                  head_off + D / 2);
-    }
-  };
-  auto store = [&](const KVRegs<D>& r) {
-    if (has_item) {
-      *reinterpret_cast<half8_t*>(s_k + it_kk * KROW + 16 * it_w) = unpack8(r.k0);
-      *reinterpret_cast<half8_t*>(s_k + (it_kk + 16) * KROW + 16 * it_w) = unpack8(r.k1);
-      const uint32_t ylo = (r.v0 & 0xFFFFu) | (r.v1 << 16);
-      const uint32_t yhi = (r.v0 >> 16) | (r.v1 & 0xFFFF0000u);
-      const int sl = key_slot(it_kk);  // even; key it_kk + 16 takes sl + 1
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * it_w + e;
-        const uint32_t y = e < 4 ? ylo : yhi;
-        *reinterpret_cast<uint32_t*>(s_vt + vt_off(d, sl >> 3) + 2 * (sl & 7)) =
-            nib_pair_f16(y >> (4 * (e & 3)));
-      }
-    }
-    if (has_sw) (sw_v ? s_vw : s_kw)[sw_key] = r.sw;
-  };
-
-  KVRegs<D> regs;
-  if (ntiles > 0) load(0, regs);
-  uint32_t* wl = s_w[wave];
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // previous tile's readers are done
-    store(regs);
-    __syncthreads();
-    if (t + 1 < ntiles) load(t + 1, regs);
-
-    // scores for keys 16n + col of this tile
-    float4_t sacc[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const half8_t kb =
-            *reinterpret_cast<const half8_t*>(s_k + (16 * n + col) * KROW + 16 * (g * NCH + c));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], kb, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], kb, acc, 0, 0, 0);
-      }
-      sacc[n] = acc;
-    }
-    float sK[2], zK[2], sV[2], zV[2];
-    int key[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const uint32_t kw = s_kw[16 * n + col], vw = s_vw[16 * n + col];
-      sK[n] = as_float(kw & 0xFFFFFFF0u);
-      zK[n] = (float)(kw & 0xFu);
-      sV[n] = as_float(vw & 0xFFFFFFF0u);
-      zV[n] = (float)(vw & 0xFu);
-      key[n] = 32 * t + 16 * n + col;
-    }
-    uint32_t wpk[4];
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float z[2];
-      bool ok[2];
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        ok[n] = key[n] <= pos[v];
-        const float tt = sacc[n][v] - zK[n] * qsum[v];
-        z[n] = ok[n] ? tt * (sK[n] * c0[v]) : -INFINITY;
-      }
-      float tmax = fmaxf(z[0], z[1]);
-      tmax = fmaxf(tmax, shfl_xor<1>(tmax));
-      tmax = fmaxf(tmax, shfl_xor<2>(tmax));
-      tmax = fmaxf(tmax, shfl_xor<4>(tmax));
-      tmax = fmaxf(tmax, shfl_xor<8>(tmax));
-      const float mnew = fmaxf(m_run[v], tmax);
-      const bool none = mnew == -INFINITY;  // row sees no key yet
-      const float alpha = none ? 1.0f : exp2f(m_run[v] - mnew);
-      m_run[v] = mnew;
-      const float p0 = ok[0] ? exp2f(z[0] - mnew) : 0.f;
-      const float p1 = ok[1] ? exp2f(z[1] - mnew) : 0.f;
-      const _Float16 w0 = (_Float16)(p0 * sV[0]);
-      const _Float16 w1 = (_Float16)(p1 * sV[1]);
-      l_run[v] = l_run[v] * alpha + (p0 + p1);
-      corr[v] = corr[v] * alpha + ((float)w0 * zV[0] + (float)w1 * zV[1]);
-#pragma unroll
-      for (int c = 0; c < NCOL; ++c) oacc[c][v] *= alpha;
-      wpk[v] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+      const int row = 32 * wq + 16 * i + 4 * g + v;
+      qsum[i][v] = sinfo[row];
+      pos[i][v] = L - qlen + min(qt * TQ + row / G, qlen - 1);
     }
-    // W [row 4g + v][slot of key col, slot + 1 for key 16 + col] through LDS
-    {
-      const int sl = key_slot(col);
+  __syncthreads();  // the staged Q and the row constants are consumed; the ring may start
+
+  // ---- K/V copies: wave q of group k copies (block q/2, K|V q%2) of tiles
+  // 2s + k
+  const uint32_t tok_g = (uint32_t)num_kv_heads * R;
+  const uint32_t half_g = 16 * tok_g;
+  const uint32_t pair_g = 2 * half_g;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
+  const int32_t* bt = block_table + (int64_t)b * bt_stride;
+  const int my_blk = wq >> 1;
+  const uint32_t my_half = (uint32_t)(wq & 1) * half_g + (uint32_t)h * R;
+  uint32_t goff[NIB];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) wl[(4 * g + v) * 16 + (sl >> 1)] = wpk[v];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const half8_t wop = *reinterpret_cast<const half8_t*>(&wl[col * 16 + 4 * g]);
+  for (int i = 0; i < NIB; ++i) {
+    const int idx = min(i * 64 + lane, 16 * RW - 1);  // padding lanes re-read the last dword
+    goff[i] = (uint32_t)(idx / RW) * tok_g + (uint32_t)(idx % RW) * 4;
+  }
+  uint32_t nid = 0;  // block id of the next tile to copy, read one step ahead
+  auto load_id = [&](int tile) { nid = (uint32_t)bt[min(2 * tile + my_blk, nblk - 1)]; };
+  auto issue = [&](int tile) {  // nid holds this tile's block id for this wave
+    const uint8_t* p = cache + (uint64_t)nid * pair_g + my_half;
+    const uint32_t sb = lds0 + (uint32_t)(tile % kStages) * PG::STAGE + (uint32_t)wq * PG::HALF;
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) {
-      const half8_t vb = *reinterpret_cast<const half8_t*>(s_vt + vt_off(16 * c + col, g));
-      oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, vb, oacc[c], 0, 0, 0);
+    for (int i = 0; i < NIB; ++i) dma4(p, goff[i], sb + (uint32_t)i * 256);
+  };
+
+  float m_run[2][4], thr[2][4], l_run[2][4], corr[2][4];
+  float4_t oacc[2][NCOL];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      // a finite floor instead of -inf: a row that has seen no key (or a group
+      // that got only masked keys) then gives p = 0, never 2^(-inf + inf)
+      m_run[i][v] = -1e30f;
+      thr[i][v] = -1e30f;
+      l_run[i][v] = 0.f;
+      corr[i][v] = 0.f;
     }
-    __builtin_amdgcn_wave_barrier();  // W tile is rewritten next iteration
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) oacc[i][c] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- finalise and rotate back; register v of column tile c holds row
-  // 16*wave + 4g + v, d = 16c + col
+  // per-lane LDS byte offsets inside a stage (loop invariant)
+  const uint32_t krow = (uint32_t)col * RW * 4;  // key col's record in a (block, K) image
+  uint32_t k_off[NCH];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    float lv = l_run[v], cv = corr[v];
-    lv += shfl_xor<1>(lv);
-    lv += shfl_xor<2>(lv);
-    lv += shfl_xor<4>(lv);
-    lv += shfl_xor<8>(lv);
-    cv += shfl_xor<1>(cv);
-    cv += shfl_xor<2>(cv);
-    cv += shfl_xor<4>(cv);
-    cv += shfl_xor<8>(cv);
-    const float inv_l = lv > 0.f ? 1.0f / lv : 0.f;
-    float o[NCOL];
+  for (int c = 0; c < NCH; ++c) k_off[c] = krow + (uint32_t)(4 * c + g) * 4;
+  const uint32_t s_off = krow + (uint32_t)(RW - 1) * 4;  // scale word
+  uint32_t v_off[8];  // slot j = 2i + n <-> key 16n + 4g + i
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) o[c] = (oacc[c][v] - cv) * inv_l;
+  for (int j = 0; j < 8; ++j) {
+    const int n = j & 1, t = 4 * g + (j >> 1);
+    v_off[j] = (uint32_t)(2 * n + 1) * PG::HALF + (uint32_t)t * RW * 4 + (uint32_t)(col % DW) * 4;
+  }
+  unsigned char* wt = smem + PG::LOW + wave * PG::WTILE;
+  uint32_t wr_off[4];  // writer: row 4g + v, dword col
 #pragma unroll
-    for (int span = 1; span < NCOL; span <<= 1) {  // d spans 16, 32, 64 over c
+  for (int v = 0; v < 4; ++v) wr_off[v] = (uint32_t)(4 * g + v) * 64 + 4 * col;
+  const uint32_t rd_off = (uint32_t)col * 64 + 16 * g;  // reader: row col, dwords 4g..4g+3
+  const int noff = (D == 64) ? 4 * (col >> 3) : 0;      // nibble offset of this lane's V dword
+
+  // steps s = 0 .. nsteps-1 process tiles 2s (even group) and 2s+1 (odd
+  // group); each group keeps kPairs - 1 of its own tiles in flight.  A tile
+  // past the last one (odd count) is a clamped copy whose keys are all masked.
+  constexpr int kPairs = kStages / 2;
+  const int nsteps = (ntiles + 1) / 2;
+  if (nsteps > 0) {
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) {
-        if (c & span) continue;
-        const float a = o[c], bb = o[c + span];
-        o[c] = a + bb;
-        o[c + span] = a - bb;
+    for (int i = 0; i < kPairs - 1; ++i) {
+      load_id(2 * i + kg);
+      issue(2 * i + kg);
+    }
+    load_id(2 * (kPairs - 1) + kg);
+  }
+
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
+    const int t = 2 * sidx + kg;
+    wait_vmem<(kPairs - 2) * NIB>();  // this wave's copies of tile t have landed
+    __syncthreads();                  // ... and everyone's; everyone is done with step s-1
+    issue(t + 2 * (kPairs - 1));      // into the stage of tile t-2 (clamped to the last block)
+    load_id(t + 2 * kPairs);
+    const unsigned char* st = smem + (uint32_t)(t % kStages) * PG::STAGE;
+
+    // K operands: raw code dword (block n, chunk c) -> 4 dwords of f16 subnormals
+    half8_t kb[2][NCH];
+    uint32_t kw[2], vw[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + k_off[c]);
+        const uint32_t w8 = w >> 8;
+        u32x4_t r;
+        r[0] = w & 0x000F000Fu;
+        r[1] = w & 0x00F000F0u;
+        r[2] = w8 & 0x000F000Fu;
+        r[3] = w8 & 0x00F000F0u;
+        kb[n][c] = __builtin_bit_cast(half8_t, r);
       }
+      kw[n] = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + s_off);
+      vw[n] = *reinterpret_cast<const uint32_t*>(st + (2 * n + 1) * PG::HALF + s_off);
+    }
+    uint32_t va[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
+
+    // scores: S[i][n] for row tile i, keys 16n + col (sum of q' * code * 2^-24)
+    float4_t sacc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        float4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[i][c], kb[n][c], a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[i][c], kb[n][c], a, 0, 0, 0);
+        }
+        sacc[i][n] = a;
+      }
+
+    // online softmax (base 2) per row; keys past a row's position are masked
+    const bool masked = 32 * t + 31 > pos_lo;  // uniform: only tiles near the diagonal
+    float sKc[2], zK[2], sV[2], zV[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      sKc[n] = as_float(kw[n] & 0xFFFFFFF0u) * c0;
+      zK[n] = (float)(kw[n] & 0xFu);
+      sV[n] = as_float(vw[n] & 0xFFFFFFF0u);
+      zV[n] = (float)(vw[n] & 0xFu);
+    }
+    // logits in base-2 units; the reference maximum m of a row only moves
+    // when a logit exceeds it by more than kLazy (so p = 2^(z - m) <= 2^kLazy),
+    // which is detected per logit against thr = m + kLazy; the row maxima are
+    // only reduced on the rare tiles where that happens
+    float z[2][4][2];
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          float zz = fmaf(-zK[n], qsum[i][v], sacc[i][n][v]) * sKc[n];
+          if (masked) zz = (32 * t + 16 * n + col <= pos[i][v]) ? zz : -INFINITY;
+          z[i][v][n] = zz;
+          over |= zz > thr[i][v];
+        }
+    if (__any(over)) {  // bring l, corr and O to the new references first
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float tmax = max16(fmaxf(z[i][v][0], z[i][v][1]));
+          const bool up = tmax > thr[i][v];
+          const float alpha = up ? __builtin_amdgcn_exp2f(m_run[i][v] - tmax) : 1.0f;
+          m_run[i][v] = up ? tmax : m_run[i][v];
+          thr[i][v] = m_run[i][v] + kLazy;
+          l_run[i][v] *= alpha;
+          corr[i][v] *= alpha;
+#pragma unroll
+          for (int c = 0; c < NCOL; ++c) oacc[i][c][v] *= alpha;
+        }
     }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {  // d spans 1, 2, 4, 8 over col
-      const bool upper = (col & m) != 0;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) {
-        const float p = shfl_xor_rt(o[c], m);
-        o[c] = upper ? p - o[c] : o[c] + p;
+      for (int v = 0; v < 4; ++v) {
+        const float p0 = __builtin_amdgcn_exp2f(z[i][v][0] - m_run[i][v]);
+        const float p1 = __builtin_amdgcn_exp2f(z[i][v][1] - m_run[i][v]);
+        half2_t wp;
+        wp[0] = (_Float16)(p0 * sV[0]);
+        wp[1] = (_Float16)(p1 * sV[1]);
+        l_run[i][v] += p0 + p1;
+        corr[i][v] = fmaf((float)wp[1], zV[1], fmaf((float)wp[0], zV[0], corr[i][v]));
+        *reinterpret_cast<half2_t*>(wt + i * 1024 + wr_off[v]) = wp;
       }
+    // weights in the A layout, read back from this wave's W tiles (LDS
+    // operations of one wave complete in order)
+    half8_t wop[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wop[i] = *reinterpret_cast<const half8_t*>(wt + i * 1024 + rd_off);
+
+    // V operands (shared by both row tiles) and O += W V.  Column tile c uses
+    // nibble c (+ noff) of the lane's dword of each slot key.
+    uint32_t ylo[4], yhi[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ylo[k] = __builtin_amdgcn_perm(va[2 * k + 1], va[2 * k], 0x05040100u);  // a.b01 b.b01
+      yhi[k] = __builtin_amdgcn_perm(va[2 * k + 1], va[2 * k], 0x07060302u);  // a.b23 b.b23
     }
-    const int row = 16 * wave + 4 * g + v;
-    const int tq = qt * TQ + row / G;
-    if (tq < qlen) {
-      const int qg = h * G + row % G;
-      uint16_t* dst = out + ((int64_t)(q0 + tq) * num_q_heads + qg) * D;
-      const float invD = 1.0f / (float)D;
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) {
-        const int d = 16 * c + col;
-        dst[d] = from_f32<BF16>(o[c] * signs[d] * invD);
+    for (int c = 0; c < NCOL; ++c) {
+      const int nib = c + noff;
+      u32x4_t vb;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t y = (nib < 4) ? ylo[k] : yhi[k];
+        const uint32_t ys = (nib & 2) ? (y >> 8) : y;
+        vb[k] = ys & ((nib & 1) ? 0x00F000F0u : 0x000F000Fu);
       }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], __builtin_bit_cast(half8_t, vb),
+                                                            oacc[i][c], 0, 0, 0);
     }
   }
+  wait_vmem<0>();  // drain the clamped look-ahead copies
+
+  // ---- merge the odd-tile group into the even one (same rows, wave q + 4 ->
+  // wave q), through LDS; per-lane partial sums are merged before reduction
+  __syncthreads();  // the ring is no longer read
+  {
+    float* mg = reinterpret_cast<float*>(smem) + (size_t)(wq * 64 + lane) * (24 + 8 * NCOL);
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          mg[(i * 4 + v) * 3 + 0] = m_run[i][v];
+          mg[(i * 4 + v) * 3 + 1] = l_run[i][v];
+          mg[(i * 4 + v) * 3 + 2] = corr[i][v];
+#pragma unroll
+          for (int c = 0; c < NCOL; ++c) mg[24 + (i * NCOL + c) * 4 + v] = oacc[i][c][v];
+        }
+    }
+    __syncthreads();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float m1 = mg[(i * 4 + v) * 3 + 0];
+        const float mm = fmaxf(m_run[i][v], m1);
+        // factors are 1 for a reference equal to the maximum (also when both
+        // groups saw no key: m = -inf)
+        const float f0 = m_run[i][v] == mm ? 1.0f : __builtin_amdgcn_exp2f(m_run[i][v] - mm);
+        const float f1 = m1 == mm ? 1.0f : __builtin_amdgcn_exp2f(m1 - mm);
+        l_run[i][v] = l_run[i][v] * f0 + mg[(i * 4 + v) * 3 + 1] * f1;
+        corr[i][v] = corr[i][v] * f0 + mg[(i * 4 + v) * 3 + 2] * f1;
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c)
+          oacc[i][c][v] = oacc[i][c][v] * f0 + mg[24 + (i * NCOL + c) * 4 + v] * f1;
+      }
+  }
+
+  // ---- finalise and rotate back.  Column tile c holds element dof(c) of this
+  // lane; its accumulator is in units of 2^-24 (and 2^-20 for odd nibbles).
+  auto dof = [&](int c) -> int {
+    return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
+  };
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float lv = l_run[i][v], cv = corr[i][v];
+      lv += shfl_xor<1>(lv);
+      lv += shfl_xor<2>(lv);
+      lv += shfl_xor<4>(lv);
+      lv += shfl_xor<8>(lv);
+      cv += shfl_xor<1>(cv);
+      cv += shfl_xor<2>(cv);
+      cv += shfl_xor<4>(cv);
+      cv += shfl_xor<8>(cv);
+      const float inv_l = lv > 0.f ? 1.0f / lv : 0.f;
+      float o[NCOL];
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) {
+        const float unit = ((c + noff) & 1) ? 1048576.0f : 16777216.0f;  // 2^20 : 2^24
+        o[c] = (oacc[i][c][v] * unit - cv) * inv_l;
+      }
+#pragma unroll
+      for (int span = 1; span < (D == 128 ? 8 : 4); span <<= 1) {
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) {
+          if (c & span) continue;
+          const float a = o[c], bb = o[c + span];
+          o[c] = a + bb;
+          o[c + span] = a - bb;
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const bool upper = (col & m) != 0;
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) {
+          const float p = shfl_xor_rt(o[c], m);
+          o[c] = upper ? p - o[c] : o[c] + p;
+        }
+      }
+      const int row = 32 * wq + 16 * i + 4 * g + v;
+      const int tq = qt * TQ + row / G;
+      if (tq < qlen) {
+        const int qg = h * G + row % G;
+        uint16_t* dst = out + ((int64_t)(q0 + tq) * num_q_heads + qg) * D;
+        const float invD = 1.0f / (float)D;
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) dst[dof(c)] = from_f32<BF16>(o[c] * signs[dof(c)] * invD);
+      }
+    }
 }
 
 template <bool BF16, int D, int G>
 hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int TQ = 64 / G;
-  dim3 grid((a.max_seqlen_q + TQ - 1) / TQ, a.num_seqs, a.num_kv_heads), block(256);
+  using PG = PGeo<D, G>;
+  static_assert(PG::TOTAL <= 160 * 1024, "LDS of a gfx950 CU");
+  auto kern = prefill_kernel<BF16, D, G>;
+  if (PG::TOTAL > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)PG::TOTAL);
+    if (e != hipSuccess) return e;
+  }
+  const int tiles_per_seq = (a.max_seqlen_q + PG::TQ - 1) / PG::TQ;
+  const int64_t groups = (int64_t)a.num_seqs * tiles_per_seq;
+  const int64_t nwg = (groups + 7) / 8 * 8 * a.num_kv_heads;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float scale_log2 = a.softmax_scale * kLog2e / (float)D;
-  hipLaunchKernelGGL((prefill_kernel<BF16, D, G>), grid, block, 0, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(512), PG::TOTAL, stream,
                      reinterpret_cast<const uint16_t*>(a.q), a.q_stride,
                      reinterpret_cast<uint16_t*>(a.out), a.cache, a.num_kv_heads, a.num_q_heads,
-                     a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs);
+                     a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs,
+                     a.num_seqs, tiles_per_seq);
   return hipGetLastError();
 }
 
