@@ -20,10 +20,15 @@
 //    three int8 planes (p2 * 65536 + p1 * 256 + p0): exact integer products,
 //    planes combined in fp32.
 //  * P . V runs on the f16 MFMA (the softmax weights need f16 precision).  V
-//    codes enter as (w & mask) | 0x6400, i.e. 1024 + code (or 1024 + 16 * code
-//    for the nibbles at bits 4..7, undone per output column); the 1024 * sum(W)
-//    bias is produced by one more MFMA against a constant operand and removed
-//    when the accumulators are flushed to fp32, every 16 tiles.
+//    codes enter as raw bit patterns: (w & 0x000F000F) is a pair of f16
+//    subnormals code * 2^-24, (w & 0x00F000F0) is 16 * code * 2^-24; products
+//    and sums stay exact in fp32 and the 2^24 (2^20) is applied per output
+//    column at the end.
+//  * The next tile's scores are computed on the matrix cores while the
+//    current tile's softmax runs; the softmax reference maximum moves only
+//    when a logit exceeds it by 4 (base-2 units, a factor 16 in probability),
+//    checked per logit, so row maxima are reduced and accumulators rescaled
+//    only on the rare tiles that need it.
 #include <type_traits>
 
 #include "device_common.h"
@@ -36,7 +41,6 @@ namespace int4kv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kFlush = 16;    // tiles between fp32 flushes of the P.V accumulators
 constexpr float kLazy = 4.0f;  // headroom of the softmax reference maximum (log2 units)
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -93,7 +97,11 @@ struct Geo {
   static constexpr int NI = (U + HPW - 1) / HPW;           // DMA instructions of waves [0, NREM)
   static constexpr int NREM = U % HPW == 0 ? HPW : U % HPW;  // the others issue NI - 1
   static constexpr uint32_t stage = U * 1024;
-  static constexpr uint32_t wtile = 17 * 64;               // per-wave W tile: 16 rows + a zero row
+  // per-wave W tile: 16 rows of 80 bytes, then a zero row placed on the banks
+  // the rows of 4 query heads leave free
+  static constexpr uint32_t WROW = 80;
+  static constexpr uint32_t WZERO = 16 * WROW + 48;
+  static constexpr uint32_t wtile = WZERO + 64;
 };
 
 // Whole LDS budget: S ring stages (the last one also holds the staged query in
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     load_ids(S - 1);
   }
   // zero row of the W tile (MFMA rows that carry no query head read it)
-  if (lane < 16) reinterpret_cast<uint32_t*>(wt + 16 * 64)[lane] = 0u;
+  if (lane < 16) reinterpret_cast<uint32_t*>(wt + GG::WZERO)[lane] = 0u;
   __syncthreads();
 
   // int8 planes of Q in the score MFMA's A layout.  Lane group g reads its K
@@ -316,31 +324,21 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     c0[v] = qok[v] ? qinfo[2 * qh + 1] : 0.f;
   }
 
-  float m_run[RPG], l_run[RPG], corr[RPG];
-  float ov[NCOL][RPG];      // flushed P.V result (fp32; code - zp applied at the end)
-  float4_t oacc[NCOL];      // MFMA accumulators of W . (1024 + scaled code)
-  float4_t bacc;            // MFMA accumulator of W . 1024
+  float m_run[RPG], thr[RPG], l_run[RPG], corr[RPG];
+  float4_t oacc[NCOL];  // sum of W * code in units of 2^-24 (2^-20 for odd nibbles)
 #pragma unroll
   for (int v = 0; v < RPG; ++v) {
-    m_run[v] = -INFINITY;
+    m_run[v] = -INFINITY;  // an empty segment reports m = -inf, l = 0
+    thr[v] = -INFINITY;
     l_run[v] = 0.f;
     corr[v] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCOL; ++c) ov[c][v] = 0.f;
   }
 #pragma unroll
   for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  bacc = float4_t{0.f, 0.f, 0.f, 0.f};
   const int noff = (D == 64) ? 4 * (col >> 3) : 0;  // nibble offset of this lane's V dword
-  auto unscale = [&](int c) -> float { return ((c + noff) & 1) ? 0.0625f : 1.0f; };
-  auto flush = [&]() {
-#pragma unroll
-    for (int c = 0; c < NCOL; ++c)
-#pragma unroll
-      for (int v = 0; v < RPG; ++v) ov[c][v] += (oacc[c][v] - bacc[v]) * unscale(c);
-#pragma unroll
-    for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-    bacc = float4_t{0.f, 0.f, 0.f, 0.f};
+  // O (rotated domain, zero point not yet removed) of column tile c
+  auto o_of = [&](int c, int v) -> float {
+    return oacc[c][v] * (((c + noff) & 1) ? 1048576.0f : 16777216.0f);  // 2^20 : 2^24
   };
 
   // per-lane LDS byte offsets inside a stage (loop invariant)
@@ -357,18 +355,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     v_off[j] = (kk >> 4) * GG::BLK + GG::lhalf + (kk & 15) * GG::TS + hoff + 4 * (col % DW);
   }
   // W tile addressing: writer (col, g) -> row qh, dword col; reader (row r, g)
-  // -> 16 bytes at dword 4g of its query head's row (or the zero row)
+  // -> 16 bytes at dword 4g of its query head's row (or the zero row).  Rows
+  // are 80 bytes apart so the 16-byte reads of 8 lanes fall in distinct banks.
   uint32_t wr_off[RPG];
 #pragma unroll
-  for (int v = 0; v < RPG; ++v) wr_off[v] = (uint32_t)min(g * RPG + v, 15) * 64 + 4 * col;
+  for (int v = 0; v < RPG; ++v) wr_off[v] = (uint32_t)min(g * RPG + v, 15) * GG::WROW + 4 * col;
   uint32_t rd_off;
   {
     const int grp = col >> 2, vv = col & 3, qh = grp * RPG + vv;
-    rd_off = (vv < RPG && qh < G ? (uint32_t)qh : 16u) * 64 + 16 * g;
+    rd_off = (vv < RPG && qh < G ? (uint32_t)qh * GG::WROW : GG::WZERO) + 16 * g;
   }
-  half8_t ones1024;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ones1024[j] = (_Float16)1024.0f;
 
   // ---- int8 K operands of one tile (low nibbles as is, high nibbles shifted)
   auto k_operands = [&](const unsigned char* st, i32x4_t (&kb)[2][NCK]) {
@@ -474,65 +470,60 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     }
     phase_end(0, kb, nxt);
 
-    // phase 2: reference maxima.  The reference m only moves when a logit
-    // exceeds it by more than kLazy (base-2 units), so p = 2^(z - m) <= 2^kLazy
-    // and the accumulators are rescaled rarely; m, l and O always share the
-    // same reference, which is all the merge and the normalisation need.
-    float mnew[RPG], alpha[RPG];
-    bool moved = false;
+    // reference maxima.  The reference m of a row only moves when a logit
+    // exceeds it by more than kLazy (base-2 units), so p = 2^(z - m) <= 2^kLazy;
+    // that is checked per logit against thr = m + kLazy, and the row maxima are
+    // reduced and the accumulators rescaled only on the rare tiles where it
+    // happens.  m, l and O always share one reference, which is all the merge
+    // and the normalisation need.
+    bool over = false;
 #pragma unroll
-    for (int v = 0; v < RPG; ++v) {
-      const float tmax = max16(fmaxf(z[v][0], z[v][1]));
-      const bool up = tmax > m_run[v] + kLazy;
-      moved |= up;
-      mnew[v] = up ? tmax : m_run[v];
-      alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - mnew[v]);
-      m_run[v] = mnew[v];
+    for (int v = 0; v < RPG; ++v) over |= (z[v][0] > thr[v]) | (z[v][1] > thr[v]);
+    if (__any(over)) {
+#pragma unroll
+      for (int v = 0; v < RPG; ++v) {
+        const float tmax = max16(fmaxf(z[v][0], z[v][1]));
+        const bool up = tmax > thr[v];
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run[v] - tmax) : 1.0f;
+        m_run[v] = up ? tmax : m_run[v];
+        thr[v] = m_run[v] + kLazy;
+        l_run[v] *= alpha;
+        corr[v] *= alpha;
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) oacc[c][v] *= alpha;
+      }
     }
-    phase_end(1, kb, nxt);
 
-    // phase 3: probabilities, weights W = p sV (f16), sums, zero-point term
+    // phase 2: probabilities, weights W = p sV (f16), sums, zero-point term
 #pragma unroll
     for (int v = 0; v < RPG; ++v) {
-      const float p0 = __builtin_amdgcn_exp2f(z[v][0] - mnew[v]);
-      const float p1 = __builtin_amdgcn_exp2f(z[v][1] - mnew[v]);
-      const _Float16 w0 = (_Float16)(p0 * sV[0]);
-      const _Float16 w1 = (_Float16)(p1 * sV[1]);
-      l_run[v] = l_run[v] * alpha[v] + (p0 + p1);
-      corr[v] = corr[v] * alpha[v] + ((float)w0 * zV[0] + (float)w1 * zV[1]);
-      const uint32_t wpk = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
-      *reinterpret_cast<uint32_t*>(wt + wr_off[v]) = wpk;
+      const float p0 = __builtin_amdgcn_exp2f(z[v][0] - m_run[v]);
+      const float p1 = __builtin_amdgcn_exp2f(z[v][1] - m_run[v]);
+      half2_t wp;
+      wp[0] = (_Float16)(p0 * sV[0]);
+      wp[1] = (_Float16)(p1 * sV[1]);
+      l_run[v] += p0 + p1;
+      corr[v] = fmaf((float)wp[1], zV[1], fmaf((float)wp[0], zV[0], corr[v]));
+      *reinterpret_cast<half2_t*>(wt + wr_off[v]) = wp;
     }
     // weights in the A layout, read back from this wave's W tile right away
     // (LDS operations of one wave complete in order); the latency is covered
     // by the work up to the P.V products
     const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
-    phase_end(2, kb, nxt);
+    phase_end(1, kb, nxt);
 
-    // phase 4: V operand bytes (pairs of keys per dword); remaining score groups
+    // phase 3: V operand bytes (pairs of keys per dword)
     uint32_t ylo[4], yhi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ylo[i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], 0x05040100u);  // a.b01 b.b01
       yhi[i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], 0x07060302u);  // a.b23 b.b23
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    if (__any(moved)) {  // rescale only when some running maximum grew
-#pragma unroll
-      for (int v = 0; v < RPG; ++v) {
-#pragma unroll
-        for (int c = 0; c < NCOL; ++c) {
-          oacc[c][v] *= alpha[v];
-          ov[c][v] *= alpha[v];
-        }
-        bacc[v] *= alpha[v];
-      }
-    }
+    phase_end(2, kb, nxt);
 
     // O += W V.  Column tile c uses nibble c (+ noff) of the lane's dword of
-    // each slot key; nibbles at odd positions come out x16.
+    // each slot key, as a pair of f16 subnormals: code * 2^-24 for nibbles at
+    // even positions, 16 * code * 2^-24 at odd ones.
 #pragma unroll
     for (int c = 0; c < NCOL; ++c) {
       const int nib = c + noff;
@@ -541,24 +532,21 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       for (int i = 0; i < 4; ++i) {
         const uint32_t y = (nib < 4) ? ylo[i] : yhi[i];
         const uint32_t ys = (nib & 2) ? (y >> 8) : y;
-        const uint32_t mask = (nib & 1) ? 0x00F000F0u : 0x000F000Fu;
-        vb[i] = and_or(ys, mask, 0x64006400u);
+        vb[i] = ys & ((nib & 1) ? 0x00F000F0u : 0x000F000Fu);
       }
       oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
                                                        oacc[c], 0, 0, 0);
     }
-    bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, ones1024, bacc, 0, 0, 0);
     // the remaining score groups of tile t+1 share this region: one MFMA per
     // four vector instructions of the V operand expansion
 #pragma unroll
     for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
 #pragma unroll
-    for (int j = 0; j < NCOL + 1 + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
+    for (int j = 0; j < NCOL + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if ((t % kFlush) == kFlush - 1) flush();
   };
 
   // ---- main loop.  Tile t+1 must have landed at the top of step t; tiles
@@ -582,7 +570,6 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
   if (t < ntile) step(t, accA, accB, wA, wB);
   wait_vmem<0>();  // drain the clamped look-ahead copies
-  flush();
 
   // ---- finalise: sums over the 16 lanes of a group
 #pragma unroll
@@ -609,7 +596,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       const int64_t base = ((int64_t)b * num_q_heads + qg) * num_segments + seg;
       float* dst = segm_out + base * D;
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) dst[dof(c)] = ov[c][v] - corr[v];
+      for (int c = 0; c < NCOL; ++c) dst[dof(c)] = o_of(c, v) - corr[v];
       if (col == 0) {
         segm_max[base] = m_run[v];
         segm_sum[base] = l_run[v];
@@ -623,7 +610,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const float inv_l = l_run[v] > 0.f ? 1.0f / l_run[v] : 0.f;
     float o[NCOL];
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) o[c] = (ov[c][v] - corr[v]) * inv_l;
+    for (int c = 0; c < NCOL; ++c) o[c] = (o_of(c, v) - corr[v]) * inv_l;
 #pragma unroll
     for (int span = 1; span < (D == 128 ? 8 : 4); span <<= 1) {
 #pragma unroll

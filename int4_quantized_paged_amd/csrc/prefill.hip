@@ -82,7 +82,10 @@ struct PGeo {
   static constexpr uint32_t RING = kStages * STAGE;
   static constexpr uint32_t QSTAGE = 128 * D * 2 * 2;  // hi and lo, operand order
   static constexpr uint32_t WBASE = RING > QSTAGE ? RING : QSTAGE;
-  static constexpr uint32_t WTILE = 2 * 16 * 64;  // per wave: 2 row tiles x 16 rows x 32 keys f16
+  // per wave: 2 row tiles x 16 rows x 32 keys f16, rows padded to 80 bytes so
+  // the 16-byte A-operand reads of 8 lanes cover all 32 banks
+  static constexpr uint32_t WROW = 80;
+  static constexpr uint32_t WTILE = 2 * 16 * WROW;
   // odd-tile group's state for the final merge: per lane 8 m, 8 l, 8 corr, 16*NCOL/2 O
   static constexpr uint32_t MERGE = 4 * 64 * (24 + 8 * (D / 16)) * 4;
   static constexpr uint32_t LOW = WBASE > MERGE ? WBASE : MERGE;
@@ -268,17 +271,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 #pragma unroll
   for (int c = 0; c < NCH; ++c) k_off[c] = krow + (uint32_t)(4 * c + g) * 4;
   const uint32_t s_off = krow + (uint32_t)(RW - 1) * 4;  // scale word
-  uint32_t v_off[8];  // slot j = 2i + n <-> key 16n + 4g + i
+  uint32_t v_off[8];  // slot j = 2i + n <-> key 16n + g + 4i
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int n = j & 1, t = 4 * g + (j >> 1);
+    const int n = j & 1, t = g + 4 * (j >> 1);
     v_off[j] = (uint32_t)(2 * n + 1) * PG::HALF + (uint32_t)t * RW * 4 + (uint32_t)(col % DW) * 4;
   }
   unsigned char* wt = smem + PG::LOW + wave * PG::WTILE;
-  uint32_t wr_off[4];  // writer: row 4g + v, dword col
+  // W tile: the f16 pair of key col (blocks 0 and 1) of row r sits at dword
+  // 4 (col % 4) + col / 4, so reader group g (dwords 4g..4g+3) gets keys g + 4i
+  uint32_t wr_off[4];  // writer: rows 4g + v
 #pragma unroll
-  for (int v = 0; v < 4; ++v) wr_off[v] = (uint32_t)(4 * g + v) * 64 + 4 * col;
-  const uint32_t rd_off = (uint32_t)col * 64 + 16 * g;  // reader: row col, dwords 4g..4g+3
+  for (int v = 0; v < 4; ++v)
+    wr_off[v] = (uint32_t)(4 * g + v) * PG::WROW + 4 * (4 * (col % 4) + col / 4);
+  const uint32_t rd_off = (uint32_t)col * PG::WROW + 16 * g;  // reader: row col
   const int noff = (D == 64) ? 4 * (col >> 3) : 0;      // nibble offset of this lane's V dword
 
   // steps s = 0 .. nsteps-1 process tiles 2s (even group) and 2s+1 (odd
@@ -395,13 +401,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         wp[1] = (_Float16)(p1 * sV[1]);
         l_run[i][v] += p0 + p1;
         corr[i][v] = fmaf((float)wp[1], zV[1], fmaf((float)wp[0], zV[0], corr[i][v]));
-        *reinterpret_cast<half2_t*>(wt + i * 1024 + wr_off[v]) = wp;
+        *reinterpret_cast<half2_t*>(wt + i * 16 * PG::WROW + wr_off[v]) = wp;
       }
     // weights in the A layout, read back from this wave's W tiles (LDS
     // operations of one wave complete in order)
     half8_t wop[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wop[i] = *reinterpret_cast<const half8_t*>(wt + i * 1024 + rd_off);
+    for (int i = 0; i < 2; ++i)
+      wop[i] = *reinterpret_cast<const half8_t*>(wt + i * 16 * PG::WROW + rd_off);
 
     // V operands (shared by both row tiles) and O += W V.  Column tile c uses
     // nibble c (+ noff) of the lane's dword of each slot key.
