@@ -8,128 +8,178 @@
 // quantizer of the test file's section 6 INT4 reference and the skip rule of
 // its section 4 (slot < 0 writes nothing).
 //
-// Work layout: one row = one (token, K|V, head) vector of D elements.  A row
-// is owned by D/16 lanes holding 16 consecutive elements each, so a wave owns
-// 64/(D/16) rows: 8 rows at D = 128, i.e. all heads of one (token, K|V) when
-// there are 8 KV heads, whose packed rows are contiguous in the cache.
-// The Walsh-Hadamard butterflies of span 1..8 run inside a lane; spans 16, 32,
-// 64 pair lanes (lane ^ 1, ^ 2, ^ 4) through DPP / ds_swizzle.  Every fp32
-// operation is a single correctly rounded op in the fixed span order, so the
-// packed bytes are reproducible bit for bit (this file is built without FMA
-// contraction).
+// Work layout: one row = one (token, K|V, head) vector of D elements, held by
+// D/64 lanes with 64 consecutive elements each (2 lanes at D = 128, 1 at
+// D = 64), so a wave covers 32 (or 64) rows.  The Walsh-Hadamard butterflies
+// of span 1..32 run inside a lane and the last one (span 64) pairs the two
+// lanes of a row through DPP, which keeps the spans in the order the encoding
+// fixes.  Every fp32 operation is a single correctly rounded op in that order,
+// so the packed bytes are reproducible bit for bit (this file is built without
+// FMA contraction):
+//   * the signs are applied as bit flips of the 16-bit inputs (exact),
+//   * clamp-then-round equals round-then-clamp for the integer bounds 0 and 15,
+//     and the rounding to nearest-even is an fp32 add of 2^23, after which the
+//     code sits in the low 4 bits of the sum.
 #include "device_common.h"
 #include "launch.h"
 
 namespace int4kv {
+
+namespace {
+
+__device__ __forceinline__ float med3(float x, float lo, float hi) {
+  return __builtin_amdgcn_fmed3f(x, lo, hi);
+}
+
+// element i of a 16-bit pair dword (i = 0: low half)
+template <bool BF16>
+__device__ __forceinline__ float half_of(uint32_t w, int i) {
+  if constexpr (BF16) {
+    return as_float(i == 0 ? (w << 16) : (w & 0xFFFF0000u));
+  } else {
+    const half2_t h = __builtin_bit_cast(half2_t, w);
+    return (float)h[i];
+  }
+}
+
+}  // namespace
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void write_kernel(
     const uint16_t* __restrict__ key, int64_t key_stride, const uint16_t* __restrict__ value,
     int64_t value_stride, const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
     uint8_t* __restrict__ cache, int32_t num_kv_heads, const float* __restrict__ signs) {
-  constexpr int LPR = D / 16;            // lanes per row
+  constexpr int LPR = D / 64;            // lanes per row
   constexpr int RPW = kWave / LPR;       // rows per wave
   constexpr int R = D / 2 + 4;           // packed row bytes
   const int lane = threadIdx.x & 63;
-  const int sub = lane % LPR;
+  const int sub = lane % LPR;            // which 64-element half of the row
   const int rw = lane / LPR;
   const int64_t total_rows = (int64_t)num_tokens * 2 * num_kv_heads;
   const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x / kWave);
   const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
 
-  float sg[16];
-  {
-    const float4* sp = reinterpret_cast<const float4*>(signs + 16 * sub);
+  // sign bits of the lane's 64 elements, as flips of 16-bit pairs
+  uint32_t flip[32];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float4 v = sp[k];
-      sg[4 * k + 0] = v.x;
-      sg[4 * k + 1] = v.y;
-      sg[4 * k + 2] = v.z;
-      sg[4 * k + 3] = v.w;
-    }
+  for (int p = 0; p < 32; ++p) {
+    const float s0 = signs[64 * sub + 2 * p], s1 = signs[64 * sub + 2 * p + 1];
+    flip[p] = (s0 < 0.f ? 0x8000u : 0u) | (s1 < 0.f ? 0x80000000u : 0u);
   }
+  const uint32_t xflip = sub ? 0x80000000u : 0u;  // upper lane of a row keeps u - v
 
-  for (int64_t base = wave_id * RPW; base < total_rows; base += waves_total * RPW) {
+  // row coordinates and the raw 16-bit inputs of one row (software-pipelined:
+  // the next row's loads are in flight while the current row is encoded)
+  struct RowIn {
+    int64_t t;
+    int h, kv;
+    bool ok;
+    u32x4_t a[8];
+  };
+  auto fetch = [&](int64_t base, RowIn& in) {
     const int64_t row = base + rw;
-    const bool in_range = row < total_rows;
-    const int64_t r = in_range ? row : total_rows - 1;  // tail lanes compute a valid row, store nothing
-    const int h = (int)(r % num_kv_heads);
+    in.ok = row < total_rows;
+    const int64_t r = in.ok ? row : total_rows - 1;  // tail lanes read a valid row, store nothing
+    in.h = (int)(r % num_kv_heads);
     const int64_t tk = r / num_kv_heads;
-    const int kv = (int)(tk & 1);
-    const int64_t t = tk >> 1;
-
-    const uint16_t* src = (kv == 0 ? key + t * key_stride : value + t * value_stride) +
-                          (int64_t)h * D + 16 * sub;
+    in.kv = (int)(tk & 1);
+    in.t = tk >> 1;
+    const uint16_t* src = (in.kv == 0 ? key + in.t * key_stride : value + in.t * value_stride) +
+                          (int64_t)in.h * D + 64 * sub;
     const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(src);
-    u32x4_t a = s4[0], b = s4[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float x[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) in.a[k] = s4[k];
+  };
+  const int64_t stride = waves_total * RPW;
+  int64_t base = wave_id * RPW;
+  if (base >= total_rows) return;
+  RowIn cur;
+  fetch(base, cur);
+  for (; base < total_rows; base += stride) {
+    RowIn nxt;
+    if (base + stride < total_rows) fetch(base + stride, nxt);  // uniform over the wave
+    const int64_t t = cur.t;
+    const int h = cur.h, kv = cur.kv;
+    const bool in_range = cur.ok;
+    float x[64];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      x[2 * k] = to_f32<BF16>((uint16_t)(w[k] & 0xFFFFu));
-      x[2 * k + 1] = to_f32<BF16>((uint16_t)(w[k] >> 16));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = cur.a[k][j] ^ flip[4 * k + j];  // x * sign, exactly
+        x[8 * k + 2 * j] = half_of<BF16>(w, 0);
+        x[8 * k + 2 * j + 1] = half_of<BF16>(w, 1);
+      }
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = __fmul_rn(x[e], sg[e]);  // exact: signs are +-1
 
-    // butterflies inside the lane: spans 1, 2, 4, 8
+    // butterflies inside the lane: spans 1 .. 32
 #pragma unroll
-    for (int span = 1; span < 16; span <<= 1) {
+    for (int span = 1; span < 64; span <<= 1) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < 64; ++e) {
         if (e & span) continue;
-        float u = x[e], v = x[e + span];
+        const float u = x[e], v = x[e + span];
         x[e] = __fadd_rn(u, v);
         x[e + span] = __fsub_rn(u, v);
       }
     }
-    // butterflies across lanes: spans 16, 32, 64.  The lower partner keeps
-    // u + v, the upper one u - v, written as partner + (-self).
+    // span 64 across the two lanes of a row: the lower lane keeps u + v, the
+    // upper one u - v, written as partner + (-self)
+    if constexpr (LPR == 2) {
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      const uint32_t flip = (sub & m) ? 0x80000000u : 0u;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float p = shfl_xor_rt(x[e], m);
-        x[e] = __fadd_rn(p, as_float(as_uint(x[e]) ^ flip));
+      for (int e = 0; e < 64; ++e) {
+        const float p = shfl_xor<1>(x[e]);
+        x[e] = __fadd_rn(p, as_float(as_uint(x[e]) ^ xflip));
       }
     }
 
     // row range
-    float mn = x[0], mx = x[0];
+    float mn = fminf(x[0], x[1]), mx = fmaxf(x[0], x[1]);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) {
-      mn = fminf(mn, x[e]);
-      mx = fmaxf(mx, x[e]);
+    for (int e = 2; e < 64; e += 2) {
+      mn = __builtin_fminf(mn, __builtin_fminf(x[e], x[e + 1]));
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[e], x[e + 1]));
     }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      mn = fminf(mn, shfl_xor_rt(mn, m));
-      mx = fmaxf(mx, shfl_xor_rt(mx, m));
+    if constexpr (LPR == 2) {
+      mn = fminf(mn, shfl_xor<1>(mn));
+      mx = fmaxf(mx, shfl_xor<1>(mx));
     }
-    float s = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
-    if (!(s > 1e-6f)) s = 1e-6f;
-    const float s_t = as_float(as_uint(s) & 0xFFFFFFF0u);
+    float sc = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+    if (!(sc > 1e-6f)) sc = 1e-6f;
+    const float s_t = as_float(as_uint(sc) & 0xFFFFFFF0u);
     const float inv = __fdiv_rn(1.0f, s_t);
     const float zpf = fminf(fmaxf(rintf(__fmul_rn(-mn, inv)), 0.0f), 15.0f);
 
-    uint32_t packed[2] = {0u, 0u};
+    // codes: clamp to [0, 15], then round to nearest even by adding 2^23; the
+    // code is then the low 4 bits of the sum's bit pattern
+    uint32_t packed[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float c = fminf(fmaxf(rintf(__fadd_rn(__fmul_rn(x[e], inv), zpf)), 0.0f), 15.0f);
-      packed[e >> 3] |= (uint32_t)c << (4 * (e & 7));
+    for (int q = 0; q < 8; ++q) {
+      uint32_t b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 8 * q + 2 * j;
+        const float c0 = __fadd_rn(med3(__fadd_rn(__fmul_rn(x[e], inv), zpf), 0.0f, 15.0f),
+                                   8388608.0f);
+        const float c1 = __fadd_rn(med3(__fadd_rn(__fmul_rn(x[e + 1], inv), zpf), 0.0f, 15.0f),
+                                   8388608.0f);
+        b[j] = (as_uint(c1) << 4) | as_uint(c0);  // byte 0 = code_lo | code_hi << 4
+      }
+      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // [b0.0 b1.0 0 0]
+      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+      packed[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);            // [lo.0 lo.1 hi.0 hi.1]
     }
 
     const int64_t slot = slot_mapping[t];
     if (in_range && slot >= 0) {
       const int64_t blk = slot / kBlockSize, off = slot % kBlockSize;
       uint8_t* dst = cache + (((blk * 2 + kv) * kBlockSize + off) * num_kv_heads + h) * R;
-      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);  // rows are 4-byte aligned
-      d32[2 * sub] = packed[0];
-      d32[2 * sub + 1] = packed[1];
-      if (sub == 0) d32[D / 8] = as_uint(s_t) | (uint32_t)zpf;
+      u32x4a4_t* d16 = reinterpret_cast<u32x4a4_t*>(dst + 32 * sub);  // rows are 4-byte aligned
+      d16[0] = u32x4a4_t{packed[0], packed[1], packed[2], packed[3]};
+      d16[1] = u32x4a4_t{packed[4], packed[5], packed[6], packed[7]};
+      if (sub == 0) reinterpret_cast<uint32_t*>(dst)[D / 8] = as_uint(s_t) | (uint32_t)zpf;
     }
+    cur = nxt;
   }
 }
 
@@ -138,7 +188,7 @@ hipError_t launch_write(const void* key, int64_t key_stride, const void* value,
                         int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
                         int32_t head_size, const float* signs, hipStream_t stream) {
   const int64_t rows = (int64_t)num_tokens * 2 * num_kv_heads;
-  const int rows_per_block = 4 * (kWave / (head_size / 16));
+  const int rows_per_block = 4 * (kWave / (head_size / 64));
   int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   const int64_t cap = 256 * 32;  // grid-stride beyond 32 blocks per CU
   if (blocks > cap) blocks = cap;
