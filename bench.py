@@ -264,6 +264,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-rows", action="store_true",
                     help="skip the prefill and Llama-3-shaped decode measurements")
+    ap.add_argument("--only-other-rows", action="store_true",
+                    help="only the prefill and Llama-3-shaped decode measurements (for profiling)")
     ap.add_argument("--eager", action="store_true",
                     help="time plain library calls instead of HIP-graph replays of them")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -288,6 +290,9 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": 4 * n, "copies": 4}), flush=True)
         return
     ik.load_library()
+    if args.only_other_rows:
+        print(json.dumps({"other_rows": other_rows(dev)}), flush=True)
+        return
     nbufs = 2  # 2 x 570 MB > 256 MB Infinity Cache
     bufs = build_buffers(nbufs, dev)
     log("caches filled")

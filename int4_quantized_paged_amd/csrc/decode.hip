@@ -285,7 +285,7 @@ __global__ __launch_bounds__(512) void decode_kernel(
         sV[n] = as_float(cur.vs[n] & 0xFFFFFFF0u);
         zV[n] = (float)(cur.vs[n] & 0xFu);
       }
-      uint32_t wpk[RPG];
+      uint32_t wpk[RPG], wpl[RPG];
   #pragma unroll
       for (int v = 0; v < RPG; ++v) {
         float z[2];
@@ -303,35 +303,43 @@ __global__ __launch_bounds__(512) void decode_kernel(
         const float alpha = exp2f(m_run[v] - mnew);
         m_run[v] = mnew;
         const float p0 = exp2f(z[0] - mnew), p1 = exp2f(z[1] - mnew);
-        const _Float16 w0 = (_Float16)(kval[0] ? p0 * sV[0] : 0.f);
-        const _Float16 w1 = (_Float16)(kval[1] ? p1 * sV[1] : 0.f);
+        // W = p sV as f16 hi + lo (22 significant bits)
+        const float f0 = kval[0] ? p0 * sV[0] : 0.f, f1 = kval[1] ? p1 * sV[1] : 0.f;
+        const _Float16 w0 = (_Float16)f0, w1 = (_Float16)f1;
+        const _Float16 u0 = (_Float16)(f0 - (float)w0), u1 = (_Float16)(f1 - (float)w1);
         l_run[v] = l_run[v] * alpha + (p0 + p1);
-        corr[v] = corr[v] * alpha + ((float)w0 * zV[0] + (float)w1 * zV[1]);
+        corr[v] = corr[v] * alpha + (f0 * zV[0] + f1 * zV[1]);
   #pragma unroll
         for (int c = 0; c < NCOL; ++c) oacc[c][v] *= alpha;
         wpk[v] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
                  ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+        wpl[v] = (uint32_t)__builtin_bit_cast(uint16_t, u0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, u1) << 16);
       }
 
       // ---- weights to the A-operand layout: lane (row r, group g) takes slot
       // pair i = (W[qh][4g + i], W[qh][16 + 4g + i]) from lane 16*(r/4) + 4g + i
-      u32x4_t wa;
+      u32x4_t wa, wb;
       {
         const int r = col, grp = r >> 2, vv = r & 3;
         const bool ok = vv < RPG && grp * RPG + vv < G;
   #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int src = 16 * grp + 4 * g + i;
-          uint32_t val = 0;
+          uint32_t val = 0, vlo = 0;
   #pragma unroll
           for (int v = 0; v < RPG; ++v) {
             const uint32_t t = lane_read(wpk[v], src);
+            const uint32_t tl = lane_read(wpl[v], src);
             val = (vv == v) ? t : val;
+            vlo = (vv == v) ? tl : vlo;
           }
           wa[i] = ok ? val : 0u;
+          wb[i] = ok ? vlo : 0u;
         }
       }
       const half8_t wop = __builtin_bit_cast(half8_t, wa);
+      const half8_t wop_lo = __builtin_bit_cast(half8_t, wb);
 
       // ---- V operands and O += W V
       {
@@ -353,6 +361,8 @@ __global__ __launch_bounds__(512) void decode_kernel(
             vb[i] = nib_pair_f16(y >> (4 * (nib & 3)));
           }
           oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
+                                                           oacc[c], 0, 0, 0);
+          oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, __builtin_bit_cast(half8_t, vb),
                                                            oacc[c], 0, 0, 0);
         }
       }

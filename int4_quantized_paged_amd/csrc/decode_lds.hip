@@ -16,11 +16,13 @@
 //    stride of 12 dwords mod 32 so the per-lane row reads spread over the banks.
 //  * Q . K^T runs on the int8 MFMA (v_mfma_i32_16x16x64_i8): K codes become
 //    int8 with one mask (low nibbles) and a shift + mask (high nibbles) per
-//    dword; the rotated query is held as a 24-bit fixed-point value split into
-//    three int8 planes (p2 * 65536 + p1 * 256 + p0): exact integer products,
-//    planes combined in fp32.
-//  * P . V runs on the f16 MFMA (the softmax weights need f16 precision).  V
-//    codes enter as raw bit patterns: (w & 0x000F000F) is a pair of f16
+//    dword; the rotated query is held as a fixed-point value below 2^22 in
+//    magnitude (23 bits with the sign) split into three int8 planes
+//    (p2 * 65536 + p1 * 256 + p0): exact integer products, planes combined in
+//    fp32.
+//  * P . V runs on the f16 MFMA with the softmax weights W = p * s_V split into
+//    f16 hi + lo (22 significant bits; f16 alone leaves an error of 2^-11 of
+//    |V| in the output).  V codes enter as raw bit patterns: (w & 0x000F000F) is a pair of f16
 //    subnormals code * 2^-24, (w & 0x00F000F0) is 16 * code * 2^-24; products
 //    and sums stay exact in fp32 and the 2^24 (2^20) is applied per output
 //    column at the end.
@@ -99,8 +101,11 @@ struct Geo {
   static constexpr uint32_t stage = U * 1024;
   // per-wave W tile: 16 rows of 80 bytes, then a zero row placed on the banks
   // the rows of 4 query heads leave free
+  // The weights are split into f16 hi + lo (22 significant bits): the lo rows
+  // follow the hi rows.
   static constexpr uint32_t WROW = 80;
-  static constexpr uint32_t WZERO = 16 * WROW + 48;
+  static constexpr uint32_t WLO = 16 * WROW;
+  static constexpr uint32_t WZERO = 2 * 16 * WROW + 48;
   static constexpr uint32_t wtile = WZERO + 64;
 };
 
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       wait_vmem<decltype(ahead)::value * (NI - 1)>();
   };
 
-  // ---- prologue: q' = H (signs * q) as 24-bit fixed point, staged in the last stage
+  // ---- prologue: q' = H (signs * q) as fixed point below 2^22, staged in the last stage
   int32_t* q24 = reinterpret_cast<int32_t*>(smem + Lay<D, G, HPW>::qbase) + wave * G * D;
   float* qinfo =
       reinterpret_cast<float*>(smem + Lay<D, G, HPW>::qbase + HPW * G * D * 4) + wave * 2 * G;
@@ -256,20 +261,21 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
     for (int m = 1; m < LPQ; m <<= 1) mx = fmaxf(mx, shfl_xor_rt(mx, m));
     const int ex = mx > 0.f ? ilogbf(mx) + 1 : 0;  // |q'| * 2^-ex < 1
-    const float nrm = ldexpf(1.0f, 23 - ex);
+    // |v| < 2^22: the centred planes p0, p1 in [-128, 127] then leave the top
+    // plane p2 within [-65, 65], so no value is ever clamped
+    const float nrm = ldexpf(1.0f, 22 - ex);
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      // |v| <= 2^23 - 2^16 keeps the top plane in [-128, 127] after carries
-      const float v = fminf(fmaxf(rintf(x[e] * nrm), -8323072.f), 8323072.f);
+      const float v = rintf(x[e] * nrm);
       q24[i * D + s * EPL + e] = (int)v;
-      sum += v;  // < 2^30 in magnitude; its rounding is far below the score's
+      sum += v;  // < 2^29 in magnitude; its rounding is far below the score's
     }
 #pragma unroll
     for (int m = 1; m < LPQ; m <<= 1) sum += shfl_xor_rt(sum, m);
     if (s == 0) {
       qinfo[2 * i + 0] = sum;
-      qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - 23);
+      qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - 22);
     }
   }
   if (ntile > 0) {  // always S - 1 tiles ahead (clamped), so the vmcnt below is exact
@@ -360,10 +366,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   uint32_t wr_off[RPG];
 #pragma unroll
   for (int v = 0; v < RPG; ++v) wr_off[v] = (uint32_t)min(g * RPG + v, 15) * GG::WROW + 4 * col;
-  uint32_t rd_off;
+  uint32_t rd_off, rd_lo;
   {
     const int grp = col >> 2, vv = col & 3, qh = grp * RPG + vv;
-    rd_off = (vv < RPG && qh < G ? (uint32_t)qh * GG::WROW : GG::WZERO) + 16 * g;
+    const bool valid = vv < RPG && qh < G;
+    rd_off = (valid ? (uint32_t)qh * GG::WROW : GG::WZERO) + 16 * g;
+    rd_lo = (valid ? GG::WLO + (uint32_t)qh * GG::WROW : GG::WZERO) + 16 * g;
   }
 
   // ---- int8 K operands of one tile (low nibbles as is, high nibbles shifted)
@@ -494,22 +502,27 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       }
     }
 
-    // phase 2: probabilities, weights W = p sV (f16), sums, zero-point term
+    // phase 2: probabilities, weights W = p sV as f16 hi + lo, sums, zero-point term
 #pragma unroll
     for (int v = 0; v < RPG; ++v) {
       const float p0 = __builtin_amdgcn_exp2f(z[v][0] - m_run[v]);
       const float p1 = __builtin_amdgcn_exp2f(z[v][1] - m_run[v]);
-      half2_t wp;
-      wp[0] = (_Float16)(p0 * sV[0]);
-      wp[1] = (_Float16)(p1 * sV[1]);
+      const float w0 = p0 * sV[0], w1 = p1 * sV[1];
+      half2_t wh, wl;
+      wh[0] = (_Float16)w0;
+      wh[1] = (_Float16)w1;
+      wl[0] = (_Float16)(w0 - (float)wh[0]);
+      wl[1] = (_Float16)(w1 - (float)wh[1]);
       l_run[v] += p0 + p1;
-      corr[v] = fmaf((float)wp[1], zV[1], fmaf((float)wp[0], zV[0], corr[v]));
-      *reinterpret_cast<half2_t*>(wt + wr_off[v]) = wp;
+      corr[v] = fmaf(w1, zV[1], fmaf(w0, zV[0], corr[v]));
+      *reinterpret_cast<half2_t*>(wt + wr_off[v]) = wh;
+      *reinterpret_cast<half2_t*>(wt + GG::WLO + wr_off[v]) = wl;
     }
     // weights in the A layout, read back from this wave's W tile right away
     // (LDS operations of one wave complete in order); the latency is covered
     // by the work up to the P.V products
     const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
+    const half8_t wop_lo = *reinterpret_cast<const half8_t*>(wt + rd_lo);
     phase_end(1, kb, nxt);
 
     // phase 3: V operand bytes (pairs of keys per dword)
@@ -536,13 +549,15 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       }
       oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
                                                        oacc[c], 0, 0, 0);
+      oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, __builtin_bit_cast(half8_t, vb),
+                                                       oacc[c], 0, 0, 0);
     }
     // the remaining score groups of tile t+1 share this region: one MFMA per
     // four vector instructions of the V operand expansion
 #pragma unroll
     for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
 #pragma unroll
-    for (int j = 0; j < NCOL + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
+    for (int j = 0; j < 2 * NCOL + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }

@@ -21,9 +21,9 @@
 //    products and sums stay exact in fp32 and the 2^24 (and the 16) are folded
 //    into per-row and per-column constants.  No bias, no subtraction.
 //  * Q . K^T: Q' as f16 hi + lo (22 significant bits), both against the same
-//    K operand.  P . V: softmax weights times the V scale (f16) as the A
-//    operand, through a per-wave LDS tile, against V codes expanded per lane
-//    from one dword of each of 8 keys.
+//    K operand.  P . V: softmax weights times the V scale, also as f16 hi +
+//    lo, as the A operand through a per-wave LDS tile, against V codes
+//    expanded per lane from one dword of each of 8 keys.
 //  * Workgroups are numbered so that the KV heads of one (sequence, tile) run
 //    on the same XCD (the heads of a token share 128-byte lines in L2), and
 //    later query tiles, which see more keys, are dispatched first.
@@ -85,7 +85,7 @@ struct PGeo {
   // per wave: 2 row tiles x 16 rows x 32 keys f16, rows padded to 80 bytes so
   // the 16-byte A-operand reads of 8 lanes cover all 32 banks
   static constexpr uint32_t WROW = 80;
-  static constexpr uint32_t WTILE = 2 * 16 * WROW;
+  static constexpr uint32_t WTILE = 2 * 2 * 16 * WROW;  // hi and lo tiles of both row tiles
   // odd-tile group's state for the final merge: per lane 8 m, 8 l, 8 corr, 16*NCOL/2 O
   static constexpr uint32_t MERGE = 4 * 64 * (24 + 8 * (D / 16)) * 4;
   static constexpr uint32_t LOW = WBASE > MERGE ? WBASE : MERGE;
@@ -396,19 +396,25 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       for (int v = 0; v < 4; ++v) {
         const float p0 = __builtin_amdgcn_exp2f(z[i][v][0] - m_run[i][v]);
         const float p1 = __builtin_amdgcn_exp2f(z[i][v][1] - m_run[i][v]);
-        half2_t wp;
-        wp[0] = (_Float16)(p0 * sV[0]);
-        wp[1] = (_Float16)(p1 * sV[1]);
+        const float w0 = p0 * sV[0], w1 = p1 * sV[1];
+        half2_t wh, wl;  // W = p sV as f16 hi + lo (22 significant bits)
+        wh[0] = (_Float16)w0;
+        wh[1] = (_Float16)w1;
+        wl[0] = (_Float16)(w0 - (float)wh[0]);
+        wl[1] = (_Float16)(w1 - (float)wh[1]);
         l_run[i][v] += p0 + p1;
-        corr[i][v] = fmaf((float)wp[1], zV[1], fmaf((float)wp[0], zV[0], corr[i][v]));
-        *reinterpret_cast<half2_t*>(wt + i * 16 * PG::WROW + wr_off[v]) = wp;
+        corr[i][v] = fmaf(w1, zV[1], fmaf(w0, zV[0], corr[i][v]));
+        *reinterpret_cast<half2_t*>(wt + (2 * i) * 16 * PG::WROW + wr_off[v]) = wh;
+        *reinterpret_cast<half2_t*>(wt + (2 * i + 1) * 16 * PG::WROW + wr_off[v]) = wl;
       }
     // weights in the A layout, read back from this wave's W tiles (LDS
     // operations of one wave complete in order)
-    half8_t wop[2];
+    half8_t wop[2], wlo[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      wop[i] = *reinterpret_cast<const half8_t*>(wt + i * 16 * PG::WROW + rd_off);
+    for (int i = 0; i < 2; ++i) {
+      wop[i] = *reinterpret_cast<const half8_t*>(wt + (2 * i) * 16 * PG::WROW + rd_off);
+      wlo[i] = *reinterpret_cast<const half8_t*>(wt + (2 * i + 1) * 16 * PG::WROW + rd_off);
+    }
 
     // V operands (shared by both row tiles) and O += W V.  Column tile c uses
     // nibble c (+ noff) of the lane's dword of each slot key.
@@ -429,9 +435,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         vb[k] = ys & ((nib & 1) ? 0x00F000F0u : 0x000F000Fu);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
         oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], __builtin_bit_cast(half8_t, vb),
                                                             oacc[i][c], 0, 0, 0);
+        oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo[i], __builtin_bit_cast(half8_t, vb),
+                                                            oacc[i][c], 0, 0, 0);
+      }
     }
   }
   wait_vmem<0>();  // drain the clamped look-ahead copies

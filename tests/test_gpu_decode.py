@@ -54,6 +54,15 @@ def test_decode_fp16_and_scaled_inputs(oracle_mod):
         _run_both(oracle_mod, w, [1, 4])
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 64), (6, 3, 128)])
+def test_decode_large_values(oracle_mod, hq, hkv, d):
+    """K and V scaled by 30 (|V| ~ 100, logits ~ 100) over many rows: the
+    softmax weights must carry more than f16 precision (hi + lo split)."""
+    w = wl.custom([(1, 300), (1, 77), (1, 513), (1, 160)] * 2, hq, hkv, d, dtype=torch.float16,
+                  seed=hq + 5 * d, write_all=True, scale=30.0)
+    _run_both(oracle_mod, w, [1, 7])
+
+
 def test_decode_empty_and_zero_length_sequences(oracle_mod):
     # sequence 1 has no query (q_len 0); sequence 2 has no keys (output zero)
     w = wl.custom([(1, 40), (0, 20), (1, 0), (1, 9)], 8, 2, 128, seed=4, write_all=True)

@@ -37,6 +37,16 @@ def test_prefill_mixed_lengths(oracle_mod, G, d):
     _run(oracle_mod, w)
 
 
+@pytest.mark.parametrize("scale", [1e-3, 30.0])
+@pytest.mark.parametrize("G,d", [(4, 128), (8, 64)])
+def test_prefill_scaled_inputs(oracle_mod, scale, G, d):
+    """fp16 inputs scaled down (tiny scales, subnormal-range f16 weights) and
+    up (logits of order 10^3: the query's hi + lo split must carry them)."""
+    w = wl.custom([(40, 120), (9, 300)], G * 2, 2, d, dtype=torch.float16, seed=11 + G + d,
+                  write_all=True, scale=scale)
+    _run(oracle_mod, w)
+
+
 def test_prefill_fp16_long_prompt(oracle_mod):
     w = wl.custom([(150, 1000), (97, 97)], 8, 2, 128, dtype=torch.float16, seed=7, write_all=True)
     _run(oracle_mod, w)
