@@ -99,13 +99,19 @@ struct Geo {
   static constexpr int NI = (U + HPW - 1) / HPW;           // DMA instructions of waves [0, NREM)
   static constexpr int NREM = U % HPW == 0 ? HPW : U % HPW;  // the others issue NI - 1
   static constexpr uint32_t stage = U * 1024;
-  // per-wave W tile: 16 rows of 80 bytes, then a zero row placed on the banks
-  // the rows of 4 query heads leave free
-  // The weights are split into f16 hi + lo (22 significant bits): the lo rows
-  // follow the hi rows.
+};
+
+// Per-wave W tile: one 80-byte row per query head of the group (8 rows for
+// groups of up to 8 heads, else 16), the weights split into f16 hi rows and
+// lo rows (22 significant bits), each half padded to a multiple of 256 bytes
+// so the bank pattern is the same for both; then a zero row placed on the
+// banks the rows of 4 query heads leave free.
+template <int G>
+struct WGeo {
+  static constexpr uint32_t ROWS = G <= 8 ? 8 : 16;
   static constexpr uint32_t WROW = 80;
-  static constexpr uint32_t WLO = 16 * WROW;
-  static constexpr uint32_t WZERO = 2 * 16 * WROW + 48;
+  static constexpr uint32_t WLO = (ROWS * WROW + 255) / 256 * 256;
+  static constexpr uint32_t WZERO = 2 * WLO + 48;
   static constexpr uint32_t wtile = WZERO + 64;
 };
 
@@ -119,12 +125,14 @@ struct Lay {
   using GG = Geo<D, HPW>;
   static constexpr uint32_t qstage = HPW * (G * D * 4 + 2 * G * 4);
   static constexpr uint32_t last = GG::stage > qstage ? GG::stage : qstage;
-  static constexpr uint32_t bytes(int s) { return (s - 1) * GG::stage + last + HPW * GG::wtile; }
+  static constexpr uint32_t bytes(int s) {
+    return (s - 1) * GG::stage + last + HPW * WGeo<G>::wtile;
+  }
   static constexpr bool fits(int s) { return s <= (HPW == 8 ? 6 : 4) && bytes(s) <= 160 * 1024; }
   static constexpr int S = fits(6) ? 6 : fits(5) ? 5 : fits(4) ? 4 : 3;
   static constexpr uint32_t qbase = (S - 1) * GG::stage;
   static constexpr uint32_t wbase = qbase + last;
-  static constexpr uint32_t total = wbase + HPW * GG::wtile;
+  static constexpr uint32_t total = wbase + HPW * WGeo<G>::wtile;
 };
 
 template <bool BF16, int D, int G, int HPW>
@@ -136,6 +144,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const float* __restrict__ signs, int32_t num_segments, float* __restrict__ segm_out,
     float* __restrict__ segm_max, float* __restrict__ segm_sum) {
   using GG = Geo<D, HPW>;
+  using WG = WGeo<G>;
   constexpr uint32_t R = GG::R;
   constexpr int DW = D / 8;      // code dwords per row
   constexpr int DWG = DW / 4;    // code dwords per lane group in the score operand
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   const uint32_t pair_g = 2 * half_g;  // bytes per cache block (K and V halves)
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
   const int32_t* bt = block_table + (int64_t)b * bt_stride;
-  unsigned char* wt = smem + Lay<D, G, HPW>::wbase + wave * GG::wtile;  // this wave's W tile
+  unsigned char* wt = smem + Lay<D, G, HPW>::wbase + wave * WG::wtile;  // this wave's W tile
 
   // ---- per-lane DMA sources (loop invariant).  Instruction i of wave w copies
   // unit u = i*HPW + w < U; units [0, UPB) hold block 0, [UPB, U) block 1; the
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     load_ids(S - 1);
   }
   // zero row of the W tile (MFMA rows that carry no query head read it)
-  if (lane < 16) reinterpret_cast<uint32_t*>(wt + GG::WZERO)[lane] = 0u;
+  if (lane < 16) reinterpret_cast<uint32_t*>(wt + WG::WZERO)[lane] = 0u;
   __syncthreads();
 
   // int8 planes of Q in the score MFMA's A layout.  Lane group g reads its K
@@ -331,7 +340,9 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
 
   float m_run[RPG], thr[RPG], l_run[RPG], corr[RPG];
-  float4_t oacc[NCOL];  // sum of W * code in units of 2^-24 (2^-20 for odd nibbles)
+  // column tile 2*beta: sum of W * (low nibble of byte beta) in units of 2^-24;
+  // tile 2*beta + 1: sum of W * (whole byte beta = low + 16 * high nibble)
+  float4_t oacc[NCOL];
 #pragma unroll
   for (int v = 0; v < RPG; ++v) {
     m_run[v] = -INFINITY;  // an empty segment reports m = -inf, l = 0
@@ -342,10 +353,20 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
   for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
   const int noff = (D == 64) ? 4 * (col >> 3) : 0;  // nibble offset of this lane's V dword
-  // O (rotated domain, zero point not yet removed) of column tile c
+  // O (rotated domain, zero point not yet removed) of column tile c: the low
+  // nibble directly, the high nibble as (byte - low) / 16
   auto o_of = [&](int c, int v) -> float {
-    return oacc[c][v] * (((c + noff) & 1) ? 1048576.0f : 16777216.0f);  // 2^20 : 2^24
+    return (c & 1) ? (oacc[c][v] - oacc[c - 1][v]) * 1048576.0f  // 2^20
+                   : oacc[c][v] * 16777216.0f;                   // 2^24
   };
+  // v_perm selectors: byte beta (+ noff / 2) of two slot keys' dwords, each
+  // zero-extended into one f16 half
+  uint32_t vsel[NCOL / 2];
+#pragma unroll
+  for (int bb = 0; bb < NCOL / 2; ++bb) {
+    const uint32_t by = (uint32_t)(bb + noff / 2);
+    vsel[bb] = 0x0C000C00u | by | ((4u + by) << 16);
+  }
 
   // per-lane LDS byte offsets inside a stage (loop invariant)
   const uint32_t hoff = (uint32_t)wave * R;
@@ -365,13 +386,13 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // are 80 bytes apart so the 16-byte reads of 8 lanes fall in distinct banks.
   uint32_t wr_off[RPG];
 #pragma unroll
-  for (int v = 0; v < RPG; ++v) wr_off[v] = (uint32_t)min(g * RPG + v, 15) * GG::WROW + 4 * col;
+  for (int v = 0; v < RPG; ++v) wr_off[v] = (uint32_t)min(g * RPG + v, (int)WG::ROWS - 1) * WG::WROW + 4 * col;
   uint32_t rd_off, rd_lo;
   {
     const int grp = col >> 2, vv = col & 3, qh = grp * RPG + vv;
     const bool valid = vv < RPG && qh < G;
-    rd_off = (valid ? (uint32_t)qh * GG::WROW : GG::WZERO) + 16 * g;
-    rd_lo = (valid ? GG::WLO + (uint32_t)qh * GG::WROW : GG::WZERO) + 16 * g;
+    rd_off = (valid ? (uint32_t)qh * WG::WROW : WG::WZERO) + 16 * g;
+    rd_lo = (valid ? WG::WLO + (uint32_t)qh * WG::WROW : WG::WZERO) + 16 * g;
   }
 
   // ---- int8 K operands of one tile (low nibbles as is, high nibbles shifted)
@@ -516,7 +537,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       l_run[v] += p0 + p1;
       corr[v] = fmaf(w1, zV[1], fmaf(w0, zV[0], corr[v]));
       *reinterpret_cast<half2_t*>(wt + wr_off[v]) = wh;
-      *reinterpret_cast<half2_t*>(wt + GG::WLO + wr_off[v]) = wl;
+      *reinterpret_cast<half2_t*>(wt + WG::WLO + wr_off[v]) = wl;
     }
     // weights in the A layout, read back from this wave's W tile right away
     // (LDS operations of one wave complete in order); the latency is covered
@@ -525,41 +546,41 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const half8_t wop_lo = *reinterpret_cast<const half8_t*>(wt + rd_lo);
     phase_end(1, kb, nxt);
 
-    // phase 3: V operand bytes (pairs of keys per dword)
-    uint32_t ylo[4], yhi[4];
+    // phase 3: V operands.  Byte beta of the lane's dword of two slot keys,
+    // each zero-extended into an f16 half: the subnormal (low + 16 * high) *
+    // 2^-24, exact in the products.
+    uint32_t vx[NCOL / 2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ylo[i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], 0x05040100u);  // a.b01 b.b01
-      yhi[i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], 0x07060302u);  // a.b23 b.b23
-    }
+    for (int bb = 0; bb < NCOL / 2; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vx[bb][i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], vsel[bb]);
     phase_end(2, kb, nxt);
 
-    // O += W V.  Column tile c uses nibble c (+ noff) of the lane's dword of
-    // each slot key, as a pair of f16 subnormals: code * 2^-24 for nibbles at
-    // even positions, 16 * code * 2^-24 at odd ones.
+    // O += W V: per byte, one column tile on the low nibbles (masked) and one
+    // on the whole bytes; the high nibble's column is their difference / 16.
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) {
-      const int nib = c + noff;
-      u32x4_t vb;
+    for (int bb = 0; bb < NCOL / 2; ++bb) {
+      u32x4_t vl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t y = (nib < 4) ? ylo[i] : yhi[i];
-        const uint32_t ys = (nib & 2) ? (y >> 8) : y;
-        vb[i] = ys & ((nib & 1) ? 0x00F000F0u : 0x000F000Fu);
-      }
-      oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
-                                                       oacc[c], 0, 0, 0);
-      oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, __builtin_bit_cast(half8_t, vb),
-                                                       oacc[c], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) vl[i] = vx[bb][i] & 0x000F000Fu;
+      const half8_t xb = __builtin_bit_cast(half8_t, vx[bb]);
+      const half8_t lb = __builtin_bit_cast(half8_t, vl);
+      float4_t& ol = oacc[2 * bb];
+      float4_t& ox = oacc[2 * bb + 1];
+      ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, xb, ox, 0, 0, 0);
+      ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, xb, ox, 0, 0, 0);
+      ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, lb, ol, 0, 0, 0);
+      ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, lb, ol, 0, 0, 0);
     }
     // the remaining score groups of tile t+1 share this region: one MFMA per
-    // four vector instructions of the V operand expansion
+    // vector instruction of the low-nibble masks
 #pragma unroll
     for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
 #pragma unroll
     for (int j = 0; j < 2 * NCOL + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
