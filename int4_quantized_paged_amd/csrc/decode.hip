@@ -480,24 +480,12 @@ __global__ __launch_bounds__(512) void decode_kernel(
 
 // Segment reduction: one 256-thread block per (sequence, query head).
 // M = max_k m_k, L = sum_k l_k 2^(m_k - M), O = sum_k O_k 2^(m_k - M) / L, then
-// the inverse rotation signs * H O / D.  The four waves split the segments and
-// combine through LDS.
-__device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_rt(v, m));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += shfl_xor_rt(v, m);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
+// the inverse rotation signs * H O / D.  Wave w takes segments w, w + 4, ...,
+// in chunks of kRedChunk whose loads are all issued before any is used, and
+// keeps its own running reference maximum; the four waves' (M, L, O) are then
+// merged once through LDS.  The order of every sum is fixed, so the result
+// does not depend on timing.
+constexpr int kRedChunk = 16;
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void reduce_kernel(
@@ -505,48 +493,66 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     const float* __restrict__ signs, int32_t num_segments, const float* __restrict__ segm_out,
     const float* __restrict__ segm_max, const float* __restrict__ segm_sum) {
   constexpr int EPL = D / 64;
-  __shared__ float red[4];
+  __shared__ float wm[4], wl[4];
   __shared__ float part[4][D];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x / num_q_heads;
   const int qg = blockIdx.x % num_q_heads;
   const int q0 = cu_seqlens_q[b];
   if (cu_seqlens_q[b + 1] - q0 <= 0) return;  // uniform over the block
   const int64_t base = ((int64_t)b * num_q_heads + qg) * num_segments;
 
-  float mloc = -INFINITY;
-  for (int k = tid; k < num_segments; k += 256) mloc = fmaxf(mloc, segm_max[base + k]);
-  const float M = block_max(mloc, red);
-  float lloc = 0.f;
-  if (M != -INFINITY)
-    for (int k = tid; k < num_segments; k += 256) {
-      const float mk = segm_max[base + k];
-      if (mk != -INFINITY) lloc += segm_sum[base + k] * exp2f(mk - M);
-    }
-  const float Lsum = block_sum(lloc, red);
-
+  float Mw = -INFINITY, lw = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int k = wv; k < num_segments; k += 4) {
-      const float mk = segm_max[base + k];
-      const float f = mk == -INFINITY ? 0.f : exp2f(mk - M);
-      const float* src = segm_out + (base + k) * D + lane * EPL;
+  for (int k0 = wv; k0 < num_segments; k0 += 4 * kRedChunk) {
+    float mk[kRedChunk], lk[kRedChunk], src[kRedChunk][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] += src[e] * f;
+    for (int j = 0; j < kRedChunk; ++j) {
+      const int k = k0 + 4 * j;
+      const bool ok = k < num_segments;
+      mk[j] = ok ? segm_max[base + k] : -INFINITY;
+      lk[j] = ok ? segm_sum[base + k] : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) src[j][e] = ok ? segm_out[(base + k) * D + lane * EPL + e] : 0.f;
     }
+    float Mn = Mw;
+#pragma unroll
+    for (int j = 0; j < kRedChunk; ++j) Mn = fmaxf(Mn, mk[j]);
+    if (Mn == -INFINITY) continue;  // no keys so far (uniform over the wave)
+    const float a = Mw == -INFINITY ? 0.f : exp2f(Mw - Mn);
+    lw *= a;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] *= a;
+#pragma unroll
+    for (int j = 0; j < kRedChunk; ++j) {
+      const float f = mk[j] == -INFINITY ? 0.f : exp2f(mk[j] - Mn);
+      lw = fmaf(lk[j], f, lw);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(src[j][e], f, o[e]);
+    }
+    Mw = Mn;
+  }
+  if (lane == 0) {
+    wm[wv] = Mw;
+    wl[wv] = lw;
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) part[wv][lane * EPL + e] = o[e];
   __syncthreads();
   if (wv != 0) return;
+  const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  float f[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) f[w] = wm[w] == -INFINITY ? 0.f : exp2f(wm[w] - M);
+  const float Lsum = (wl[0] * f[0] + wl[1] * f[1]) + (wl[2] * f[2] + wl[3] * f[3]);
   const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const int d = lane * EPL + e;
-    o[e] = ((part[0][d] + part[1][d]) + (part[2][d] + part[3][d])) * inv;
+    o[e] = ((part[0][d] * f[0] + part[1][d] * f[1]) + (part[2][d] * f[2] + part[3][d] * f[3])) * inv;
   }
 #pragma unroll
   for (int span = 1; span < EPL; span <<= 1) {

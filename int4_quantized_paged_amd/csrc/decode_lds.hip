@@ -155,6 +155,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int LPQ = 64 / G;
   constexpr int NI = GG::NI;
   constexpr int S = Lay<D, G, HPW>::S;
+  // with four or more ring stages the workgroup synchronises every other step
+  constexpr bool kPairSync = S >= 4;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
@@ -208,16 +210,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       goff[i] = off;
     }
   }
-  // block ids of the next tile to copy, read one step before they are needed
-  // so the scalar loads never stall the copy issue
-  uint32_t nid0 = 0, nid1 = 0;
-  auto load_ids = [&](int tile) {
-    nid0 = (uint32_t)bt[min(b0 + 2 * tile, b1 - 1)];
-    nid1 = (uint32_t)bt[min(b0 + 2 * tile + 1, b1 - 1)];
+  // block ids of the next tiles to copy (two slots), read one step before
+  // they are needed so the scalar loads never stall the copy issue
+  uint32_t nid[2][2] = {{0u, 0u}, {0u, 0u}};
+  auto load_ids = [&](int slot, int tile) {
+    nid[slot][0] = (uint32_t)bt[min(b0 + 2 * tile, b1 - 1)];
+    nid[slot][1] = (uint32_t)bt[min(b0 + 2 * tile + 1, b1 - 1)];
   };
-  auto issue = [&](int tile) {  // nid0 / nid1 hold this tile's block ids
-    const uint8_t* p0 = cache + (uint64_t)nid0 * pair_g;
-    const uint8_t* p1 = cache + (uint64_t)nid1 * pair_g;
+  auto issue = [&](int slot, int tile) {  // nid[slot] holds this tile's block ids
+    const uint8_t* p0 = cache + (uint64_t)nid[slot][0] * pair_g;
+    const uint8_t* p1 = cache + (uint64_t)nid[slot][1] * pair_g;
     asm volatile("" : "+s"(p0), "+s"(p1));  // keep both bases in SGPRs; select per copy
     const uint32_t sb = lds0 + (uint32_t)(tile % S) * GG::stage + (uint32_t)wave * 1024;
 #pragma unroll
@@ -287,13 +289,14 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - 22);
     }
   }
-  if (ntile > 0) {  // always S - 1 tiles ahead (clamped), so the vmcnt below is exact
+  if (ntile > 0) {  // always S - 1 tiles ahead (clamped), so the vmcnts below are exact
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) {
-      load_ids(i);
-      issue(i);
+      load_ids(0, i);
+      issue(0, i);
     }
-    load_ids(S - 1);
+    load_ids(0, S - 1);
+    if constexpr (kPairSync) load_ids(1, S);
   }
   // zero row of the W tile (MFMA rows that carry no query head read it)
   if (lane < 16) reinterpret_cast<uint32_t*>(wt + WG::WZERO)[lane] = 0u;
@@ -455,12 +458,27 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int j = 0; j < 8; ++j) w.va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
   };
 
-  auto step = [&](int t, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3], const TileWords& cw,
-                  TileWords& nw) {
-    wait_tiles(std::integral_constant<int, S - 3>());  // this wave's copies of tile t+1
-    __syncthreads();   // ... and everyone's; everyone is done with tile t-1
-    issue(t + S - 1);  // into the stage of tile t-1 (clamped to the segment's last block)
-    load_ids(t + S);
+  auto step = [&](int t, auto even, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3],
+                  const TileWords& cw, TileWords& nw) {
+    if constexpr (kPairSync) {
+      // one barrier per two steps: at an even step, tiles t+1 and t+2 must
+      // have landed for every wave (their words are read in this step and the
+      // next), and everyone is done with tiles t-1 and t, whose stages take
+      // tiles t+S-1 and t+S (clamped to the segment's last block)
+      if constexpr (decltype(even)::value) {
+        wait_tiles(std::integral_constant<int, S - 4>());
+        __syncthreads();
+        issue(0, t + S - 1);
+        issue(1, t + S);
+        load_ids(0, t + S + 1);
+        load_ids(1, t + S + 2);
+      }
+    } else {
+      wait_tiles(std::integral_constant<int, S - 3>());  // this wave's copies of tile t+1
+      __syncthreads();      // ... and everyone's; everyone is done with tile t-1
+      issue(0, t + S - 1);  // into the stage of tile t-1 (clamped to the segment's last block)
+      load_ids(0, t + S);
+    }
     const unsigned char* st = smem + (uint32_t)(t % S) * GG::stage;
     const int tb = b0 + 2 * t;
 
@@ -601,10 +619,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
   int t = 0;
   for (; t + 1 < ntile; t += 2) {
-    step(t, accA, accB, wA, wB);
-    step(t + 1, accB, accA, wB, wA);
+    step(t, std::true_type(), accA, accB, wA, wB);
+    step(t + 1, std::false_type(), accB, accA, wB, wA);
   }
-  if (t < ntile) step(t, accA, accB, wA, wB);
+  if (t < ntile) step(t, std::true_type(), accA, accB, wA, wB);
   wait_vmem<0>();  // drain the clamped look-ahead copies
 
   // ---- finalise: sums over the 16 lanes of a group

@@ -9,11 +9,13 @@
 // its section 4 (slot < 0 writes nothing).
 //
 // Work layout: one row = one (token, K|V, head) vector of D elements, held by
-// D/64 lanes with 64 consecutive elements each (2 lanes at D = 128, 1 at
-// D = 64), so a wave covers 32 (or 64) rows.  The Walsh-Hadamard butterflies
-// of span 1..32 run inside a lane and the last one (span 64) pairs the two
-// lanes of a row through DPP, which keeps the spans in the order the encoding
-// fixes.  Every fp32 operation is a single correctly rounded op in that order,
+// D/E lanes with E consecutive elements each.  Bulk writes use E = 64 (2
+// lanes per row at D = 128, 1 at D = 64: the fewest cross-lane steps per
+// element); writes of fewer rows than fill the GPU use E = 16 (8 or 4 lanes
+// per row: a chain four times shorter per row, four times as many waves).
+// The Walsh-Hadamard butterflies of span 1..E/2 run inside a lane and the
+// spans E, 2E, ... pair the lanes of a row through DPP, which keeps the spans
+// in the increasing order the encoding fixes.  Every fp32 operation is a single correctly rounded op in that order,
 // so the packed bytes are reproducible bit for bit (this file is built without
 // FMA contraction):
 //   * the signs are applied as bit flips of the 16-bit inputs (exact),
@@ -42,31 +44,35 @@ __device__ __forceinline__ float half_of(uint32_t w, int i) {
   }
 }
 
+// rows at and above which writes take 64 elements per lane
+constexpr int64_t kBulkRows = 65536;
+
 }  // namespace
 
-template <bool BF16, int D>
+template <bool BF16, int D, int E>
 __global__ __launch_bounds__(256) void write_kernel(
     const uint16_t* __restrict__ key, int64_t key_stride, const uint16_t* __restrict__ value,
     int64_t value_stride, const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
     uint8_t* __restrict__ cache, int32_t num_kv_heads, const float* __restrict__ signs) {
-  constexpr int LPR = D / 64;            // lanes per row
+  constexpr int LPR = D / E;             // lanes per row
   constexpr int RPW = kWave / LPR;       // rows per wave
   constexpr int R = D / 2 + 4;           // packed row bytes
+  constexpr int NV = E / 8;              // 16-byte input vectors per lane
+  constexpr int NP = E / 8;              // packed code dwords per lane
   const int lane = threadIdx.x & 63;
-  const int sub = lane % LPR;            // which 64-element half of the row
+  const int sub = lane % LPR;            // which E-element piece of the row
   const int rw = lane / LPR;
   const int64_t total_rows = (int64_t)num_tokens * 2 * num_kv_heads;
   const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x / kWave);
   const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
 
-  // sign bits of the lane's 64 elements, as flips of 16-bit pairs
-  uint32_t flip[32];
+  // sign bits of the lane's E elements, as flips of 16-bit pairs
+  uint32_t flip[E / 2];
 #pragma unroll
-  for (int p = 0; p < 32; ++p) {
-    const float s0 = signs[64 * sub + 2 * p], s1 = signs[64 * sub + 2 * p + 1];
+  for (int p = 0; p < E / 2; ++p) {
+    const float s0 = signs[E * sub + 2 * p], s1 = signs[E * sub + 2 * p + 1];
     flip[p] = (s0 < 0.f ? 0x8000u : 0u) | (s1 < 0.f ? 0x80000000u : 0u);
   }
-  const uint32_t xflip = sub ? 0x80000000u : 0u;  // upper lane of a row keeps u - v
 
   // row coordinates and the raw 16-bit inputs of one row (software-pipelined:
   // the next row's loads are in flight while the current row is encoded)
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(256) void write_kernel(
     int64_t t;
     int h, kv;
     bool ok;
-    u32x4_t a[8];
+    u32x4_t a[NV];
   };
   auto fetch = [&](int64_t base, RowIn& in) {
     const int64_t row = base + rw;
@@ -85,10 +91,10 @@ __global__ __launch_bounds__(256) void write_kernel(
     in.kv = (int)(tk & 1);
     in.t = tk >> 1;
     const uint16_t* src = (in.kv == 0 ? key + in.t * key_stride : value + in.t * value_stride) +
-                          (int64_t)in.h * D + 64 * sub;
+                          (int64_t)in.h * D + E * sub;
     const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(src);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) in.a[k] = s4[k];
+    for (int k = 0; k < NV; ++k) in.a[k] = s4[k];
   };
   const int64_t stride = waves_total * RPW;
   int64_t base = wave_id * RPW;
@@ -101,9 +107,9 @@ __global__ __launch_bounds__(256) void write_kernel(
     const int64_t t = cur.t;
     const int h = cur.h, kv = cur.kv;
     const bool in_range = cur.ok;
-    float x[64];
+    float x[E];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NV; ++k) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w = cur.a[k][j] ^ flip[4 * k + j];  // x * sign, exactly
@@ -112,23 +118,25 @@ __global__ __launch_bounds__(256) void write_kernel(
       }
     }
 
-    // butterflies inside the lane: spans 1 .. 32
+    // butterflies inside the lane: spans 1 .. E/2
 #pragma unroll
-    for (int span = 1; span < 64; span <<= 1) {
+    for (int span = 1; span < E; span <<= 1) {
 #pragma unroll
-      for (int e = 0; e < 64; ++e) {
+      for (int e = 0; e < E; ++e) {
         if (e & span) continue;
         const float u = x[e], v = x[e + span];
         x[e] = __fadd_rn(u, v);
         x[e + span] = __fsub_rn(u, v);
       }
     }
-    // span 64 across the two lanes of a row: the lower lane keeps u + v, the
-    // upper one u - v, written as partner + (-self)
-    if constexpr (LPR == 2) {
+    // spans E, 2E, ... across the lanes of a row: the lower partner keeps
+    // u + v, the upper one u - v, written as partner + (-self)
 #pragma unroll
-      for (int e = 0; e < 64; ++e) {
-        const float p = shfl_xor<1>(x[e]);
+    for (int m = 1; m < LPR; m <<= 1) {
+      const uint32_t xflip = (sub & m) ? 0x80000000u : 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float p = shfl_xor_rt(x[e], m);
         x[e] = __fadd_rn(p, as_float(as_uint(x[e]) ^ xflip));
       }
     }
@@ -136,13 +144,14 @@ __global__ __launch_bounds__(256) void write_kernel(
     // row range
     float mn = fminf(x[0], x[1]), mx = fmaxf(x[0], x[1]);
 #pragma unroll
-    for (int e = 2; e < 64; e += 2) {
+    for (int e = 2; e < E; e += 2) {
       mn = __builtin_fminf(mn, __builtin_fminf(x[e], x[e + 1]));
       mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[e], x[e + 1]));
     }
-    if constexpr (LPR == 2) {
-      mn = fminf(mn, shfl_xor<1>(mn));
-      mx = fmaxf(mx, shfl_xor<1>(mx));
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+      mn = fminf(mn, shfl_xor_rt(mn, m));
+      mx = fmaxf(mx, shfl_xor_rt(mx, m));
     }
     float sc = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
     if (!(sc > 1e-6f)) sc = 1e-6f;
@@ -152,9 +161,9 @@ __global__ __launch_bounds__(256) void write_kernel(
 
     // codes: clamp to [0, 15], then round to nearest even by adding 2^23; the
     // code is then the low 4 bits of the sum's bit pattern
-    uint32_t packed[8];
+    uint32_t packed[NP];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NP; ++q) {
       uint32_t b[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -174,9 +183,15 @@ __global__ __launch_bounds__(256) void write_kernel(
     if (in_range && slot >= 0) {
       const int64_t blk = slot / kBlockSize, off = slot % kBlockSize;
       uint8_t* dst = cache + (((blk * 2 + kv) * kBlockSize + off) * num_kv_heads + h) * R;
-      u32x4a4_t* d16 = reinterpret_cast<u32x4a4_t*>(dst + 32 * sub);  // rows are 4-byte aligned
-      d16[0] = u32x4a4_t{packed[0], packed[1], packed[2], packed[3]};
-      d16[1] = u32x4a4_t{packed[4], packed[5], packed[6], packed[7]};
+      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + (E / 2) * sub);  // rows are 4-byte aligned
+      if constexpr (E == 64) {
+        u32x4a4_t* d16 = reinterpret_cast<u32x4a4_t*>(d32);
+        d16[0] = u32x4a4_t{packed[0], packed[1], packed[2], packed[3]};
+        d16[1] = u32x4a4_t{packed[4], packed[5], packed[6], packed[7]};
+      } else {
+#pragma unroll
+        for (int q = 0; q < NP; ++q) d32[q] = packed[q];
+      }
       if (sub == 0) reinterpret_cast<uint32_t*>(dst)[D / 8] = as_uint(s_t) | (uint32_t)zpf;
     }
     cur = nxt;
@@ -188,21 +203,33 @@ hipError_t launch_write(const void* key, int64_t key_stride, const void* value,
                         int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
                         int32_t head_size, const float* signs, hipStream_t stream) {
   const int64_t rows = (int64_t)num_tokens * 2 * num_kv_heads;
-  const int rows_per_block = 4 * (kWave / (head_size / 64));
+  // 64 elements per lane once there are enough rows for every SIMD to hold
+  // several waves of them; 16 below that, where the per-row chain is the cost
+  const bool bulk = rows >= kBulkRows;
+  const int e = bulk ? 64 : 16;
+  const int rows_per_block = 4 * (kWave / (head_size / e));
   int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   const int64_t cap = 256 * 32;  // grid-stride beyond 32 blocks per CU
   if (blocks > cap) blocks = cap;
   dim3 grid((unsigned)blocks), block(256);
   auto k16 = reinterpret_cast<const uint16_t*>(key);
   auto v16 = reinterpret_cast<const uint16_t*>(value);
-#define INT4KV_W(BF, DD)                                                                  \
-  hipLaunchKernelGGL((write_kernel<BF, DD>), grid, block, 0, stream, k16, key_stride, v16, \
+#define INT4KV_W(BF, DD, EE)                                                                  \
+  hipLaunchKernelGGL((write_kernel<BF, DD, EE>), grid, block, 0, stream, k16, key_stride, v16, \
                      value_stride, slot_mapping, num_tokens, cache, num_kv_heads, signs)
+#define INT4KV_WE(BF, DD) \
+  do {                    \
+    if (bulk)             \
+      INT4KV_W(BF, DD, 64); \
+    else                  \
+      INT4KV_W(BF, DD, 16); \
+  } while (0)
   if (bf16) {
-    if (head_size == 128) INT4KV_W(true, 128); else INT4KV_W(true, 64);
+    if (head_size == 128) INT4KV_WE(true, 128); else INT4KV_WE(true, 64);
   } else {
-    if (head_size == 128) INT4KV_W(false, 128); else INT4KV_W(false, 64);
+    if (head_size == 128) INT4KV_WE(false, 128); else INT4KV_WE(false, 64);
   }
+#undef INT4KV_WE
 #undef INT4KV_W
   return hipGetLastError();
 }

@@ -42,6 +42,23 @@ def test_write_page_grid_bit_exact(oracle_mod, T, hkv, d, dtype):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [4000, 4100])
+def test_write_both_lane_layouts(oracle_mod, T, d):
+    """8 KV heads: 4000 tokens (64000 rows) take the 16-elements-per-lane
+    layout, 4100 tokens (65600 rows) the 64-elements-per-lane one; both bit
+    for bit over the whole cache."""
+    header(f"write lane layouts T={T} d={d}")
+    random.seed(T + d)
+    g = torch.Generator().manual_seed(T + d)
+    nb = (T + 15) // 16 + 8
+    slots = torch.tensor(random.sample(range(nb * 16), T), dtype=torch.int64)
+    key = torch.randn((T, 8, d), generator=g).to(torch.bfloat16)
+    value = (3.0 * torch.randn((T, 8, d), generator=g)).to(torch.bfloat16)
+    got, ref = _write_both(oracle_mod, key, value, slots, nb, 8, d, wl.rht_signs(d))
+    assert np.array_equal(got, ref)
+
+
 def test_write_negative_slots(oracle_mod):
     header("write negative slots")
     g = torch.Generator().manual_seed(5)
