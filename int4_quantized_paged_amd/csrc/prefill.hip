@@ -286,6 +286,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     wr_off[v] = (uint32_t)(4 * g + v) * PG::WROW + 4 * (4 * (col % 4) + col / 4);
   const uint32_t rd_off = (uint32_t)col * PG::WROW + 16 * g;  // reader: row col
   const int noff = (D == 64) ? 4 * (col >> 3) : 0;      // nibble offset of this lane's V dword
+  // v_perm selectors: byte bb (+ noff / 2) of two slot keys' dwords, each
+  // zero-extended into one f16 half
+  uint32_t vsel[NCOL / 2];
+#pragma unroll
+  for (int bb = 0; bb < NCOL / 2; ++bb) {
+    const uint32_t by = (uint32_t)(bb + noff / 2);
+    vsel[bb] = 0x0C000C00u | by | ((4u + by) << 16);
+  }
 
   // steps s = 0 .. nsteps-1 process tiles 2s (even group) and 2s+1 (odd
   // group); each group keeps kPairs - 1 of its own tiles in flight.  A tile
@@ -416,30 +424,29 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       wlo[i] = *reinterpret_cast<const half8_t*>(wt + (2 * i + 1) * 16 * PG::WROW + rd_off);
     }
 
-    // V operands (shared by both row tiles) and O += W V.  Column tile c uses
-    // nibble c (+ noff) of the lane's dword of each slot key.
-    uint32_t ylo[4], yhi[4];
+    // V operands (shared by both row tiles) and O += W V.  Byte bb (+ noff/2)
+    // of the lane's dword of two slot keys, zero-extended into f16 halves, is
+    // the subnormal (low + 16 high) * 2^-24; masked, the low nibble alone.
+    // Column tile 2bb takes the low nibbles, 2bb + 1 the whole bytes; the
+    // high nibble's column is their difference / 16.
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ylo[k] = __builtin_amdgcn_perm(va[2 * k + 1], va[2 * k], 0x05040100u);  // a.b01 b.b01
-      yhi[k] = __builtin_amdgcn_perm(va[2 * k + 1], va[2 * k], 0x07060302u);  // a.b23 b.b23
-    }
-#pragma unroll
-    for (int c = 0; c < NCOL; ++c) {
-      const int nib = c + noff;
-      u32x4_t vb;
+    for (int bb = 0; bb < NCOL / 2; ++bb) {
+      u32x4_t vx, vl;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t y = (nib < 4) ? ylo[k] : yhi[k];
-        const uint32_t ys = (nib & 2) ? (y >> 8) : y;
-        vb[k] = ys & ((nib & 1) ? 0x00F000F0u : 0x000F000Fu);
+        vx[k] = __builtin_amdgcn_perm(va[2 * k + 1], va[2 * k], vsel[bb]);
+        vl[k] = vx[k] & 0x000F000Fu;
       }
+      const half8_t xb = __builtin_bit_cast(half8_t, vx);
+      const half8_t lb = __builtin_bit_cast(half8_t, vl);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], __builtin_bit_cast(half8_t, vb),
-                                                            oacc[i][c], 0, 0, 0);
-        oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo[i], __builtin_bit_cast(half8_t, vb),
-                                                            oacc[i][c], 0, 0, 0);
+        float4_t& ol = oacc[i][2 * bb];
+        float4_t& ox = oacc[i][2 * bb + 1];
+        ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], xb, ox, 0, 0, 0);
+        ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], lb, ol, 0, 0, 0);
+        ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo[i], xb, ox, 0, 0, 0);
+        ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo[i], lb, ol, 0, 0, 0);
       }
     }
   }
@@ -483,7 +490,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   }
 
   // ---- finalise and rotate back.  Column tile c holds element dof(c) of this
-  // lane; its accumulator is in units of 2^-24 (and 2^-20 for odd nibbles).
+  // lane: even tiles directly in units of 2^-24, odd ones as (bytes - low) in
+  // units of 2^-20.
   auto dof = [&](int c) -> int {
     return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
   };
@@ -504,8 +512,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       float o[NCOL];
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) {
-        const float unit = ((c + noff) & 1) ? 1048576.0f : 16777216.0f;  // 2^20 : 2^24
-        o[c] = (oacc[i][c][v] * unit - cv) * inv_l;
+        const float oc = (c & 1) ? (oacc[i][c][v] - oacc[i][c - 1][v]) * 1048576.0f  // 2^20
+                                 : oacc[i][c][v] * 16777216.0f;                      // 2^24
+        o[c] = (oc - cv) * inv_l;
       }
 #pragma unroll
       for (int span = 1; span < (D == 128 ? 8 : 4); span <<= 1) {
