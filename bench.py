@@ -2,9 +2,12 @@
 
 Workload: long-context decode, 4 sequences x 131072 tokens, 64 query heads,
 8 KV heads, head_size 128, bf16 inputs, split-K over 64 segments.  One step =
-write the new token of every sequence into the packed cache (int4_kv_write),
-then one decode step of causal paged attention over the full context
-(int4_paged_attention: split-K kernel + segment reduction).  Two independent
+write the new token of every sequence into the packed cache, then one decode
+step of causal paged attention over the full context: int4_decode_step, which
+does both in the split-K launch (the workgroup that reads a new token's block
+encodes and stores it first) followed by the segment reduction;
+`--separate-calls` times int4_kv_write + int4_paged_attention instead (same
+bytes and output, one more launch).  Two independent
 caches alternate between steps so that no step reads a cache still resident
 in the 256 MB Infinity Cache.
 
@@ -12,7 +15,8 @@ Steps are plain library calls: the host enqueues a step in about a fifth of
 its GPU time, and HIP-graph replays of the same calls (`--graph`, checked bit
 for bit against plain calls) measured a few microseconds slower per step.
 The default warm-up (100 steps) lets the GPU reach its steady clock and
-address-translation state; the first tens of steps run about 15% slower.  Prints one JSON line: decode
+address-translation state; the first tens of steps run about 15% slower.
+Prints one JSON line: decode
 effective KV GB/s (packed K+V bytes of every key attended, once per KV head,
 over the step time), the bulk cache-write rate (tokens/s, from a timed
 full-cache fill), the roofline of the attention call (HIP events on the
@@ -109,6 +113,17 @@ def attend(b):
 
 
 def step(b):
+    """One decode step in one launch: the new tokens' rows are encoded by the
+    workgroups that read their blocks (int4_decode_step)."""
+    w = b["w"]
+    ik.int4_decode_step(b["key_new"], b["value_new"], b["slots_new"], b["query"], b["cache"],
+                        b["cu"], b["su"], 1, w.max_seqlen_k, b["bt"], w.softmax_scale,
+                        b["signs"], out=b["out"], num_segments=NUM_SEGMENTS,
+                        segm_output=b["segs"][0], segm_max=b["segs"][1],
+                        segm_expsum=b["segs"][2])
+
+
+def step_separate(b):
     write_new(b)
     attend(b)
 
@@ -270,6 +285,8 @@ def main():
                     help="only the prefill and Llama-3-shaped decode measurements (for profiling)")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the library calls instead of plain calls")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time the step as int4_kv_write + int4_paged_attention (two calls)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -301,14 +318,15 @@ def main():
     w = bufs[0]["w"]
     kv_bytes = w.kv_bytes_attended()
 
+    step_fn = step_separate if args.separate_calls else step
     if args.graph:
-        graphs = [capture(lambda b=b: step(b)) for b in bufs]
+        graphs = [capture(lambda b=b: step_fn(b)) for b in bufs]
         attn_graphs = [capture(lambda b=b: attend(b)) for b in bufs]
         check_replay(bufs, attn_graphs)
         run = [g.replay for g in graphs]
         run_attn = [g.replay for g in attn_graphs]
     else:
-        run = [lambda b=b: step(b) for b in bufs]
+        run = [lambda b=b: step_fn(b) for b in bufs]
         run_attn = [lambda b=b: attend(b) for b in bufs]
 
     for i in range(args.warmup):
@@ -343,6 +361,8 @@ def main():
         "config": {"workload": "long-context decode: 4 seqs x 131072 tokens, 64 q / 8 KV heads, "
                                "head_size 128, bf16 K/V/Q N(0,1), block_size 16, split-K 64 "
                                "segments + segment reduction; step = write 4 new tokens + decode",
+                   "step_call": ("int4_kv_write + int4_paged_attention" if args.separate_calls
+                                 else "int4_decode_step (write fused into the decode launch)"),
                    "global_batch": 4, "seq_len": 131072, "parallelism": "none (1 GPU)",
                    "launch": "hip graph replay" if args.graph else "plain calls"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),

@@ -141,6 +141,43 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
                                      int32_t num_segments, float* segm_output, float* segm_max,
                                      float* segm_expsum, void* stream);
 
+/*
+ * int4_decode_step: int4_kv_write of one new token per sequence followed by
+ * int4_paged_attention, in one launch on the decode path.
+ * (The write half and the read half above, in the order a decode step runs
+ *  them: [report] implementation breakdown, items 2 and 5; [testfile] §2 and
+ *  §6 call the write, then unified_attention, on the same cache.)
+ *
+ * The result (cache bytes and `out`) is the same as the two calls in that
+ * order.  Token b of key_new / value_new belongs to sequence b and must be its
+ * last key: slot_mapping[b] is the cache position of key seqused_k[b] - 1 of
+ * sequence b, or < 0 (nothing written for that sequence).  With
+ * max_seqlen_q == 1 and a KV-head count that the LDS-staged decode kernel
+ * takes (1, 2, 4, 8 or a multiple of 8), the workgroup whose split-K segment
+ * holds that key's block encodes and stores the token's rows before copying
+ * the block, so no separate write launch is needed; otherwise the library
+ * enqueues the write and then the attention.
+ *
+ *   key_new, value_new  [num_seqs, num_kv_heads, head_size] of `dtype` (the
+ *                       dtype of q), token stride given (elements, multiple of
+ *                       8), heads contiguous, 16-byte aligned base.
+ *   slot_mapping        int64 [num_seqs].
+ *   the other arguments as for int4_paged_attention; kv_cache is written.
+ * Errors and support as for the two calls.  num_seqs == 0 is a no-op.
+ */
+int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
+                                 const void* value_new, int64_t value_token_stride,
+                                 const int64_t* slot_mapping, const void* q,
+                                 int64_t q_token_stride, void* out, int4kv_dtype_t dtype,
+                                 uint8_t* kv_cache, int32_t num_blocks, int32_t block_size,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t num_q_heads,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 const int32_t* block_table, int32_t block_table_stride,
+                                 float softmax_scale, const float* rht_signs,
+                                 int32_t num_segments, float* segm_output, float* segm_max,
+                                 float* segm_expsum, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* int4kv_status_string(int4kv_status_t s);
 

@@ -8,6 +8,7 @@ library is missing, every call raises: there is no CPU fallback.
 Exports the C entry points under the same names:
     int4_kv_write(...)          quantize + pack K/V rows into the paged cache
     int4_paged_attention(...)   causal attention over the packed cache
+    int4_decode_step(...)       both for a decode step, in one launch where it can
 plus small helpers to size and allocate the buffers those calls take.
 """
 from __future__ import annotations
@@ -18,7 +19,7 @@ import os
 import torch
 
 __all__ = [
-    "int4_kv_write", "int4_paged_attention", "int4kv_cache_bytes", "int4kv_status_string",
+    "int4_kv_write", "int4_paged_attention", "int4_decode_step", "int4kv_cache_bytes", "int4kv_status_string",
     "int4kv_last_error", "Int4KVError", "cache_shape", "empty_cache", "segment_buffers",
     "library_path", "load_library",
 ]
@@ -63,6 +64,10 @@ def load_library():
     lib.int4_paged_attention.argtypes = [P, i64, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P, P,
                                          i32, i32, i32, P, i32, ctypes.c_float, P, i32, P, P, P, P]
     lib.int4_paged_attention.restype = ctypes.c_int
+    lib.int4_decode_step.argtypes = [P, i64, P, i64, P, P, i64, P, ctypes.c_int, P, i32, i32, i32,
+                                     i32, i32, P, P, i32, i32, i32, P, i32, ctypes.c_float, P,
+                                     i32, P, P, P, P]
+    lib.int4_decode_step.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -176,4 +181,53 @@ def int4_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: 
         int(max_seqlen_k), _ptr(block_table), block_table.stride(0), float(softmax_scale),
         _ptr(rht_signs.contiguous()), int(num_segments), _ptr(segm_output), _ptr(segm_max),
         _ptr(segm_expsum), _stream(q.device)))
+    return out
+
+
+def int4_decode_step(key_new: torch.Tensor, value_new: torch.Tensor, slot_mapping: torch.Tensor,
+                     q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                     seqused_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                     block_table: torch.Tensor, softmax_scale: float, rht_signs: torch.Tensor,
+                     out: torch.Tensor | None = None, num_segments: int = 1,
+                     segm_output: torch.Tensor | None = None,
+                     segm_max: torch.Tensor | None = None,
+                     segm_expsum: torch.Tensor | None = None) -> torch.Tensor:
+    """``int4_kv_write`` of one new token per sequence (``key_new``/``value_new``
+    [S, Hkv, d], token b is sequence b's last key, at ``slot_mapping[b]``), then
+    ``int4_paged_attention``; one launch on the decode path.  Returns ``out``."""
+    lib = load_library()
+    S = seqused_k.shape[0]
+    if key_new.dim() != 3 or value_new.shape != key_new.shape or key_new.shape[0] != S:
+        raise ValueError("key_new and value_new must both be [S, Hkv, d], one token per sequence")
+    if key_new.dtype != q.dtype or value_new.dtype != q.dtype:
+        raise ValueError("key_new, value_new and q must share one dtype")
+    for t in (key_new, value_new):
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError("key_new/value_new heads must be contiguous")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,):
+        raise ValueError("slot_mapping must be int64 [S]")
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [Tq, Hq, d] with contiguous heads")
+    Tq, hq, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, hq, d), dtype=q.dtype, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous with q's shape and dtype")
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 5 or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous uint8 [NB, 2, B, Hkv, d/2+4] tensor")
+    nb, two, bs, hkv, _ = kv_cache.shape
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k),
+                    ("block_table", block_table)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [S, max_blocks] with unit column stride")
+    _check(lib.int4_decode_step(
+        _ptr(key_new), key_new.stride(0), _ptr(value_new), value_new.stride(0),
+        _ptr(slot_mapping.contiguous()), _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype),
+        _ptr(kv_cache), nb, bs, hkv, d, hq, _ptr(cu_seqlens_q.contiguous()),
+        _ptr(seqused_k.contiguous()), S, int(max_seqlen_q), int(max_seqlen_k), _ptr(block_table),
+        block_table.stride(0), float(softmax_scale), _ptr(rht_signs.contiguous()),
+        int(num_segments), _ptr(segm_output), _ptr(segm_max), _ptr(segm_expsum),
+        _stream(q.device)))
     return out

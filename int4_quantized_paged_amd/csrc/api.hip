@@ -41,6 +41,64 @@ int4kv_status_t check_common(const void* cache, int32_t num_blocks, int32_t bloc
   return INT4KV_OK;
 }
 
+int4kv_status_t check_write_inputs(const void* key, int64_t key_token_stride, const void* value,
+                                   int64_t value_token_stride, const int64_t* slot_mapping,
+                                   int32_t num_kv_heads, int32_t head_size) {
+  if (!key || !value || !slot_mapping)
+    return fail(INT4KV_ERR_INVALID_ARG, "null key, value or slot_mapping pointer");
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_token_stride < row || value_token_stride < row)
+    return fail(INT4KV_ERR_INVALID_ARG, "token strides (%lld, %lld) smaller than heads*head_size %lld",
+                (long long)key_token_stride, (long long)value_token_stride, (long long)row);
+  if ((key_token_stride % 8) || (value_token_stride % 8) || !aligned16(key) || !aligned16(value))
+    return fail(INT4KV_ERR_INVALID_ARG,
+                "key/value must be 16-byte aligned with token strides a multiple of 8 elements");
+  return INT4KV_OK;
+}
+
+// Validates the attention arguments (after check_common) and fills `a`.
+int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out,
+                                int4kv_dtype_t dtype, const uint8_t* kv_cache,
+                                int32_t num_kv_heads, int32_t head_size, int32_t num_q_heads,
+                                const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                const int32_t* block_table, int32_t block_table_stride,
+                                int32_t block_size, float softmax_scale, const float* rht_signs,
+                                int32_t num_segments, float* segm_output, float* segm_max,
+                                float* segm_expsum, int4kv::AttnArgs& a) {
+  if (!q || !out || !cu_seqlens_q || !seqused_k || !block_table)
+    return fail(INT4KV_ERR_INVALID_ARG, "null q, out, cu_seqlens_q, seqused_k or block_table");
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(INT4KV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(INT4KV_ERR_UNSUPPORTED, "query heads per KV head %d: supported 1, 2, 4, 8, 16", G);
+  if (q_token_stride < (int64_t)num_q_heads * head_size || (q_token_stride % 8) || !aligned16(q) ||
+      !aligned16(out))
+    return fail(INT4KV_ERR_INVALID_ARG,
+                "q token stride %lld must be >= heads*head_size and a multiple of 8; q and out "
+                "16-byte aligned", (long long)q_token_stride);
+  if (block_table_stride < (max_seqlen_k + block_size - 1) / block_size)
+    return fail(INT4KV_ERR_INVALID_ARG, "block_table_stride %d < ceil(max_seqlen_k / block_size)",
+                block_table_stride);
+  if (num_segments < 1) return fail(INT4KV_ERR_INVALID_ARG, "num_segments %d < 1", num_segments);
+  if (!std::isfinite(softmax_scale))
+    return fail(INT4KV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const bool decode = max_seqlen_q == 1;
+  if (decode && num_segments > 1 && (!segm_output || !segm_max || !segm_expsum))
+    return fail(INT4KV_ERR_WORKSPACE, "num_segments %d > 1 needs the three segment buffers",
+                num_segments);
+  if (num_segments > 65535) return fail(INT4KV_ERR_INVALID_ARG, "num_segments too large");
+  if (num_seqs > 65535 || num_kv_heads > 65535)
+    return fail(INT4KV_ERR_UNSUPPORTED, "num_seqs and num_kv_heads are limited to 65535");
+  a = int4kv::AttnArgs{q, q_token_stride, out, dtype == INT4KV_BF16, kv_cache, num_kv_heads,
+                       head_size, num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q,
+                       max_seqlen_k, block_table, block_table_stride, softmax_scale, rht_signs,
+                       decode ? num_segments : 1, segm_output, segm_max, segm_expsum};
+  return INT4KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,15 +135,9 @@ int4kv_status_t int4_kv_write(const void* key, int64_t key_token_stride, const v
     return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
   if (num_tokens < 0) return fail(INT4KV_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
   if (num_tokens == 0) return ok();
-  if (!key || !value || !slot_mapping)
-    return fail(INT4KV_ERR_INVALID_ARG, "null key, value or slot_mapping pointer");
-  const int64_t row = (int64_t)num_kv_heads * head_size;
-  if (key_token_stride < row || value_token_stride < row)
-    return fail(INT4KV_ERR_INVALID_ARG, "token strides (%lld, %lld) smaller than heads*head_size %lld",
-                (long long)key_token_stride, (long long)value_token_stride, (long long)row);
-  if ((key_token_stride % 8) || (value_token_stride % 8) || !aligned16(key) || !aligned16(value))
-    return fail(INT4KV_ERR_INVALID_ARG,
-                "key/value must be 16-byte aligned with token strides a multiple of 8 elements");
+  s = check_write_inputs(key, key_token_stride, value, value_token_stride, slot_mapping,
+                         num_kv_heads, head_size);
+  if (s != INT4KV_OK) return s;
   hipError_t e = int4kv::launch_write(key, key_token_stride, value, value_token_stride,
                                       dtype == INT4KV_BF16, slot_mapping, num_tokens, kv_cache,
                                       num_kv_heads, head_size, rht_signs,
@@ -113,41 +165,75 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
   if (num_seqs == 0 || max_seqlen_q == 0) return ok();
-  if (!q || !out || !cu_seqlens_q || !seqused_k || !block_table)
-    return fail(INT4KV_ERR_INVALID_ARG, "null q, out, cu_seqlens_q, seqused_k or block_table");
-  if (num_q_heads < 1 || num_q_heads % num_kv_heads)
-    return fail(INT4KV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
-                num_q_heads, num_kv_heads);
-  const int G = num_q_heads / num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
-    return fail(INT4KV_ERR_UNSUPPORTED, "query heads per KV head %d: supported 1, 2, 4, 8, 16", G);
-  if (q_token_stride < (int64_t)num_q_heads * head_size || (q_token_stride % 8) || !aligned16(q) ||
-      !aligned16(out))
-    return fail(INT4KV_ERR_INVALID_ARG,
-                "q token stride %lld must be >= heads*head_size and a multiple of 8; q and out "
-                "16-byte aligned", (long long)q_token_stride);
-  if (block_table_stride < (max_seqlen_k + block_size - 1) / block_size)
-    return fail(INT4KV_ERR_INVALID_ARG, "block_table_stride %d < ceil(max_seqlen_k / block_size)",
-                block_table_stride);
-  if (num_segments < 1) return fail(INT4KV_ERR_INVALID_ARG, "num_segments %d < 1", num_segments);
-  if (!std::isfinite(softmax_scale))
-    return fail(INT4KV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  int4kv::AttnArgs a;
+  s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
+                      num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
+                      block_table, block_table_stride, block_size, softmax_scale, rht_signs,
+                      num_segments, segm_output, segm_max, segm_expsum, a);
+  if (s != INT4KV_OK) return s;
   const bool decode = max_seqlen_q == 1;
-  if (decode && num_segments > 1 && (!segm_output || !segm_max || !segm_expsum))
-    return fail(INT4KV_ERR_WORKSPACE, "num_segments %d > 1 needs the three segment buffers",
-                num_segments);
-  if (num_segments > 65535) return fail(INT4KV_ERR_INVALID_ARG, "num_segments too large");
-  if (num_seqs > 65535 || num_kv_heads > 65535)
-    return fail(INT4KV_ERR_UNSUPPORTED, "num_seqs and num_kv_heads are limited to 65535");
-
-  int4kv::AttnArgs a{q, q_token_stride, out, dtype == INT4KV_BF16, kv_cache, num_kv_heads,
-                     head_size, num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q,
-                     max_seqlen_k, block_table, block_table_stride, softmax_scale, rht_signs,
-                     decode ? num_segments : 1, segm_output, segm_max, segm_expsum};
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = decode ? int4kv::launch_decode(a, st) : int4kv::launch_prefill(a, st);
   if (e != hipSuccess)
     return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
+                                 const void* value_new, int64_t value_token_stride,
+                                 const int64_t* slot_mapping, const void* q,
+                                 int64_t q_token_stride, void* out, int4kv_dtype_t dtype,
+                                 uint8_t* kv_cache, int32_t num_blocks, int32_t block_size,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t num_q_heads,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 const int32_t* block_table, int32_t block_table_stride,
+                                 float softmax_scale, const float* rht_signs,
+                                 int32_t num_segments, float* segm_output, float* segm_max,
+                                 float* segm_expsum, void* stream) {
+  int4kv_status_t s =
+      check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
+  if (s != INT4KV_OK) return s;
+  if (dtype != INT4KV_F16 && dtype != INT4KV_BF16)
+    return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
+  if (num_seqs == 0) return ok();
+  s = check_write_inputs(key_new, key_token_stride, value_new, value_token_stride, slot_mapping,
+                         num_kv_heads, head_size);
+  if (s != INT4KV_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == INT4KV_BF16;
+  if (max_seqlen_q == 0) {  // nothing to attend: the write alone
+    hipError_t e = int4kv::launch_write(key_new, key_token_stride, value_new, value_token_stride,
+                                        bf16, slot_mapping, num_seqs, kv_cache, num_kv_heads,
+                                        head_size, rht_signs, st);
+    if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "write launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  int4kv::AttnArgs a;
+  s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
+                      num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
+                      block_table, block_table_stride, block_size, softmax_scale, rht_signs,
+                      num_segments, segm_output, segm_max, segm_expsum, a);
+  if (s != INT4KV_OK) return s;
+  hipError_t e;
+  if (max_seqlen_q == 1 && int4kv::decode_lds_supported(a)) {
+    a.key_new = key_new;
+    a.key_new_stride = key_token_stride;
+    a.value_new = value_new;
+    a.value_new_stride = value_token_stride;
+    a.slot_new = slot_mapping;
+    e = int4kv::launch_decode_lds(a, st);
+  } else {  // the same result as two calls: the write, then the attention
+    e = int4kv::launch_write(key_new, key_token_stride, value_new, value_token_stride, bf16,
+                             slot_mapping, num_seqs, kv_cache, num_kv_heads, head_size,
+                             rht_signs, st);
+    if (e == hipSuccess)
+      e = max_seqlen_q == 1 ? int4kv::launch_decode(a, st) : int4kv::launch_prefill(a, st);
+  }
+  if (e != hipSuccess)
+    return fail(INT4KV_ERR_LAUNCH, "decode step launch: %s", hipGetErrorString(e));
   return ok();
 }
 

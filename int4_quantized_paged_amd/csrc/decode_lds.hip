@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "encode_row.h"
 #include "launch.h"
 
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -142,7 +143,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
     const float* __restrict__ signs, int32_t num_segments, float* __restrict__ segm_out,
-    float* __restrict__ segm_max, float* __restrict__ segm_sum) {
+    float* __restrict__ segm_max, float* __restrict__ segm_sum,
+    const uint16_t* __restrict__ key_new, int64_t key_new_stride,
+    const uint16_t* __restrict__ value_new, int64_t value_new_stride,
+    const int64_t* __restrict__ slot_new) {
   using GG = Geo<D, HPW>;
   using WG = WGeo<G>;
   constexpr uint32_t R = GG::R;
@@ -168,13 +172,61 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 
   const int q0 = cu_seqlens_q[b];
   const int qlen = cu_seqlens_q[b + 1] - q0;
-  if (qlen <= 0) return;  // uniform over the workgroup
   const int L = seqused_k[b];
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
   const int per = (nblk + num_segments - 1) / num_segments;
   const int b0 = seg * per;
   const int b1 = min(b0 + per, nblk);
   const int ntile = b1 > b0 ? (b1 - b0 + 1) / 2 : 0;
+
+  // ---- fused decode step: the new token of sequence b (its last key, at
+  // position L - 1) is encoded exactly as the cache write does and stored by
+  // the workgroup whose segment holds that key's block, before any copy of
+  // the block is issued.  The writing waves' stores complete (vmcnt 0) before
+  // a barrier that precedes that copy: the barrier right here when the
+  // block's tile is among the first S - 1 (copied before the loop), else the
+  // barrier at which tile 0 has landed.  The block is read only by this
+  // workgroup, through L2.
+  bool store_pending = false;  // this wave stored rows whose completion is still to be awaited
+  if (slot_new != nullptr) {
+    const int64_t slot = slot_new[b];
+    if (slot >= 0 && L > 0 && (L - 1) / kBlockSize / per == seg) {  // uniform over the workgroup
+      constexpr int WE = 16, WLPR = D / WE, WRPW = kWave / WLPR;  // rows of 8 or 4 lanes
+      if (wave * WRPW < 2 * HPW) {
+        const int r = wave * WRPW + lane / WLPR;  // row kv * HPW + head of the group
+        const int rr = min(r, 2 * HPW - 1);      // spare lanes encode a valid row, store nothing
+        const int sub = lane % WLPR, kv = rr / HPW, hd = h0 + rr % HPW;
+        const uint16_t* src = (kv == 0 ? key_new + (int64_t)b * key_new_stride
+                                       : value_new + (int64_t)b * value_new_stride) +
+                              (int64_t)hd * D + WE * sub;
+        u32x4_t in[WE / 8];
+#pragma unroll
+        for (int k = 0; k < WE / 8; ++k) in[k] = reinterpret_cast<const u32x4_t*>(src)[k];
+        uint32_t flip[WE / 2];
+        row_flips<WE>(signs, sub, flip);
+        float x[WE];
+        row_inputs<BF16, WE>(in, flip, x);
+        uint32_t packed[WE / 8];
+        const uint32_t word = encode_piece<WE, WLPR>(x, sub, packed);
+        if (r < 2 * HPW) {
+          const int64_t blk = slot / kBlockSize, off = slot % kBlockSize;
+          uint8_t* dst = const_cast<uint8_t*>(cache) +
+                         (((blk * 2 + kv) * kBlockSize + off) * num_kv_heads + hd) * R;
+          uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + (WE / 2) * sub);
+#pragma unroll
+          for (int k = 0; k < WE / 8; ++k) d32[k] = packed[k];
+          if (sub == 0) reinterpret_cast<uint32_t*>(dst)[D / 8] = word;
+        }
+      }
+      if (ntile <= S - 1) {
+        wait_vmem<0>();  // the stores have reached L2
+        __syncthreads();
+      } else {
+        store_pending = wave * WRPW < 2 * HPW;
+      }
+    }
+  }
+  if (qlen <= 0) return;  // uniform over the workgroup
 
   const uint32_t tok_g = (uint32_t)num_kv_heads * R;  // global token stride
   const uint32_t half_g = 16 * tok_g;
@@ -610,6 +662,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   TileWords wA, wB;
   if (ntile > 0) {
     wait_tiles(std::integral_constant<int, S - 2>());  // tile 0
+    if (store_pending) wait_vmem<0>();  // this wave's stores of the new token, too
     __syncthreads();
     i32x4_t kb[2][NCK];
     k_operands(smem, kb);
@@ -709,7 +762,10 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(kern, grid, block, lds, stream, reinterpret_cast<const uint16_t*>(a.q),
                      a.q_stride, reinterpret_cast<uint16_t*>(a.out), a.cache, a.num_kv_heads,
                      a.num_q_heads, a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride,
-                     scale_log2, a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum);
+                     scale_log2, a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum,
+                     reinterpret_cast<const uint16_t*>(a.key_new), a.key_new_stride,
+                     reinterpret_cast<const uint16_t*>(a.value_new), a.value_new_stride,
+                     a.slot_new);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_segments == 1) return e;
   return launch_reduce(a, stream);

@@ -1,0 +1,132 @@
+// Encoding of one (token, K|V, head) row into its packed INT4 form, shared by
+// the cache write and the fused decode step so both store the same bytes.
+//
+// PR #40633's description and the PR #40835 report (implementation breakdown,
+// item 2): random Hadamard rotation, asymmetric 16-level codes, one fp32 scale
+// per row with the zero point in its low 4 mantissa bits; the quantizer is the
+// test file's section 6 INT4 reference.  A row of D elements is held by
+// LPR = D / E lanes (adjacent lanes, piece `sub` = lane % LPR) with E
+// consecutive elements each.  Every fp32 operation is one correctly rounded op
+// in a fixed order (spans 1, 2, 4, ..., D/2; contraction is switched off
+// here), so the bytes are reproducible bit for bit:
+//   * the signs are applied as bit flips of the 16-bit inputs (exact),
+//   * clamp-then-round equals round-then-clamp for the integer bounds 0 and
+//     15, and rounding to nearest-even is an fp32 add of 2^23, after which
+//     the code sits in the low 4 bits of the sum.
+#pragma once
+
+#include "device_common.h"
+
+namespace int4kv {
+
+__device__ __forceinline__ float enc_med3(float x, float lo, float hi) {
+  return __builtin_amdgcn_fmed3f(x, lo, hi);
+}
+
+// element i of a 16-bit pair dword (i = 0: low half)
+template <bool BF16>
+__device__ __forceinline__ float half_of(uint32_t w, int i) {
+  if constexpr (BF16) {
+    return as_float(i == 0 ? (w << 16) : (w & 0xFFFF0000u));
+  } else {
+    const half2_t hh = __builtin_bit_cast(half2_t, w);
+    return (float)hh[i];
+  }
+}
+
+// sign bits of elements [E * sub, E * sub + E) as flips of 16-bit pairs
+template <int E>
+__device__ __forceinline__ void row_flips(const float* __restrict__ signs, int sub,
+                                          uint32_t (&flip)[E / 2]) {
+#pragma unroll
+  for (int p = 0; p < E / 2; ++p) {
+    const float s0 = signs[E * sub + 2 * p], s1 = signs[E * sub + 2 * p + 1];
+    flip[p] = (s0 < 0.f ? 0x8000u : 0u) | (s1 < 0.f ? 0x80000000u : 0u);
+  }
+}
+
+// the lane's E inputs (E / 8 vectors of 8 16-bit values) times the signs, in fp32
+template <bool BF16, int E>
+__device__ __forceinline__ void row_inputs(const u32x4_t (&a)[E / 8], const uint32_t (&flip)[E / 2],
+                                           float (&x)[E]) {
+#pragma unroll
+  for (int k = 0; k < E / 8; ++k) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = a[k][j] ^ flip[4 * k + j];  // x * sign, exactly
+      x[8 * k + 2 * j] = half_of<BF16>(w, 0);
+      x[8 * k + 2 * j + 1] = half_of<BF16>(w, 1);
+    }
+  }
+}
+
+// Rotation, range, scale, zero point and codes of one row: the lane's E / 8
+// packed code dwords (bytes j = code_{2j} | code_{2j+1} << 4) and the row's
+// scale word bits(s_t) | zp.
+template <int E, int LPR>
+__device__ __forceinline__ uint32_t encode_piece(float (&x)[E], int sub,
+                                                 uint32_t (&packed)[E / 8]) {
+#pragma clang fp contract(off)
+  // butterflies inside the lane: spans 1 .. E/2
+#pragma unroll
+  for (int span = 1; span < E; span <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (e & span) continue;
+      const float u = x[e], v = x[e + span];
+      x[e] = __fadd_rn(u, v);
+      x[e + span] = __fsub_rn(u, v);
+    }
+  }
+  // spans E, 2E, ... across the lanes of a row: the lower partner keeps
+  // u + v, the upper one u - v, written as partner + (-self)
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+    const uint32_t xflip = (sub & m) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float p = shfl_xor_rt(x[e], m);
+      x[e] = __fadd_rn(p, as_float(as_uint(x[e]) ^ xflip));
+    }
+  }
+
+  // row range
+  float mn = fminf(x[0], x[1]), mx = fmaxf(x[0], x[1]);
+#pragma unroll
+  for (int e = 2; e < E; e += 2) {
+    mn = __builtin_fminf(mn, __builtin_fminf(x[e], x[e + 1]));
+    mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[e], x[e + 1]));
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+    mn = fminf(mn, shfl_xor_rt(mn, m));
+    mx = fmaxf(mx, shfl_xor_rt(mx, m));
+  }
+  float sc = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+  if (!(sc > 1e-6f)) sc = 1e-6f;
+  const float s_t = as_float(as_uint(sc) & 0xFFFFFFF0u);
+  const float inv = __fdiv_rn(1.0f, s_t);
+  const float zpf = fminf(fmaxf(rintf(__fmul_rn(-mn, inv)), 0.0f), 15.0f);
+
+  // codes: clamp to [0, 15], then round to nearest even by adding 2^23; the
+  // code is then the low 4 bits of the sum's bit pattern
+#pragma unroll
+  for (int q = 0; q < E / 8; ++q) {
+    uint32_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 8 * q + 2 * j;
+      const float c0 = __fadd_rn(enc_med3(__fadd_rn(__fmul_rn(x[e], inv), zpf), 0.0f, 15.0f),
+                                 8388608.0f);
+      const float c1 = __fadd_rn(enc_med3(__fadd_rn(__fmul_rn(x[e + 1], inv), zpf), 0.0f, 15.0f),
+                                 8388608.0f);
+      b[j] = (as_uint(c1) << 4) | as_uint(c0);  // byte 0 = code_lo | code_hi << 4
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // [b0.0 b1.0 0 0]
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+    packed[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);            // [lo.0 lo.1 hi.0 hi.1]
+  }
+  return as_uint(s_t) | (uint32_t)zpf;
+}
+
+}  // namespace int4kv

@@ -29,6 +29,14 @@ struct AttnArgs {
   float* segm_out;
   float* segm_max;
   float* segm_sum;
+  // fused decode step only: the new token of each sequence (token b belongs to
+  // sequence b and is its last key), encoded into the cache by the workgroup
+  // that reads its block; null otherwise
+  const void* key_new = nullptr;
+  int64_t key_new_stride = 0;
+  const void* value_new = nullptr;
+  int64_t value_new_stride = 0;
+  const int64_t* slot_new = nullptr;
 };
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);

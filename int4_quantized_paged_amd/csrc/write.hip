@@ -15,34 +15,14 @@
 // per row: a chain four times shorter per row, four times as many waves).
 // The Walsh-Hadamard butterflies of span 1..E/2 run inside a lane and the
 // spans E, 2E, ... pair the lanes of a row through DPP, which keeps the spans
-// in the increasing order the encoding fixes.  Every fp32 operation is a single correctly rounded op in that order,
-// so the packed bytes are reproducible bit for bit (this file is built without
-// FMA contraction):
-//   * the signs are applied as bit flips of the 16-bit inputs (exact),
-//   * clamp-then-round equals round-then-clamp for the integer bounds 0 and 15,
-//     and the rounding to nearest-even is an fp32 add of 2^23, after which the
-//     code sits in the low 4 bits of the sum.
+// in the increasing order the encoding fixes (encode_row.h).
 #include "device_common.h"
+#include "encode_row.h"
 #include "launch.h"
 
 namespace int4kv {
 
 namespace {
-
-__device__ __forceinline__ float med3(float x, float lo, float hi) {
-  return __builtin_amdgcn_fmed3f(x, lo, hi);
-}
-
-// element i of a 16-bit pair dword (i = 0: low half)
-template <bool BF16>
-__device__ __forceinline__ float half_of(uint32_t w, int i) {
-  if constexpr (BF16) {
-    return as_float(i == 0 ? (w << 16) : (w & 0xFFFF0000u));
-  } else {
-    const half2_t h = __builtin_bit_cast(half2_t, w);
-    return (float)h[i];
-  }
-}
 
 // rows at and above which writes take 64 elements per lane
 constexpr int64_t kBulkRows = 65536;
@@ -68,11 +48,7 @@ __global__ __launch_bounds__(256) void write_kernel(
 
   // sign bits of the lane's E elements, as flips of 16-bit pairs
   uint32_t flip[E / 2];
-#pragma unroll
-  for (int p = 0; p < E / 2; ++p) {
-    const float s0 = signs[E * sub + 2 * p], s1 = signs[E * sub + 2 * p + 1];
-    flip[p] = (s0 < 0.f ? 0x8000u : 0u) | (s1 < 0.f ? 0x80000000u : 0u);
-  }
+  row_flips<E>(signs, sub, flip);
 
   // row coordinates and the raw 16-bit inputs of one row (software-pipelined:
   // the next row's loads are in flight while the current row is encoded)
@@ -108,76 +84,9 @@ __global__ __launch_bounds__(256) void write_kernel(
     const int h = cur.h, kv = cur.kv;
     const bool in_range = cur.ok;
     float x[E];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = cur.a[k][j] ^ flip[4 * k + j];  // x * sign, exactly
-        x[8 * k + 2 * j] = half_of<BF16>(w, 0);
-        x[8 * k + 2 * j + 1] = half_of<BF16>(w, 1);
-      }
-    }
-
-    // butterflies inside the lane: spans 1 .. E/2
-#pragma unroll
-    for (int span = 1; span < E; span <<= 1) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (e & span) continue;
-        const float u = x[e], v = x[e + span];
-        x[e] = __fadd_rn(u, v);
-        x[e + span] = __fsub_rn(u, v);
-      }
-    }
-    // spans E, 2E, ... across the lanes of a row: the lower partner keeps
-    // u + v, the upper one u - v, written as partner + (-self)
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      const uint32_t xflip = (sub & m) ? 0x80000000u : 0u;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float p = shfl_xor_rt(x[e], m);
-        x[e] = __fadd_rn(p, as_float(as_uint(x[e]) ^ xflip));
-      }
-    }
-
-    // row range
-    float mn = fminf(x[0], x[1]), mx = fmaxf(x[0], x[1]);
-#pragma unroll
-    for (int e = 2; e < E; e += 2) {
-      mn = __builtin_fminf(mn, __builtin_fminf(x[e], x[e + 1]));
-      mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[e], x[e + 1]));
-    }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      mn = fminf(mn, shfl_xor_rt(mn, m));
-      mx = fmaxf(mx, shfl_xor_rt(mx, m));
-    }
-    float sc = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
-    if (!(sc > 1e-6f)) sc = 1e-6f;
-    const float s_t = as_float(as_uint(sc) & 0xFFFFFFF0u);
-    const float inv = __fdiv_rn(1.0f, s_t);
-    const float zpf = fminf(fmaxf(rintf(__fmul_rn(-mn, inv)), 0.0f), 15.0f);
-
-    // codes: clamp to [0, 15], then round to nearest even by adding 2^23; the
-    // code is then the low 4 bits of the sum's bit pattern
+    row_inputs<BF16, E>(cur.a, flip, x);
     uint32_t packed[NP];
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-      uint32_t b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 8 * q + 2 * j;
-        const float c0 = __fadd_rn(med3(__fadd_rn(__fmul_rn(x[e], inv), zpf), 0.0f, 15.0f),
-                                   8388608.0f);
-        const float c1 = __fadd_rn(med3(__fadd_rn(__fmul_rn(x[e + 1], inv), zpf), 0.0f, 15.0f),
-                                   8388608.0f);
-        b[j] = (as_uint(c1) << 4) | as_uint(c0);  // byte 0 = code_lo | code_hi << 4
-      }
-      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // [b0.0 b1.0 0 0]
-      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
-      packed[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);            // [lo.0 lo.1 hi.0 hi.1]
-    }
+    const uint32_t word = encode_piece<E, LPR>(x, sub, packed);
 
     const int64_t slot = slot_mapping[t];
     if (in_range && slot >= 0) {
@@ -192,7 +101,7 @@ __global__ __launch_bounds__(256) void write_kernel(
 #pragma unroll
         for (int q = 0; q < NP; ++q) d32[q] = packed[q];
       }
-      if (sub == 0) reinterpret_cast<uint32_t*>(dst)[D / 8] = as_uint(s_t) | (uint32_t)zpf;
+      if (sub == 0) reinterpret_cast<uint32_t*>(dst)[D / 8] = word;
     }
     cur = nxt;
   }
