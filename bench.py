@@ -64,7 +64,7 @@ def _traffic_from_profiles(kernel_hash: str):
 def _kernel_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode_lds.hip", "decode.hip", "device_common.h", "launch.h"):
+    for f in ("decode_lds.hip", "decode.hip", "device_common.h", "launch.h", "encode_row.h"):
         with open(os.path.join(HERE, "int4_quantized_paged_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
