@@ -172,15 +172,18 @@ def measure_bulk_write(b, reps: int = 5):
     return T / t, t, T
 
 
-def _median_event_us(fn, reps):
+def _median_event_us(fn, reps, rounds=5):
+    """Per-call time of `reps` back-to-back calls between two HIP events on the
+    launch stream (as the headline attention figure), median of `rounds`."""
     ts = []
-    for _ in range(reps):
+    for _ in range(rounds):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        fn()
+        for _ in range(reps):
+            fn()
         e1.record()
         e1.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
     ts.sort()
     return ts[len(ts) // 2]
 
@@ -211,7 +214,7 @@ def other_rows(dev):
     """The other timed rows of the path, each at its full size: prefill on the
     chunked-prefill mix (MFMA-bound; TFLOP/s against the dense f16 peak) and
     decode on the Llama-3-8B-shaped batch (HBM-bound; two cache copies
-    alternate).  Median of hipEvent-timed calls."""
+    alternate).  Back-to-back calls between HIP events, median of five rounds."""
     rows = {}
     for d in (128, 64):
         w = wl.chunked_prefill(device=dev, head_size=d)
