@@ -50,9 +50,10 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 // 16 bytes per lane from global memory (uniform base + 32-bit lane offset)
-// straight into LDS at M0 + lane * 16.
+// straight into LDS at M0 + lane * 16.  Marked non-temporal: every cache line
+// is read once, so it should not displace lines that are reused.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
