@@ -244,7 +244,10 @@ def other_rows(dev):
     kv = w.kv_bytes_attended()
     rows["llama3_8b_decode"] = {
         "workload": "64 seqs x 4096 tokens, 32 q / 8 KV heads, d 128 (outlier K channels)",
-        "num_segments": best[0], "us": round(best[1], 2),
+        "num_segments": best[0],
+        "num_segments_library_choice": ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads,
+                                                                     w.max_seqlen_k),
+        "us": round(best[1], 2),
         "GBps": round(kv / best[1] / 1e3, 1), "hbm_frac": round(kv / best[1] / 1e3 / HBM_PEAK_GBS, 4)}
     return rows
 
@@ -369,6 +372,8 @@ def main():
                    "global_batch": 4, "seq_len": 131072, "parallelism": "none (1 GPU)",
                    "launch": "hip graph replay" if args.graph else "plain calls"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "num_segments_library_choice": ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads,
+                                                                     w.max_seqlen_k),
         "write_tokens_per_s": round(wr_tps, 1),
         "write_bulk": {"tokens": wr_T, "seconds": wr_t,
                        "GB_per_s": round(w.write_bytes("all") / wr_t / 1e9, 1)},

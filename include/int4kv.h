@@ -178,6 +178,18 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
                                  int32_t num_segments, float* segm_output, float* segm_max,
                                  float* segm_expsum, void* stream);
 
+/*
+ * int4kv_decode_num_segments: the split-K segment count the library's decode
+ * kernels run best with for a decode batch (max_seqlen_q == 1) of `num_seqs`
+ * sequences whose longest has `max_seqlen_k` keys: enough segments for one
+ * workgroup per CU of MI355X, none shorter than 512 keys.  Host only; never
+ * fails (returns >= 1).  The caller sizes the segment buffers of
+ * int4_paged_attention / int4_decode_step with it and passes it as
+ * num_segments.  (The pages' attention test sizes its segment buffers from a
+ * segment count chosen by the caller: [testfile] §6.)
+ */
+int32_t int4kv_decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seqlen_k);
+
 /* Human-readable name of a status code (static storage). */
 const char* int4kv_status_string(int4kv_status_t s);
 

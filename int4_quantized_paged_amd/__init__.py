@@ -19,7 +19,8 @@ import os
 import torch
 
 __all__ = [
-    "int4_kv_write", "int4_paged_attention", "int4_decode_step", "int4kv_cache_bytes", "int4kv_status_string",
+    "int4_kv_write", "int4_paged_attention", "int4_decode_step", "int4kv_decode_num_segments",
+    "int4kv_cache_bytes", "int4kv_status_string",
     "int4kv_last_error", "Int4KVError", "cache_shape", "empty_cache", "segment_buffers",
     "library_path", "load_library",
 ]
@@ -68,6 +69,8 @@ def load_library():
                                      i32, i32, P, P, i32, i32, i32, P, i32, ctypes.c_float, P,
                                      i32, P, P, P, P]
     lib.int4_decode_step.restype = ctypes.c_int
+    lib.int4kv_decode_num_segments.argtypes = [i32, i32, i32]
+    lib.int4kv_decode_num_segments.restype = i32
     _lib = lib
     return lib
 
@@ -103,6 +106,11 @@ def int4kv_status_string(status: int) -> str:
 
 def int4kv_last_error() -> str:
     return load_library().int4kv_last_error().decode()
+
+
+def int4kv_decode_num_segments(num_seqs: int, num_kv_heads: int, max_seqlen_k: int) -> int:
+    """The library's split-K segment count for a decode batch (host only)."""
+    return int(load_library().int4kv_decode_num_segments(num_seqs, num_kv_heads, max_seqlen_k))
 
 
 def cache_shape(num_blocks: int, num_kv_heads: int, head_size: int, block_size: int = 16):

@@ -110,3 +110,53 @@ def test_attention_rejects_invalid_host_arguments(kw, status):
 def test_attention_empty_batch_is_a_no_op():
     assert _attn(S=0) == 0
     assert _attn(mq=0) == 0
+
+
+def _step(**kw):
+    a = dict(kn=FAKE, ks=1024, vn=FAKE, vs=1024, slots=FAKE, q=FAKE, qs=4096, out=FAKE, dtype=1,
+             cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32, cu=FAKE, su=FAKE, S=4, mq=1, mk=1024,
+             bt=FAKE, bts=64, scale=0.088, signs=FAKE, ns=1, so=None, sm=None, ss=None,
+             stream=None)
+    a.update(kw)
+    lib = ik.load_library()
+    return lib.int4_decode_step(a["kn"], a["ks"], a["vn"], a["vs"], a["slots"], a["q"], a["qs"],
+                                a["out"], a["dtype"], a["cache"], a["nb"], a["bs"], a["hkv"],
+                                a["d"], a["hq"], a["cu"], a["su"], a["S"], a["mq"], a["mk"],
+                                a["bt"], a["bts"], a["scale"], a["signs"], a["ns"], a["so"],
+                                a["sm"], a["ss"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), 1), (dict(slots=None), 1), (dict(ks=100), 1), (dict(vn=FAKE + 2), 1),
+    (dict(hq=30), 1), (dict(d=80), 2), (dict(ns=16), 3), (dict(cache=None), 1),
+    (dict(dtype=5), 1), (dict(bts=10), 1), (dict(S=-1), 1),
+])
+def test_decode_step_rejects_invalid_host_arguments(kw, status):
+    """The fused step validates both halves' arguments before enqueuing."""
+    assert _step(**kw) == status
+    assert ik.int4kv_last_error() != ""
+
+
+def test_decode_step_empty_batch_is_a_no_op():
+    assert _step(S=0) == 0
+
+
+@pytest.mark.parametrize("S,hkv,L,ns", [
+    (4, 8, 131072, 64),  # long-context decode: one workgroup per CU
+    (64, 8, 4096, 4),    # Llama-3-8B-shaped decode: 256 workgroups
+    (1, 8, 100, 1),      # shorter than one minimum segment
+    (8, 8, 1024, 2),     # capped by the 16-tile minimum segment
+    (32, 3, 5000, 3),    # register-path head count (one head per workgroup)
+    (2, 16, 65536, 64),  # two workgroups per segment index
+    (1, 1, 10 ** 7, 256),
+])
+def test_decode_num_segments_heuristic(S, hkv, L, ns):
+    """Enough segments for one workgroup per CU, none shorter than 16 tiles of
+    32 keys, at most 256; the two benchmark shapes get the split counts that
+    measured fastest (64 and 4)."""
+    assert ik.int4kv_decode_num_segments(S, hkv, L) == ns
+
+
+def test_decode_num_segments_degenerate_inputs():
+    for args in ((0, 8, 100), (4, 0, 100), (4, 8, 0), (-1, 8, 100)):
+        assert ik.int4kv_decode_num_segments(*args) == 1
