@@ -232,6 +232,38 @@ def other_rows(dev):
             "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
         del w, call
     w = wl.llama3_8b_decode(device=dev)
+    # its bulk cache fill (262144 tokens) and a decode step's write (64 tokens)
+    cache = ik.empty_cache(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)
+    _, slots_all = w.token_set("all")
+    slots_all = slots_all.to(dev)
+    signs = w.signs.to(dev)
+    fill = lambda: ik.int4_kv_write(w.key, w.value, slots_all, cache, signs)  # noqa: E731
+    for _ in range(2):
+        fill()
+    fill_us = _median_event_us(fill, 3)
+    idx_new, slots_new = w.token_set("new")
+    kn, vn = w.key[idx_new.to(dev)].contiguous(), w.value[idx_new.to(dev)].contiguous()
+    slots_new = slots_new.to(dev)
+    step_write = lambda: ik.int4_kv_write(kn, vn, slots_new, cache, signs)  # noqa: E731
+    for _ in range(3):
+        step_write()
+    # 20 writes in one HIP graph: a launch this small is otherwise timed at the
+    # host's call rate, not the GPU's
+    g20 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g20):
+        for _ in range(20):
+            step_write()
+    g20.replay()
+    step_write_us = _median_event_us(g20.replay, 3) / 20
+    T = w.key.shape[0]
+    rows["llama3_8b_write"] = {
+        "workload": "bulk fill of 262144 tokens (64 x 4096, 8 KV heads, d 128, bf16) and one "
+                    "decode step's write of 64 tokens",
+        "bulk_us": round(fill_us, 1), "bulk_tokens_per_s": round(T / fill_us * 1e6, 1),
+        "bulk_GBps": round(w.write_bytes("all") / fill_us / 1e3, 1),
+        "step_64_tokens_us": round(step_write_us, 2),
+        "step_64_tokens_timing": "20 writes replayed from one HIP graph, per write"}
+    del cache, fill, step_write, g20
     best = None
     for ns in (1, 2, 4, 8):
         call = _attention_setup(w, dev, ns, ncaches=2)
