@@ -8,10 +8,11 @@
 //    and V halves of a cache block it reads are 16-byte-aligned runs
 //    (16 tokens x HPW x R bytes).  Each 2-block tile is copied HBM -> LDS with
 //    global_load_lds_dwordx4 by all waves together (every 128-byte line is
-//    fetched once) into a ring of 3 to 6 stages (as deep as the 160 KiB of LDS
-//    allows), all but one stage ahead of the math.  The copies
-//    are issued from inline assembly and waited for with explicit vmcnt so the
-//    compiler does not drain the ring at every barrier.  When a token's run is
+//    fetched once, non-temporal) into a ring of 3 to 6 stages (as deep as the
+//    160 KiB of LDS allows), all but one stage ahead of the math; with 4 or
+//    more stages the workgroup meets at a barrier every other step.  The
+//    copies are issued from inline assembly and waited for with explicit
+//    vmcnt so the compiler does not drain the ring at every barrier.  When a token's run is
 //    a whole number of 16-byte chunks, token rows are re-laid out in LDS with a
 //    stride of 12 dwords mod 32 so the per-lane row reads spread over the banks.
 //  * Q . K^T runs on the int8 MFMA (v_mfma_i32_16x16x64_i8): K codes become
@@ -22,15 +23,22 @@
 //    fp32.
 //  * P . V runs on the f16 MFMA with the softmax weights W = p * s_V split into
 //    f16 hi + lo (22 significant bits; f16 alone leaves an error of 2^-11 of
-//    |V| in the output).  V codes enter as raw bit patterns: (w & 0x000F000F) is a pair of f16
-//    subnormals code * 2^-24, (w & 0x00F000F0) is 16 * code * 2^-24; products
-//    and sums stay exact in fp32 and the 2^24 (2^20) is applied per output
-//    column at the end.
+//    |V| in the output).  V enters as raw bit patterns: a byte of two slot
+//    keys' dwords, zero-extended into f16 halves, is the subnormal pair
+//    (low + 16 high) * 2^-24, and masked to 0x000F000F the low nibbles alone;
+//    per byte one column tile takes the whole bytes and one the low nibbles,
+//    the high nibble's column is their difference / 16.  Products and sums
+//    stay exact in fp32; the 2^24 (2^20) is applied per output column at the
+//    end.
 //  * The next tile's scores are computed on the matrix cores while the
 //    current tile's softmax runs; the softmax reference maximum moves only
 //    when a logit exceeds it by 4 (base-2 units, a factor 16 in probability),
 //    checked per logit, so row maxima are reduced and accumulators rescaled
 //    only on the rare tiles that need it.
+//  * Fused decode step: given one new token per sequence, the workgroup whose
+//    segment holds the sequence's last block encodes and stores that token's
+//    rows (the cache write's own encoding, encode_row.h) before its copy of
+//    the block, so the write needs no launch of its own.
 #include <type_traits>
 
 #include "device_common.h"

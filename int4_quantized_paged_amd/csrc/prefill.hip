@@ -14,15 +14,18 @@
 //  * The K and V rows of the head (R bytes at the cache's token stride) are
 //    copied HBM -> LDS with global_load_lds_dword into an 8-stage ring, six
 //    tiles ahead of the math; wave q of a group copies (block q/2, K|V q%2)
-//    of each of the group's two-block tiles.  Rows land as 17-dword (d = 128) or 9-dword (d = 64)
-//    records, an odd stride, so the per-key reads of 16 lanes hit 16 banks.
-//  * Codes enter the f16 MFMAs as raw bit patterns: (w & 0x000F000F) is a pair
-//    of f16 subnormals code * 2^-24, (w & 0x00F000F0) is 16 * code * 2^-24;
-//    products and sums stay exact in fp32 and the 2^24 (and the 16) are folded
-//    into per-row and per-column constants.  No bias, no subtraction.
+//    of each of the group's two-block tiles.  Rows land as 17-dword (d =
+//    128) or 9-dword (d = 64) records, an odd stride, so the per-key reads of
+//    16 lanes hit 16 banks.
+//  * Codes enter the f16 MFMAs as raw bit patterns: K as (w & 0x000F000F), a
+//    pair of f16 subnormals code * 2^-24, and (w & 0x00F000F0), 16 * code *
+//    2^-24; V as whole bytes zero-extended into halves, (low + 16 high) *
+//    2^-24, and their low nibbles, the high nibble's column taken as the
+//    difference / 16.  Products and sums stay exact in fp32 and the 2^24 (and
+//    the 16) are folded into per-row and per-column constants.
 //  * Q . K^T: Q' as f16 hi + lo (22 significant bits), both against the same
 //    K operand.  P . V: softmax weights times the V scale, also as f16 hi +
-//    lo, as the A operand through a per-wave LDS tile, against V codes
+//    lo, as the A operand through a per-wave LDS tile, against V bytes
 //    expanded per lane from one dword of each of 8 keys.
 //  * Workgroups are numbered so that the KV heads of one (sequence, tile) run
 //    on the same XCD (the heads of a token share 128-byte lines in L2), and
