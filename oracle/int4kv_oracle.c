@@ -40,7 +40,14 @@
  *           at position seqused_k - q_len + i and sees keys [0, pos].
  *   R-gqa   query head g reads KV head g / (Hq / Hkv).
  *   R-seg   split-K segment k of a sequence with nb blocks covers blocks
- *           [k*c, min((k+1)*c, nb)), c = ceil(nb / NS).
+ *           [k*c, min((k+1)*c, nb)), c = ceil(nb / NS); with a window, the
+ *           segments split the blocks from the first one any query row of
+ *           the sequence can see, b_lo, in the same way: [b_lo + k*c, ...),
+ *           c = ceil((nb - b_lo) / NS).
+ *   R-win   sliding window W > 0: the query at position pos sees keys
+ *           [max(0, pos - W + 1), pos], W keys counting its own; W <= 0 is no
+ *           window.  ([pr40633] description: the packed read path shares the
+ *           common kernel's sliding-window masking helper.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -269,7 +276,7 @@ void oracle_attention_plain(const uint16_t* q, int64_t q_stride, int dtype,
                             int num_kv_heads, int d, int num_q_heads,
                             const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                             int num_seqs, const int32_t* block_table, int bt_stride,
-                            double softmax_scale, const float* signs, double* out) {
+                            double softmax_scale, const float* signs, int window, double* out) {
   (void)num_blocks;
   int G = num_q_heads / num_kv_heads;
   for (int b = 0; b < num_seqs; ++b) {
@@ -297,19 +304,21 @@ void oracle_attention_plain(const uint16_t* q, int64_t q_stride, int dtype,
           double* o = out + ((int64_t)(q0 + i) * num_q_heads + g) * d;
           for (int k = 0; k < d; ++k) o[k] = 0.0;
           if (pos < 0) continue;
+          int64_t jlo = 0; /* R-win */
+          if (window > 0 && pos - window + 1 > 0) jlo = pos - window + 1;
           double zmax = -INFINITY;
-          for (int64_t j = 0; j <= pos; ++j) {
+          for (int64_t j = jlo; j <= pos; ++j) {
             double acc = 0.0;
             for (int k = 0; k < d; ++k) acc += qv[k] * K[j * d + k];
             z[j] = softmax_scale * acc;
             if (z[j] > zmax) zmax = z[j];
           }
           double den = 0.0;
-          for (int64_t j = 0; j <= pos; ++j) {
+          for (int64_t j = jlo; j <= pos; ++j) {
             z[j] = exp(z[j] - zmax);
             den += z[j];
           }
-          for (int64_t j = 0; j <= pos; ++j) {
+          for (int64_t j = jlo; j <= pos; ++j) {
             double w = z[j] / den;
             for (int k = 0; k < d; ++k) o[k] += w * V[j * d + k];
           }
@@ -338,7 +347,7 @@ void oracle_attention_method(const uint16_t* q, int64_t q_stride, int dtype,
                              const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                              int num_seqs, const int32_t* block_table, int bt_stride,
                              double softmax_scale, const float* signs, int num_segments,
-                             double* out) {
+                             int window, double* out) {
   (void)num_blocks;
   int G = num_q_heads / num_kv_heads;
   if (num_segments < 1) num_segments = 1;
@@ -352,9 +361,13 @@ void oracle_attention_method(const uint16_t* q, int64_t q_stride, int dtype,
     int64_t L = seqused_k[b];
     if (qlen <= 0 || L <= 0) continue;
     int64_t nblk = (L + block_size - 1) / block_size;
-    int64_t per = (nblk + num_segments - 1) / num_segments; /* R-seg */
+    int64_t blo = 0; /* first block any row of the sequence sees (R-win, R-seg) */
+    if (window > 0 && L - qlen - window + 1 > 0) blo = (L - qlen - window + 1) / block_size;
+    int64_t per = (nblk - blo + num_segments - 1) / num_segments; /* R-seg */
     for (int i = 0; i < qlen; ++i) {
       int64_t pos = L - qlen + i;
+      int64_t jlo = 0; /* R-win */
+      if (window > 0 && pos - window + 1 > 0) jlo = pos - window + 1;
       for (int g = 0; g < num_q_heads; ++g) {
         int h = g / G;
         double* o = out + ((int64_t)(q0 + i) * num_q_heads + g) * d;
@@ -370,12 +383,13 @@ void oracle_attention_method(const uint16_t* q, int64_t q_stride, int dtype,
         for (int sgi = 0; sgi < num_segments; ++sgi) {
           double m = -INFINITY, l = 0.0;
           for (int k = 0; k < d; ++k) acc[k] = 0.0;
-          int64_t b0 = (int64_t)sgi * per, b1 = b0 + per;
+          int64_t b0 = blo + (int64_t)sgi * per, b1 = b0 + per;
           if (b1 > nblk) b1 = nblk;
           for (int64_t blk = b0; blk < b1; ++blk) {
             /* scores of this block's keys that the query may see */
             double zb[1024]; /* block_size <= 1024 (checked by the Python wrapper) */
             int64_t j0 = blk * block_size, j1 = j0 + block_size;
+            if (j0 < jlo) j0 = jlo;
             if (j1 > pos + 1) j1 = pos + 1;
             if (j0 >= j1) continue;
             double bmax = -INFINITY;
