@@ -119,6 +119,12 @@ int4kv_status_t int4_kv_write(const void* key, int64_t key_token_stride, const v
  *                     prefill/mixed path (no split-K; segments ignored).
  *   max_seqlen_k      host: >= every L_b.
  *   block_table       int32 [num_seqs, block_table_stride], entries < num_blocks.
+ *   sliding_window    W > 0: query row i of sequence b (position pos) attends to
+ *                     keys [max(0, pos - W + 1), pos] only; <= 0: no window.
+ *                     ([pr40633] description: the packed read path shares the
+ *                     common kernel's sliding-window masking.)  On the decode
+ *                     path the split-K segments divide the blocks from the
+ *                     first one the query sees.
  *   rht_signs         fp32 [head_size], the signs used by int4_kv_write.
  *   num_segments      >= 1.  When > 1 on the decode path, segm_output fp32
  *                     [num_seqs, num_q_heads, num_segments, head_size],
@@ -137,9 +143,10 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
                                      const int32_t* seqused_k, int32_t num_seqs,
                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
                                      const int32_t* block_table, int32_t block_table_stride,
-                                     float softmax_scale, const float* rht_signs,
-                                     int32_t num_segments, float* segm_output, float* segm_max,
-                                     float* segm_expsum, void* stream);
+                                     float softmax_scale, int32_t sliding_window,
+                                     const float* rht_signs, int32_t num_segments,
+                                     float* segm_output, float* segm_max, float* segm_expsum,
+                                     void* stream);
 
 /*
  * int4_decode_step: int4_kv_write of one new token per sequence followed by
@@ -174,9 +181,10 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
                                  const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                                  int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                  const int32_t* block_table, int32_t block_table_stride,
-                                 float softmax_scale, const float* rht_signs,
-                                 int32_t num_segments, float* segm_output, float* segm_max,
-                                 float* segm_expsum, void* stream);
+                                 float softmax_scale, int32_t sliding_window,
+                                 const float* rht_signs, int32_t num_segments,
+                                 float* segm_output, float* segm_max, float* segm_expsum,
+                                 void* stream);
 
 /*
  * int4kv_decode_num_segments: the split-K segment count the library's decode

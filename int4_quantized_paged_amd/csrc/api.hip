@@ -69,9 +69,10 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
                                 const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                 const int32_t* block_table, int32_t block_table_stride,
-                                int32_t block_size, float softmax_scale, const float* rht_signs,
-                                int32_t num_segments, float* segm_output, float* segm_max,
-                                float* segm_expsum, int4kv::AttnArgs& a) {
+                                int32_t block_size, float softmax_scale, int32_t sliding_window,
+                                const float* rht_signs, int32_t num_segments,
+                                float* segm_output, float* segm_max, float* segm_expsum,
+                                int4kv::AttnArgs& a) {
   if (!q || !out || !cu_seqlens_q || !seqused_k || !block_table)
     return fail(INT4KV_ERR_INVALID_ARG, "null q, out, cu_seqlens_q, seqused_k or block_table");
   if (num_q_heads < 1 || num_q_heads % num_kv_heads)
@@ -102,6 +103,7 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
                        head_size, num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q,
                        max_seqlen_k, block_table, block_table_stride, softmax_scale, rht_signs,
                        decode ? num_segments : 1, segm_output, segm_max, segm_expsum};
+  a.window = sliding_window > 0 ? sliding_window : 0;
   return INT4KV_OK;
 }
 
@@ -179,9 +181,10 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
                                      const int32_t* seqused_k, int32_t num_seqs,
                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
                                      const int32_t* block_table, int32_t block_table_stride,
-                                     float softmax_scale, const float* rht_signs,
-                                     int32_t num_segments, float* segm_output, float* segm_max,
-                                     float* segm_expsum, void* stream) {
+                                     float softmax_scale, int32_t sliding_window,
+                                     const float* rht_signs, int32_t num_segments,
+                                     float* segm_output, float* segm_max, float* segm_expsum,
+                                     void* stream) {
   int4kv_status_t s =
       check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
   if (s != INT4KV_OK) return s;
@@ -193,8 +196,8 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
   int4kv::AttnArgs a;
   s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
                       num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
-                      block_table, block_table_stride, block_size, softmax_scale, rht_signs,
-                      num_segments, segm_output, segm_max, segm_expsum, a);
+                      block_table, block_table_stride, block_size, softmax_scale, sliding_window,
+                      rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
   if (s != INT4KV_OK) return s;
   const bool decode = max_seqlen_q == 1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -213,9 +216,10 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
                                  const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                                  int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                  const int32_t* block_table, int32_t block_table_stride,
-                                 float softmax_scale, const float* rht_signs,
-                                 int32_t num_segments, float* segm_output, float* segm_max,
-                                 float* segm_expsum, void* stream) {
+                                 float softmax_scale, int32_t sliding_window,
+                                 const float* rht_signs, int32_t num_segments,
+                                 float* segm_output, float* segm_max, float* segm_expsum,
+                                 void* stream) {
   int4kv_status_t s =
       check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
   if (s != INT4KV_OK) return s;
@@ -239,8 +243,8 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
   int4kv::AttnArgs a;
   s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
                       num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
-                      block_table, block_table_stride, block_size, softmax_scale, rht_signs,
-                      num_segments, segm_output, segm_max, segm_expsum, a);
+                      block_table, block_table_stride, block_size, softmax_scale, sliding_window,
+                      rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
   if (s != INT4KV_OK) return s;
   hipError_t e;
   if (max_seqlen_q == 1 && int4kv::decode_lds_supported(a)) {

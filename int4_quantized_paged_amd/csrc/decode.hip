@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512) void decode_kernel(
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
     const float* __restrict__ signs, int32_t num_segments, float* __restrict__ segm_out,
-    float* __restrict__ segm_max, float* __restrict__ segm_sum) {
+    float* __restrict__ segm_max, float* __restrict__ segm_sum, int32_t window) {
   constexpr int NCH = D / 32;
   constexpr int NCOL = D / 16;
   constexpr int R = D / 2 + 4;
@@ -141,8 +141,12 @@ __global__ __launch_bounds__(512) void decode_kernel(
   if (qlen <= 0) return;  // uniform over the workgroup
   const int L = seqused_k[b];
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
-  const int per = (nblk + num_segments - 1) / num_segments;
-  const int b0 = seg * per;
+  // the query sits at L - 1; with a window it sees keys [lo, L) and the
+  // segments split the blocks from the first one it sees
+  const int lo = (window > 0 && L - window > 0) ? L - window : 0;
+  const int blo = lo / kBlockSize;
+  const int per = (nblk - blo + num_segments - 1) / num_segments;
+  const int b0 = blo + seg * per;
   const int b1 = min(b0 + per, nblk);
 
   // ---- prologue: q' = H (signs * q), split into f16 hi + lo parts
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(512) void decode_kernel(
   #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int key = tb * kBlockSize + 16 * n + col;
-        kval[n] = (tb + n < b1) && key < L;
+        kval[n] = (tb + n < b1) && key < L && key >= lo;
         sK[n] = as_float(cur.ks[n] & 0xFFFFFFF0u);
         zK[n] = (float)(cur.ks[n] & 0xFu);
         sV[n] = as_float(cur.vs[n] & 0xFFFFFFF0u);
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(512) void decode_kernel(
         m_run[v] = mnew;
         const float p0 = exp2f(z[0] - mnew), p1 = exp2f(z[1] - mnew);
         // W = p sV as f16 hi + lo (22 significant bits)
-        const float f0 = kval[0] ? p0 * sV[0] : 0.f, f1 = kval[1] ? p1 * sV[1] : 0.f;
+        const float f0 = opaque(kval[0] ? p0 * sV[0] : 0.f), f1 = opaque(kval[1] ? p1 * sV[1] : 0.f);
         const _Float16 w0 = (_Float16)f0, w1 = (_Float16)f1;
         const _Float16 u0 = (_Float16)(f0 - (float)w0), u1 = (_Float16)(f1 - (float)w1);
         l_run[v] = l_run[v] * alpha + (p0 + p1);
@@ -592,7 +596,7 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
                      reinterpret_cast<const uint16_t*>(a.q), a.q_stride,
                      reinterpret_cast<uint16_t*>(a.out), a.cache, hkv, a.num_q_heads,
                      a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs,
-                     ns, a.segm_out, a.segm_max, a.segm_sum);
+                     ns, a.segm_out, a.segm_max, a.segm_sum, a.window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   return launch_reduce(a, stream);

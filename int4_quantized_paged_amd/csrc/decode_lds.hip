@@ -155,7 +155,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     float* __restrict__ segm_max, float* __restrict__ segm_sum,
     const uint16_t* __restrict__ key_new, int64_t key_new_stride,
     const uint16_t* __restrict__ value_new, int64_t value_new_stride,
-    const int64_t* __restrict__ slot_new) {
+    const int64_t* __restrict__ slot_new, int32_t window) {
   using GG = Geo<D, HPW>;
   using WG = WGeo<G>;
   constexpr uint32_t R = GG::R;
@@ -183,8 +183,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   const int qlen = cu_seqlens_q[b + 1] - q0;
   const int L = seqused_k[b];
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
-  const int per = (nblk + num_segments - 1) / num_segments;
-  const int b0 = seg * per;
+  // the query sits at L - 1; with a window it sees keys [lo, L) and the
+  // segments split the blocks from the first one it sees
+  const int lo = (window > 0 && L - window > 0) ? L - window : 0;
+  const int blo = lo / kBlockSize;
+  const int per = (nblk - blo + num_segments - 1) / num_segments;
+  const int b0 = blo + seg * per;
   const int b1 = min(b0 + per, nblk);
   const int ntile = b1 > b0 ? (b1 - b0 + 1) / 2 : 0;
 
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   bool store_pending = false;  // this wave stored rows whose completion is still to be awaited
   if (slot_new != nullptr) {
     const int64_t slot = slot_new[b];
-    if (slot >= 0 && L > 0 && (L - 1) / kBlockSize / per == seg) {  // uniform over the workgroup
+    if (slot >= 0 && L > 0 && ((L - 1) / kBlockSize - blo) / per == seg) {  // uniform over the workgroup
       constexpr int WE = 16, WLPR = D / WE, WRPW = kWave / WLPR;  // rows of 8 or 4 lanes
       if (wave * WRPW < 2 * HPW) {
         const int r = wave * WRPW + lane / WLPR;  // row kv * HPW + head of the group
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int key = tb * kBlockSize + 16 * n + col;
-      kval[n] = (tb + n < b1) && key < L;
+      kval[n] = (tb + n < b1) && key < L && key >= lo;
       const float sK = as_float(cw.kw[n] & 0xFFFFFFF0u);
       const float zK = (float)(cw.kw[n] & 0xFu);
       sV[n] = kval[n] ? as_float(cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked keys get zero weight
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int v = 0; v < RPG; ++v) {
       const float p0 = __builtin_amdgcn_exp2f(z[v][0] - m_run[v]);
       const float p1 = __builtin_amdgcn_exp2f(z[v][1] - m_run[v]);
-      const float w0 = p0 * sV[0], w1 = p1 * sV[1];
+      const float w0 = opaque(p0 * sV[0]), w1 = opaque(p1 * sV[1]);
       half2_t wh, wl;
       wh[0] = (_Float16)w0;
       wh[1] = (_Float16)w1;
@@ -774,7 +778,7 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
                      scale_log2, a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum,
                      reinterpret_cast<const uint16_t*>(a.key_new), a.key_new_stride,
                      reinterpret_cast<const uint16_t*>(a.value_new), a.value_new_stride,
-                     a.slot_new);
+                     a.slot_new, a.window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_segments == 1) return e;
   return launch_reduce(a, stream);

@@ -29,6 +29,9 @@ struct AttnArgs {
   float* segm_out;
   float* segm_max;
   float* segm_sum;
+  // sliding window: the query at position pos sees keys [pos - window + 1,
+  // pos]; <= 0 is no window
+  int32_t window = 0;
   // fused decode step only: the new token of each sequence (token b belongs to
   // sequence b and is its last key), encoded into the cache by the workgroup
   // that reads its block; null otherwise

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
-    const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq) {
+    const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq, int32_t window) {
   using PG = PGeo<D, G>;
   constexpr int R = PG::R, RW = PG::RW, DW = PG::DW, NIB = PG::NIB;
   constexpr int NCH = D / 32;   // f16 MFMA k-chunks of the score
@@ -136,6 +136,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int ntiles = nkeys > 0 ? (nkeys + 31) / 32 : 0;
   const int nblk = (nkeys + kBlockSize - 1) / kBlockSize;
   const int pos_lo = L - qlen + qt * TQ;          // position of the first row's token
+  // sliding window (keys [pos - window + 1, pos] per row): the first row's
+  // window start bounds the key range from below; tiles before it are skipped
+  const int last_lo = L - qlen + t_hi - window + 1;  // the last row's window start
+  const int t0 = (window > 0 && pos_lo - window + 1 > 0) ? (pos_lo - window + 1) / 32 : 0;
 
   // ---- prologue: q' = H (signs * q), normalised per row to |q'| < 2^10, split
   // into f16 hi + lo and staged in LDS in the MFMA operand order
@@ -298,22 +302,23 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     vsel[bb] = 0x0C000C00u | by | ((4u + by) << 16);
   }
 
-  // steps s = 0 .. nsteps-1 process tiles 2s (even group) and 2s+1 (odd
-  // group); each group keeps kPairs - 1 of its own tiles in flight.  A tile
-  // past the last one (odd count) is a clamped copy whose keys are all masked.
+  // steps s = 0 .. nsteps-1 process tiles t0 + 2s (even group) and t0 + 2s + 1
+  // (odd group); each group keeps kPairs - 1 of its own tiles in flight.  A
+  // tile past the last one (odd count) is a clamped copy whose keys are all
+  // masked.
   constexpr int kPairs = kStages / 2;
-  const int nsteps = (ntiles + 1) / 2;
+  const int nsteps = (ntiles - t0 + 1) / 2;
   if (nsteps > 0) {
 #pragma unroll
     for (int i = 0; i < kPairs - 1; ++i) {
-      load_id(2 * i + kg);
-      issue(2 * i + kg);
+      load_id(t0 + 2 * i + kg);
+      issue(t0 + 2 * i + kg);
     }
-    load_id(2 * (kPairs - 1) + kg);
+    load_id(t0 + 2 * (kPairs - 1) + kg);
   }
 
   for (int sidx = 0; sidx < nsteps; ++sidx) {
-    const int t = 2 * sidx + kg;
+    const int t = t0 + 2 * sidx + kg;
     wait_vmem<(kPairs - 2) * NIB>();  // this wave's copies of tile t have landed
     __syncthreads();                  // ... and everyone's; everyone is done with step s-1
     issue(t + 2 * (kPairs - 1));      // into the stage of tile t-2 (clamped to the last block)
@@ -359,7 +364,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       }
 
     // online softmax (base 2) per row; keys past a row's position are masked
-    const bool masked = 32 * t + 31 > pos_lo;  // uniform: only tiles near the diagonal
+    // uniform: only tiles near the diagonal, or near a row's window start
+    const bool masked = 32 * t + 31 > pos_lo || (window > 0 && 32 * t < last_lo);
     float sKc[2], zK[2], sV[2], zV[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -381,7 +387,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           float zz = fmaf(-zK[n], qsum[i][v], sacc[i][n][v]) * sKc[n];
-          if (masked) zz = (32 * t + 16 * n + col <= pos[i][v]) ? zz : -INFINITY;
+          if (masked) {
+            const int key = 32 * t + 16 * n + col;
+            zz = (key <= pos[i][v] && (window <= 0 || key > pos[i][v] - window)) ? zz : -INFINITY;
+          }
           z[i][v][n] = zz;
           over |= zz > thr[i][v];
         }
@@ -407,7 +416,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       for (int v = 0; v < 4; ++v) {
         const float p0 = __builtin_amdgcn_exp2f(z[i][v][0] - m_run[i][v]);
         const float p1 = __builtin_amdgcn_exp2f(z[i][v][1] - m_run[i][v]);
-        const float w0 = p0 * sV[0], w1 = p1 * sV[1];
+        const float w0 = opaque(p0 * sV[0]), w1 = opaque(p1 * sV[1]);
         half2_t wh, wl;  // W = p sV as f16 hi + lo (22 significant bits)
         wh[0] = (_Float16)w0;
         wh[1] = (_Float16)w1;
@@ -569,7 +578,7 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
                      reinterpret_cast<const uint16_t*>(a.q), a.q_stride,
                      reinterpret_cast<uint16_t*>(a.out), a.cache, a.num_kv_heads, a.num_q_heads,
                      a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs,
-                     a.num_seqs, tiles_per_seq);
+                     a.num_seqs, tiles_per_seq, a.window);
   return hipGetLastError();
 }
 

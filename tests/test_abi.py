@@ -86,14 +86,14 @@ def test_write_zero_tokens_is_a_no_op():
 
 def _attn(**kw):
     a = dict(q=FAKE, qs=4096, out=FAKE, dtype=1, cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32,
-             cu=FAKE, su=FAKE, S=4, mq=1, mk=1024, bt=FAKE, bts=64, scale=0.088, signs=FAKE, ns=1,
-             so=None, sm=None, ss=None, stream=None)
+             cu=FAKE, su=FAKE, S=4, mq=1, mk=1024, bt=FAKE, bts=64, scale=0.088, win=0,
+             signs=FAKE, ns=1, so=None, sm=None, ss=None, stream=None)
     a.update(kw)
     lib = ik.load_library()
     return lib.int4_paged_attention(a["q"], a["qs"], a["out"], a["dtype"], a["cache"], a["nb"],
                                     a["bs"], a["hkv"], a["d"], a["hq"], a["cu"], a["su"], a["S"],
-                                    a["mq"], a["mk"], a["bt"], a["bts"], a["scale"], a["signs"],
-                                    a["ns"], a["so"], a["sm"], a["ss"], a["stream"])
+                                    a["mq"], a["mk"], a["bt"], a["bts"], a["scale"], a["win"],
+                                    a["signs"], a["ns"], a["so"], a["sm"], a["ss"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -115,15 +115,15 @@ def test_attention_empty_batch_is_a_no_op():
 def _step(**kw):
     a = dict(kn=FAKE, ks=1024, vn=FAKE, vs=1024, slots=FAKE, q=FAKE, qs=4096, out=FAKE, dtype=1,
              cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32, cu=FAKE, su=FAKE, S=4, mq=1, mk=1024,
-             bt=FAKE, bts=64, scale=0.088, signs=FAKE, ns=1, so=None, sm=None, ss=None,
+             bt=FAKE, bts=64, scale=0.088, win=0, signs=FAKE, ns=1, so=None, sm=None, ss=None,
              stream=None)
     a.update(kw)
     lib = ik.load_library()
     return lib.int4_decode_step(a["kn"], a["ks"], a["vn"], a["vs"], a["slots"], a["q"], a["qs"],
                                 a["out"], a["dtype"], a["cache"], a["nb"], a["bs"], a["hkv"],
                                 a["d"], a["hq"], a["cu"], a["su"], a["S"], a["mq"], a["mk"],
-                                a["bt"], a["bts"], a["scale"], a["signs"], a["ns"], a["so"],
-                                a["sm"], a["ss"], a["stream"])
+                                a["bt"], a["bts"], a["scale"], a["win"], a["signs"], a["ns"],
+                                a["so"], a["sm"], a["ss"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
