@@ -308,8 +308,8 @@ __global__ __launch_bounds__(512) void decode_kernel(
         m_run[v] = mnew;
         const float p0 = exp2f(z[0] - mnew), p1 = exp2f(z[1] - mnew);
         // W = p sV as f16 hi + lo (22 significant bits)
-        const float f0 = opaque(kval[0] ? p0 * sV[0] : 0.f), f1 = opaque(kval[1] ? p1 * sV[1] : 0.f);
-        const _Float16 w0 = (_Float16)f0, w1 = (_Float16)f1;
+        const float f0 = kval[0] ? p0 * sV[0] : 0.f, f1 = kval[1] ? p1 * sV[1] : 0.f;
+        const _Float16 w0 = opaque((_Float16)f0), w1 = opaque((_Float16)f1);  // lo is taken against this hi
         const _Float16 u0 = (_Float16)(f0 - (float)w0), u1 = (_Float16)(f1 - (float)w1);
         l_run[v] = l_run[v] * alpha + (p0 + p1);
         corr[v] = corr[v] * alpha + (f0 * zV[0] + f1 * zV[1]);

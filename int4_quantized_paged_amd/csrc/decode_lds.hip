@@ -611,10 +611,11 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int v = 0; v < RPG; ++v) {
       const float p0 = __builtin_amdgcn_exp2f(z[v][0] - m_run[v]);
       const float p1 = __builtin_amdgcn_exp2f(z[v][1] - m_run[v]);
-      const float w0 = opaque(p0 * sV[0]), w1 = opaque(p1 * sV[1]);
+      const float w0 = p0 * sV[0], w1 = p1 * sV[1];
       half2_t wh, wl;
       wh[0] = (_Float16)w0;
       wh[1] = (_Float16)w1;
+      wh = opaque(wh);  // lo is taken against this hi
       wl[0] = (_Float16)(w0 - (float)wh[0]);
       wl[1] = (_Float16)(w1 - (float)wh[1]);
       l_run[v] += p0 + p1;

@@ -94,14 +94,16 @@ __device__ __forceinline__ uint32_t nib_pair_f16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// An f32 value the compiler cannot trace back to the expression that made it.
-// The f16 hi + lo split of a product w needs hi rounded from the f32 value w in
-// every use: left visible, the product may be folded into an f16 conversion
-// (v_fma_mix with a zero addend, rounding the exact product once) in one use
-// while another converts the f32 w, and hi + lo is then off by an f16 ulp.
-__device__ __forceinline__ float opaque(float x) {
+// A value the compiler cannot trace back to the expression that made it.
+// The f16 hi + lo split of a softmax weight w = p * s needs lo computed
+// against the hi that is stored.  Left visible, hi = f16(p * s) may be formed
+// twice: once from the fp32 product for the stored copy and once by rounding
+// the exact product straight to f16 (v_fma_mix with a zero addend) for lo's
+// subtrahend.  The two differ at fp32 ties, and hi + lo is then off by an f16
+// ulp.  Pinning hi leaves lo = f16(w - hi) free to use the exact product.
+template <typename T>
+__device__ __forceinline__ T opaque(T x) {
   asm("" : "+v"(x));
   return x;
 }
-
 }  // namespace int4kv

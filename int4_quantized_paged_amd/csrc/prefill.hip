@@ -416,10 +416,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       for (int v = 0; v < 4; ++v) {
         const float p0 = __builtin_amdgcn_exp2f(z[i][v][0] - m_run[i][v]);
         const float p1 = __builtin_amdgcn_exp2f(z[i][v][1] - m_run[i][v]);
-        const float w0 = opaque(p0 * sV[0]), w1 = opaque(p1 * sV[1]);
+        const float w0 = p0 * sV[0], w1 = p1 * sV[1];
         half2_t wh, wl;  // W = p sV as f16 hi + lo (22 significant bits)
         wh[0] = (_Float16)w0;
         wh[1] = (_Float16)w1;
+        wh = opaque(wh);  // lo is taken against this hi
         wl[0] = (_Float16)(w0 - (float)wh[0]);
         wl[1] = (_Float16)(w1 - (float)wh[1]);
         l_run[i][v] += p0 + p1;

@@ -123,9 +123,11 @@ def test_llama3_decode_full_size_sampled(oracle_mod, ns):
         assert_attention_close(out[seqs], ref, f"seq {seqs}")
 
 
-@pytest.mark.parametrize("ns", [64])
+@pytest.mark.parametrize("ns", [64, 1])
 def test_long_context_decode_full_size_sampled(oracle_mod, ns):
-    """4 x 131072, 64 q / 8 KV heads: split-K at full size; one sequence checked."""
+    """4 x 131072, 64 q / 8 KV heads: split-K at full size (64 segments, the
+    benchmark's launch) and one segment of 8192 tiles, the longest fp32
+    accumulation the kernel runs; one sequence checked."""
     header(f"long-context decode full size NS={ns}")
     w = wl.long_context_decode(device="cuda")
     t = to_dev(w)
