@@ -9,8 +9,9 @@
 //    (16 tokens x HPW x R bytes).  Each 2-block tile is copied HBM -> LDS with
 //    global_load_lds_dwordx4 by all waves together (every 128-byte line is
 //    fetched once, non-temporal) into a ring of 3 to 6 stages (as deep as the
-//    160 KiB of LDS allows), all but one stage ahead of the math; with 4 or
-//    more stages the workgroup meets at a barrier every other step.  The
+//    160 KiB of LDS allows).  A tile's words are read one step before its
+//    math, so at the barrier of step t the stage of tile t is already free and
+//    takes tile t + S: S - 2 to S - 1 tiles stay in flight.  The
 //    copies are issued from inline assembly and waited for with explicit
 //    vmcnt so the compiler does not drain the ring at every barrier.  When a token's run is
 //    a whole number of 16-byte chunks, token rows are re-laid out in LDS with a
@@ -168,8 +169,6 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int LPQ = 64 / G;
   constexpr int NI = GG::NI;
   constexpr int S = Lay<D, G, HPW>::S;
-  // with four or more ring stages the workgroup synchronises every other step
-  constexpr bool kPairSync = S >= 4;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
@@ -354,14 +353,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - 22);
     }
   }
-  if (ntile > 0) {  // always S - 1 tiles ahead (clamped), so the vmcnts below are exact
+  // tiles 0 .. S-2 now; tile S-1 goes into the last stage once every wave has
+  // read the staged query (the barrier where tile 0 has landed).  Copies past
+  // the segment's end re-read its last block, so the vmcnts below are exact.
+  if (ntile > 0) {
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) {
       load_ids(0, i);
       issue(0, i);
     }
     load_ids(0, S - 1);
-    if constexpr (kPairSync) load_ids(1, S);
   }
   // zero row of the W tile (MFMA rows that carry no query head read it)
   if (lane < 16) reinterpret_cast<uint32_t*>(wt + WG::WZERO)[lane] = 0u;
@@ -523,27 +524,13 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int j = 0; j < 8; ++j) w.va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
   };
 
-  auto step = [&](int t, auto even, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3],
+  auto step = [&](int t, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3],
                   const TileWords& cw, TileWords& nw) {
-    if constexpr (kPairSync) {
-      // one barrier per two steps: at an even step, tiles t+1 and t+2 must
-      // have landed for every wave (their words are read in this step and the
-      // next), and everyone is done with tiles t-1 and t, whose stages take
-      // tiles t+S-1 and t+S (clamped to the segment's last block)
-      if constexpr (decltype(even)::value) {
-        wait_tiles(std::integral_constant<int, S - 4>());
-        __syncthreads();
-        issue(0, t + S - 1);
-        issue(1, t + S);
-        load_ids(0, t + S + 1);
-        load_ids(1, t + S + 2);
-      }
-    } else {
-      wait_tiles(std::integral_constant<int, S - 3>());  // this wave's copies of tile t+1
-      __syncthreads();      // ... and everyone's; everyone is done with tile t-1
-      issue(0, t + S - 1);  // into the stage of tile t-1 (clamped to the segment's last block)
-      load_ids(0, t + S);
-    }
+    wait_tiles(std::integral_constant<int, S - 2>());  // this wave's copies of tile t+1
+    __syncthreads();  // ... and everyone's.  Every wave read tile t's words in step t-1
+                      // (LDS reads complete before the barrier), so its stage is free:
+    issue(0, t + S);  // tile t+S (clamped to the segment's last block)
+    load_ids(0, t + S + 1);
     const unsigned char* st = smem + (uint32_t)(t % S) * GG::stage;
     const int tb = b0 + 2 * t;
 
@@ -670,14 +657,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   };
 
   // ---- main loop.  Tile t+1 must have landed at the top of step t; tiles
-  // t+2 .. t+S-1 are in flight.  Unrolled by two so the score accumulators
-  // alternate without copies.
+  // t+2 .. t+S-1 are in flight, and t+S joins them.  Unrolled by two so the
+  // score accumulators alternate without copies.
   i32x4_t accA[2][3], accB[2][3];
   TileWords wA, wB;
   if (ntile > 0) {
     wait_tiles(std::integral_constant<int, S - 2>());  // tile 0
     if (store_pending) wait_vmem<0>();  // this wave's stores of the new token, too
     __syncthreads();
+    issue(0, S - 1);  // the staged query has been read by every wave
+    load_ids(0, S);
     i32x4_t kb[2][NCK];
     k_operands(smem, kb);
     tile_words(smem, wA);
@@ -686,10 +675,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
   int t = 0;
   for (; t + 1 < ntile; t += 2) {
-    step(t, std::true_type(), accA, accB, wA, wB);
-    step(t + 1, std::false_type(), accB, accA, wB, wA);
+    step(t, accA, accB, wA, wB);
+    step(t + 1, accB, accA, wB, wA);
   }
-  if (t < ntile) step(t, std::true_type(), accA, accB, wA, wB);
+  if (t < ntile) step(t, accA, accB, wA, wB);
   wait_vmem<0>();  // drain the clamped look-ahead copies
 
   // ---- finalise: sums over the 16 lanes of a group
