@@ -11,8 +11,8 @@
 // here), so the bytes are reproducible bit for bit:
 //   * the signs are applied as bit flips of the 16-bit inputs (exact),
 //   * clamp-then-round equals round-then-clamp for the integer bounds 0 and
-//     15, and rounding to nearest-even is an fp32 add of 2^23, after which
-//     the code sits in the low 4 bits of the sum.
+//     15, and rounding to nearest-even is an fp32 add of 1.5 * 2^23, after
+//     which the code sits in the low 4 bits of the sum.
 #pragma once
 
 #include "device_common.h"
@@ -60,9 +60,59 @@ __device__ __forceinline__ void row_inputs(const u32x4_t (&a)[E / 8], const uint
   }
 }
 
+// x[e + i] = partner(x[e + i]) * c + x[e + i] for i < 8, the partner being
+// lane ^ m (m = 1 or 2) read through a DPP quad permute of the fmac's first
+// operand.  The leading s_nop gives the two wait states a DPP read needs after
+// the VALU writes of these registers, which all precede the block.
+template <int E>
+__device__ __forceinline__ void cross_fmac8(int m, float (&x)[E], int e, float c) {
+  if (m == 1) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(x[e]), "+v"(x[e + 1]), "+v"(x[e + 2]), "+v"(x[e + 3]), "+v"(x[e + 4]),
+          "+v"(x[e + 5]), "+v"(x[e + 6]), "+v"(x[e + 7])
+        : "v"(c));
+  } else {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(x[e]), "+v"(x[e + 1]), "+v"(x[e + 2]), "+v"(x[e + 3]), "+v"(x[e + 4]),
+          "+v"(x[e + 5]), "+v"(x[e + 6]), "+v"(x[e + 7])
+        : "v"(c));
+  }
+}
+
 // Rotation, range, scale, zero point and codes of one row: the lane's E / 8
 // packed code dwords (bytes j = code_{2j} | code_{2j+1} << 4) and the row's
 // scale word bits(s_t) | zp.
+//
+// The spans that pair lanes (E, 2E, ...) take one fused multiply-add per
+// element, new = partner * c + self with c = +1 in the lower lane of a pair
+// and -1 in the upper one: the product is exact, so the sum is rounded once
+// and the lower lane holds u + v while the upper one holds v - u = -(u - v)
+// (round-to-nearest-even is symmetric).  A lane's values are therefore its
+// row elements times sigma = (-1)^popcount(sub); the range and the codes
+// undo that exactly (min and max swap under negation, and the codes are
+// fl(stored * (sigma * inv)) = fl(y * inv)).
+//
+// Codes: t = fl(fl(y * inv) + zp) is clamped to [0, 15] and rounded to
+// nearest even by adding 1.5 * 2^23, after which the code sits in the low 4
+// bits of the sum.
 template <int E, int LPR>
 __device__ __forceinline__ uint32_t encode_piece(float (&x)[E], int sub,
                                                  uint32_t (&packed)[E / 8]) {
@@ -78,24 +128,33 @@ __device__ __forceinline__ uint32_t encode_piece(float (&x)[E], int sub,
       x[e + span] = __fsub_rn(u, v);
     }
   }
-  // spans E, 2E, ... across the lanes of a row: the lower partner keeps
-  // u + v, the upper one u - v, written as partner + (-self)
+  // spans E, 2E, ... across the lanes of a row
+  float sigma = 1.0f;
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) {
-    const uint32_t xflip = (sub & m) ? 0x80000000u : 0u;
+    const float c = (sub & m) ? -1.0f : 1.0f;
+    sigma *= c;
+    if (m <= 2) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float p = shfl_xor_rt(x[e], m);
-      x[e] = __fadd_rn(p, as_float(as_uint(x[e]) ^ xflip));
+      for (int e = 0; e < E; e += 8) cross_fmac8(m, x, e, c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = __builtin_fmaf(shfl_xor_rt(x[e], m), c, x[e]);
     }
   }
 
-  // row range
-  float mn = fminf(x[0], x[1]), mx = fmaxf(x[0], x[1]);
+  // row range of the stored values (one min3 / max3 per two elements), then
+  // of the row's elements, then over the row's lanes
+  float mn = __builtin_fminf(x[0], x[1]), mx = __builtin_fmaxf(x[0], x[1]);
 #pragma unroll
   for (int e = 2; e < E; e += 2) {
-    mn = __builtin_fminf(mn, __builtin_fminf(x[e], x[e + 1]));
-    mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[e], x[e + 1]));
+    mn = __builtin_fminf(__builtin_fminf(mn, x[e]), x[e + 1]);
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, x[e]), x[e + 1]);
+  }
+  if (LPR > 1 && sigma < 0.0f) {
+    const float t = mn;
+    mn = -mx;
+    mx = -t;
   }
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) {
@@ -107,19 +166,18 @@ __device__ __forceinline__ uint32_t encode_piece(float (&x)[E], int sub,
   const float s_t = as_float(as_uint(sc) & 0xFFFFFFF0u);
   const float inv = __fdiv_rn(1.0f, s_t);
   const float zpf = fminf(fmaxf(rintf(__fmul_rn(-mn, inv)), 0.0f), 15.0f);
+  const float invs = LPR > 1 ? sigma * inv : inv;  // exact
+  constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
 
-  // codes: clamp to [0, 15], then round to nearest even by adding 2^23; the
-  // code is then the low 4 bits of the sum's bit pattern
 #pragma unroll
   for (int q = 0; q < E / 8; ++q) {
     uint32_t b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 8 * q + 2 * j;
-      const float c0 = __fadd_rn(enc_med3(__fadd_rn(__fmul_rn(x[e], inv), zpf), 0.0f, 15.0f),
-                                 8388608.0f);
-      const float c1 = __fadd_rn(enc_med3(__fadd_rn(__fmul_rn(x[e + 1], inv), zpf), 0.0f, 15.0f),
-                                 8388608.0f);
+      const float t0 = enc_med3(__fadd_rn(__fmul_rn(x[e], invs), zpf), 0.0f, 15.0f);
+      const float t1 = enc_med3(__fadd_rn(__fmul_rn(x[e + 1], invs), zpf), 0.0f, 15.0f);
+      const float c0 = __fadd_rn(t0, kMagic), c1 = __fadd_rn(t1, kMagic);
       b[j] = (as_uint(c1) << 4) | as_uint(c0);  // byte 0 = code_lo | code_hi << 4
     }
     const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // [b0.0 b1.0 0 0]
