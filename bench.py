@@ -14,8 +14,10 @@ in the 256 MB Infinity Cache.
 Steps are plain library calls: the host enqueues a step in about a fifth of
 its GPU time, and HIP-graph replays of the same calls (`--graph`, checked bit
 for bit against plain calls) measured a few microseconds slower per step.
-The default warm-up (100 steps) lets the GPU reach its steady clock and
-address-translation state; the first tens of steps run about 15% slower.
+The default warm-up (2000 steps, about 0.2 s) lets the GPU reach its steady
+clock and address-translation state: after 100 warm-up steps the next 200
+still ran about 4% slower than they do after 2000 (106.5-108 against
+101.8-103.5 us per step on one box), and the first tens run about 15% slower.
 Prints one JSON line: decode
 effective KV GB/s (packed K+V bytes of every key attended, once per KV head,
 over the step time), the bulk cache-write rate (tokens/s, from a timed
@@ -315,7 +317,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-rows", action="store_true",
                     help="skip the prefill and Llama-3-shaped decode measurements")
