@@ -214,9 +214,10 @@ def _attention_setup(w, dev, ns, ncaches=1):
 
 def other_rows(dev):
     """The other timed rows of the path, each at its full size: prefill on the
-    chunked-prefill mix (MFMA-bound; TFLOP/s against the dense f16 peak) and
-    decode on the Llama-3-8B-shaped batch (HBM-bound; two cache copies
-    alternate).  Back-to-back calls between HIP events, median of five rounds."""
+    chunked-prefill mix (MFMA-bound; TFLOP/s against the dense f16 peak), the
+    GQA decode step (8 short sequences, latency-bound) and decode on the
+    Llama-3-8B-shaped batch (HBM-bound; two cache copies alternate).
+    Back-to-back calls between HIP events, median of five rounds."""
     rows = {}
     for d in (128, 64):
         w = wl.chunked_prefill(device=dev, head_size=d)
@@ -233,6 +234,34 @@ def other_rows(dev):
             "algorithmic_gflop": round(fl / 1e9, 2),
             "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
         del w, call
+    # GQA decode: 8 sequences of 1..1024 keys, one new token each, in one
+    # int4_decode_step (latency-bound: reported in us and GB/s, not against HBM peak)
+    w = wl.gqa_decode(device=dev)
+    cache = ik.empty_cache(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)
+    signs = w.signs.to(dev)
+    idx_p, slots_p = w.token_set("prior")
+    ik.int4_kv_write(w.key[idx_p.to(dev)], w.value[idx_p.to(dev)], slots_p.to(dev), cache, signs)
+    idx_n, slots_n = w.token_set("new")
+    kn, vn, sn = w.key[idx_n.to(dev)].contiguous(), w.value[idx_n.to(dev)].contiguous(), slots_n.to(dev)
+    ns = ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads, w.max_seqlen_k)
+    segs = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns, w.head_size, dev) if ns > 1 else \
+        (None, None, None)
+    cu, su, bt = w.cu_seqlens_q().to(dev), w.seqused_k().to(dev), w.block_table.to(dev)
+    out = torch.empty_like(w.query)
+    gstep = lambda: ik.int4_decode_step(kn, vn, sn, w.query, cache, cu, su, 1, w.max_seqlen_k,  # noqa: E731
+                                        bt, w.softmax_scale, signs, out=out, num_segments=ns,
+                                        segm_output=segs[0], segm_max=segs[1],
+                                        segm_expsum=segs[2])
+    for _ in range(20):
+        gstep()
+    us = _median_event_us(gstep, 50)
+    rows["gqa_decode_step"] = {
+        "workload": f"8 seqs, {sum(w.kv_lens)} keys in all (1..1024 each), 32 q / 8 KV heads, "
+                    "d 128; write 8 new tokens + decode (int4_decode_step)",
+        "num_segments": ns, "us": round(us, 2),
+        "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
+    del w, cache, gstep
+
     w = wl.llama3_8b_decode(device=dev)
     # its bulk cache fill (262144 tokens) and a decode step's write (64 tokens)
     cache = ik.empty_cache(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)

@@ -48,9 +48,9 @@ def _load():
     lib.oracle_kv_write.argtypes = [P, i64, P, i64, i32, P, i32, P, i32, i32, i32, i32, P]
     lib.oracle_decode_row.argtypes = [P, i32, P, P]
     lib.oracle_attention_plain.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i32,
-                                           P, P, i32, P, i32, f64, P, i32, P]
+                                           P, P, i32, P, i32, f64, P, i32, f64, P]
     lib.oracle_attention_method.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i32,
-                                            P, P, i32, P, i32, f64, P, i32, i32, P]
+                                            P, P, i32, P, i32, f64, P, i32, i32, f64, P]
     _lib = lib
     return lib
 
@@ -174,9 +174,11 @@ def _attn_args(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table, num_q
 
 
 def attention_plain(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table,
-                    softmax_scale, signs, num_q_heads, window: int = 0) -> np.ndarray:
+                    softmax_scale, signs, num_q_heads, window: int = 0,
+                    softcap: float = 0.0) -> np.ndarray:
     """Causal softmax attention over the decoded cache, fp64 [Tq, Hq, d].
-    window > 0: the query at position pos sees keys [pos - window + 1, pos]."""
+    window > 0: the query at position pos sees keys [pos - window + 1, pos].
+    softcap > 0: scores z become softcap * tanh(z / softcap) before the softmax."""
     q, nb, bs, hkv, d, Tq, cu, su, bt = _attn_args(q_bits, dtype, cache, cu_seqlens_q,
                                                    seqused_k, block_table, num_q_heads)
     out = np.zeros((Tq, num_q_heads, d), np.float64)
@@ -184,13 +186,14 @@ def attention_plain(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table,
     _load().oracle_attention_plain(_p(q), num_q_heads * d, _DT[dtype], _p(cache), nb, bs, hkv,
                                    d, num_q_heads, _p(cu), _p(su), su.shape[0], _p(bt),
                                    bt.shape[1], float(softmax_scale),
-                                   _p(_c(signs, np.float32)), int(window), _p(out))
+                                   _p(_c(signs, np.float32)), int(window), float(softcap),
+                                   _p(out))
     return out
 
 
 def attention_method(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table,
                      softmax_scale, signs, num_q_heads, num_segments=1,
-                     window: int = 0) -> np.ndarray:
+                     window: int = 0, softcap: float = 0.0) -> np.ndarray:
     """Same result as attention_plain, computed the way the packed read path does."""
     q, nb, bs, hkv, d, Tq, cu, su, bt = _attn_args(q_bits, dtype, cache, cu_seqlens_q,
                                                    seqused_k, block_table, num_q_heads)
@@ -200,5 +203,5 @@ def attention_method(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table,
                                     d, num_q_heads, _p(cu), _p(su), su.shape[0], _p(bt),
                                     bt.shape[1], float(softmax_scale),
                                     _p(_c(signs, np.float32)), int(num_segments),
-                                    int(window), _p(out))
+                                    int(window), float(softcap), _p(out))
     return out

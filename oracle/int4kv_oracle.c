@@ -48,6 +48,11 @@
  *           [max(0, pos - W + 1), pos], W keys counting its own; W <= 0 is no
  *           window.  ([pr40633] description: the packed read path shares the
  *           common kernel's sliding-window masking helper.)
+ *   R-cap   logit soft-capping c > 0: each scaled score z becomes
+ *           c * tanh(z / c) before the softmax; c <= 0 is no capping.
+ *           ([pr40633] description: the packed read path shares the common
+ *           kernel's softcap helper; the pages do not restate its formula,
+ *           and this is the usual tanh soft cap.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -276,7 +281,8 @@ void oracle_attention_plain(const uint16_t* q, int64_t q_stride, int dtype,
                             int num_kv_heads, int d, int num_q_heads,
                             const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                             int num_seqs, const int32_t* block_table, int bt_stride,
-                            double softmax_scale, const float* signs, int window, double* out) {
+                            double softmax_scale, const float* signs, int window,
+                            double softcap, double* out) {
   (void)num_blocks;
   int G = num_q_heads / num_kv_heads;
   for (int b = 0; b < num_seqs; ++b) {
@@ -311,6 +317,7 @@ void oracle_attention_plain(const uint16_t* q, int64_t q_stride, int dtype,
             double acc = 0.0;
             for (int k = 0; k < d; ++k) acc += qv[k] * K[j * d + k];
             z[j] = softmax_scale * acc;
+            if (softcap > 0.0) z[j] = softcap * tanh(z[j] / softcap); /* R-cap */
             if (z[j] > zmax) zmax = z[j];
           }
           double den = 0.0;
@@ -347,7 +354,7 @@ void oracle_attention_method(const uint16_t* q, int64_t q_stride, int dtype,
                              const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                              int num_seqs, const int32_t* block_table, int bt_stride,
                              double softmax_scale, const float* signs, int num_segments,
-                             int window, double* out) {
+                             int window, double softcap, double* out) {
   (void)num_blocks;
   int G = num_q_heads / num_kv_heads;
   if (num_segments < 1) num_segments = 1;
@@ -405,6 +412,7 @@ void oracle_attention_method(const uint16_t* q, int64_t q_stride, int dtype,
                 dot_odd += qr[2 * jj + 1] * (double)((row[jj] >> 4) & 0xF);
               }
               zb[j - j0] = c * (double)s_t * (dot_even + dot_odd - (double)zp * qsum);
+              if (softcap > 0.0) zb[j - j0] = softcap * tanh(zb[j - j0] / softcap); /* R-cap */
               if (zb[j - j0] > bmax) bmax = zb[j - j0];
             }
             /* online softmax: rescale the running state to the new maximum */

@@ -39,7 +39,7 @@ def _run(oracle_mod, w, cache, method=False, ns=1):
     return oracle_mod.attention_plain(*args)
 
 
-def _numpy_brute(w, cache):
+def _numpy_brute(w, cache, softcap=0.0):
     d, B = w.head_size, w.block_size
     H = sylvester(d).astype(np.float64)
     sg = w.signs.numpy().astype(np.float64)
@@ -66,6 +66,8 @@ def _numpy_brute(w, cache):
                 pos = L - ql + i
                 for g in range(h * G, (h + 1) * G):
                     z = w.softmax_scale * (K[: pos + 1] @ q[cu[b] + i, g])
+                    if softcap > 0:
+                        z = softcap * np.tanh(z / softcap)
                     p = np.exp(z - z.max())
                     out[cu[b] + i, g] = (p / p.sum()) @ V[: pos + 1]
     return out
