@@ -125,6 +125,12 @@ int4kv_status_t int4_kv_write(const void* key, int64_t key_token_stride, const v
  *                     common kernel's sliding-window masking.)  On the decode
  *                     path the split-K segments divide the blocks from the
  *                     first one the query sees.
+ *   softcap           c > 0: each score z = softmax_scale * q . k_hat becomes
+ *                     c * tanh(z / c) before the softmax; <= 0: none.
+ *                     ([pr40633] description: the packed read path shares the
+ *                     common kernel's softcap helper.)  Must be finite, with a
+ *                     finite reciprocal when > 0; computed in fp32 from one
+ *                     exp2 per score (absolute error a few 2^-24 of c).
  *   rht_signs         fp32 [head_size], the signs used by int4_kv_write.
  *   num_segments      >= 1.  When > 1 on the decode path, segm_output fp32
  *                     [num_seqs, num_q_heads, num_segments, head_size],
@@ -144,7 +150,8 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
                                      const int32_t* block_table, int32_t block_table_stride,
                                      float softmax_scale, int32_t sliding_window,
-                                     const float* rht_signs, int32_t num_segments,
+                                     float softcap, const float* rht_signs,
+                                     int32_t num_segments,
                                      float* segm_output, float* segm_max, float* segm_expsum,
                                      void* stream);
 
@@ -181,7 +188,7 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
                                  const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                                  int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                  const int32_t* block_table, int32_t block_table_stride,
-                                 float softmax_scale, int32_t sliding_window,
+                                 float softmax_scale, int32_t sliding_window, float softcap,
                                  const float* rht_signs, int32_t num_segments,
                                  float* segm_output, float* segm_max, float* segm_expsum,
                                  void* stream);
@@ -190,7 +197,7 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
  * int4kv_decode_num_segments: the split-K segment count the library's decode
  * kernels run best with for a decode batch (max_seqlen_q == 1) of `num_seqs`
  * sequences whose longest has `max_seqlen_k` keys: enough segments for one
- * workgroup per CU of MI355X, none shorter than 512 keys.  Host only; never
+ * workgroup per CU of MI355X, none shorter than 64 keys.  Host only; never
  * fails (returns >= 1).  The caller sizes the segment buffers of
  * int4_paged_attention / int4_decode_step with it and passes it as
  * num_segments.  (The pages' attention test sizes its segment buffers from a

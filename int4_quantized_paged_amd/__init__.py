@@ -63,12 +63,12 @@ def load_library():
     lib.int4_kv_write.argtypes = [P, i64, P, i64, ctypes.c_int, P, i32, P, i32, i32, i32, i32, P, P]
     lib.int4_kv_write.restype = ctypes.c_int
     lib.int4_paged_attention.argtypes = [P, i64, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P, P,
-                                         i32, i32, i32, P, i32, ctypes.c_float, i32, P, i32, P, P,
-                                         P, P]
+                                         i32, i32, i32, P, i32, ctypes.c_float, i32,
+                                         ctypes.c_float, P, i32, P, P, P, P]
     lib.int4_paged_attention.restype = ctypes.c_int
     lib.int4_decode_step.argtypes = [P, i64, P, i64, P, P, i64, P, ctypes.c_int, P, i32, i32, i32,
-                                     i32, i32, P, P, i32, i32, i32, P, i32, ctypes.c_float, i32, P,
-                                     i32, P, P, P, P]
+                                     i32, i32, P, P, i32, i32, i32, P, i32, ctypes.c_float, i32,
+                                     ctypes.c_float, P, i32, P, P, P, P]
     lib.int4_decode_step.restype = ctypes.c_int
     lib.int4kv_decode_num_segments.argtypes = [i32, i32, i32]
     lib.int4kv_decode_num_segments.restype = i32
@@ -167,9 +167,10 @@ def int4_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: 
                          num_segments: int = 1, segm_output: torch.Tensor | None = None,
                          segm_max: torch.Tensor | None = None,
                          segm_expsum: torch.Tensor | None = None,
-                         sliding_window: int = 0) -> torch.Tensor:
+                         sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
     """Causal attention of ``q`` [Tq, Hq, d] over the packed cache; returns ``out``.
-    ``sliding_window`` W > 0: a query at position pos sees keys [pos - W + 1, pos]."""
+    ``sliding_window`` W > 0: a query at position pos sees keys [pos - W + 1, pos].
+    ``softcap`` c > 0: scores z become c * tanh(z / c) before the softmax."""
     lib = load_library()
     if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
         raise ValueError("q must be [Tq, Hq, d] with contiguous heads")
@@ -190,7 +191,8 @@ def int4_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: 
         _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype), _ptr(kv_cache), nb, bs, hkv, d, hq,
         _ptr(cu_seqlens_q.contiguous()), _ptr(seqused_k.contiguous()), S, int(max_seqlen_q),
         int(max_seqlen_k), _ptr(block_table), block_table.stride(0), float(softmax_scale),
-        int(sliding_window), _ptr(rht_signs.contiguous()), int(num_segments), _ptr(segm_output),
+        int(sliding_window), float(softcap), _ptr(rht_signs.contiguous()), int(num_segments),
+        _ptr(segm_output),
         _ptr(segm_max), _ptr(segm_expsum), _stream(q.device)))
     return out
 
@@ -203,7 +205,7 @@ def int4_decode_step(key_new: torch.Tensor, value_new: torch.Tensor, slot_mappin
                      segm_output: torch.Tensor | None = None,
                      segm_max: torch.Tensor | None = None,
                      segm_expsum: torch.Tensor | None = None,
-                     sliding_window: int = 0) -> torch.Tensor:
+                     sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
     """``int4_kv_write`` of one new token per sequence (``key_new``/``value_new``
     [S, Hkv, d], token b is sequence b's last key, at ``slot_mapping[b]``), then
     ``int4_paged_attention``; one launch on the decode path.  Returns ``out``."""
@@ -239,7 +241,7 @@ def int4_decode_step(key_new: torch.Tensor, value_new: torch.Tensor, slot_mappin
         _ptr(slot_mapping.contiguous()), _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype),
         _ptr(kv_cache), nb, bs, hkv, d, hq, _ptr(cu_seqlens_q.contiguous()),
         _ptr(seqused_k.contiguous()), S, int(max_seqlen_q), int(max_seqlen_k), _ptr(block_table),
-        block_table.stride(0), float(softmax_scale), int(sliding_window),
+        block_table.stride(0), float(softmax_scale), int(sliding_window), float(softcap),
         _ptr(rht_signs.contiguous()), int(num_segments), _ptr(segm_output), _ptr(segm_max),
         _ptr(segm_expsum), _stream(q.device)))
     return out

@@ -27,10 +27,13 @@ int4kv_status_t ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Split-count heuristic of the decode path: enough segments that the grid has
-// a workgroup per CU (256 on MI355X), but no segment shorter than 16 tiles of
-// 32 keys, below which the copy ring's fill and drain dominate a workgroup.
+// a workgroup per CU (256 on MI355X), but no segment shorter than 2 tiles of
+// 32 keys.  Large batches are limited by the first rule (the long-context and
+// Llama-3-shaped decodes get 64 and 4 segments, the fastest measured); short
+// batches with few workgroups by the second: 8 sequences of up to 909 keys
+// took 36.5 us at 1 segment, 15 us at 8 and 14 us at 16.
 constexpr int64_t kDecodeTargetWorkgroups = 256;
-constexpr int64_t kDecodeMinTilesPerSegment = 16;
+constexpr int64_t kDecodeMinTilesPerSegment = 2;
 
 int4kv_status_t check_common(const void* cache, int32_t num_blocks, int32_t block_size,
                              int32_t num_kv_heads, int32_t head_size, const float* signs) {
@@ -70,7 +73,7 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                 const int32_t* block_table, int32_t block_table_stride,
                                 int32_t block_size, float softmax_scale, int32_t sliding_window,
-                                const float* rht_signs, int32_t num_segments,
+                                float softcap, const float* rht_signs, int32_t num_segments,
                                 float* segm_output, float* segm_max, float* segm_expsum,
                                 int4kv::AttnArgs& a) {
   if (!q || !out || !cu_seqlens_q || !seqused_k || !block_table)
@@ -92,6 +95,10 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
   if (num_segments < 1) return fail(INT4KV_ERR_INVALID_ARG, "num_segments %d < 1", num_segments);
   if (!std::isfinite(softmax_scale))
     return fail(INT4KV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (std::isnan(softcap) || std::isinf(softcap) ||
+      (softcap > 0.f && !std::isfinite(1.0f / (softcap * 1.4426950408889634f))))
+    return fail(INT4KV_ERR_INVALID_ARG, "softcap must be finite, and > 0 only with a finite "
+                "reciprocal");
   const bool decode = max_seqlen_q == 1;
   if (decode && num_segments > 1 && (!segm_output || !segm_max || !segm_expsum))
     return fail(INT4KV_ERR_WORKSPACE, "num_segments %d > 1 needs the three segment buffers",
@@ -104,6 +111,7 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
                        max_seqlen_k, block_table, block_table_stride, softmax_scale, rht_signs,
                        decode ? num_segments : 1, segm_output, segm_max, segm_expsum};
   a.window = sliding_window > 0 ? sliding_window : 0;
+  a.softcap = softcap > 0.f ? softcap : 0.f;
   return INT4KV_OK;
 }
 
@@ -182,7 +190,8 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
                                      const int32_t* block_table, int32_t block_table_stride,
                                      float softmax_scale, int32_t sliding_window,
-                                     const float* rht_signs, int32_t num_segments,
+                                     float softcap, const float* rht_signs,
+                                     int32_t num_segments,
                                      float* segm_output, float* segm_max, float* segm_expsum,
                                      void* stream) {
   int4kv_status_t s =
@@ -197,7 +206,7 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
   s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
                       num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
                       block_table, block_table_stride, block_size, softmax_scale, sliding_window,
-                      rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
+                      softcap, rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
   if (s != INT4KV_OK) return s;
   const bool decode = max_seqlen_q == 1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -216,7 +225,7 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
                                  const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                                  int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                  const int32_t* block_table, int32_t block_table_stride,
-                                 float softmax_scale, int32_t sliding_window,
+                                 float softmax_scale, int32_t sliding_window, float softcap,
                                  const float* rht_signs, int32_t num_segments,
                                  float* segm_output, float* segm_max, float* segm_expsum,
                                  void* stream) {
@@ -244,7 +253,7 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
   s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
                       num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
                       block_table, block_table_stride, block_size, softmax_scale, sliding_window,
-                      rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
+                      softcap, rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
   if (s != INT4KV_OK) return s;
   hipError_t e;
   if (max_seqlen_q == 1 && int4kv::decode_lds_supported(a)) {

@@ -120,7 +120,8 @@ __global__ __launch_bounds__(512) void decode_kernel(
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
     const float* __restrict__ signs, int32_t num_segments, float* __restrict__ segm_out,
-    float* __restrict__ segm_max, float* __restrict__ segm_sum, int32_t window) {
+    float* __restrict__ segm_max, float* __restrict__ segm_sum, int32_t window, float cap2,
+    float inv_cap2) {
   constexpr int NCH = D / 32;
   constexpr int NCOL = D / 16;
   constexpr int R = D / 2 + 4;
@@ -296,7 +297,9 @@ __global__ __launch_bounds__(512) void decode_kernel(
   #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const float t = sacc[n][v] - zK[n] * qsum[v];
-          z[n] = kval[n] ? t * (sK[n] * c0[v]) : -INFINITY;
+          float zz = t * (sK[n] * c0[v]);
+          if (cap2 > 0.f) zz = soft_cap(zz, cap2, inv_cap2);  // uniform
+          z[n] = kval[n] ? zz : -INFINITY;
         }
         float tmax = fmaxf(z[0], z[1]);
         tmax = fmaxf(tmax, shfl_xor<1>(tmax));
@@ -592,11 +595,13 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(ns, a.num_seqs, hkv / hpw), block(64 * hpw);
   const size_t lds = (size_t)hpw * lds_per_wave;
   const float scale_log2 = a.softmax_scale * kLog2e / (float)D;
+  const float cap2 = a.softcap > 0.f ? a.softcap * kLog2e : 0.f;  // base-2 units
   hipLaunchKernelGGL((decode_kernel<BF16, D, G>), grid, block, lds, stream,
                      reinterpret_cast<const uint16_t*>(a.q), a.q_stride,
                      reinterpret_cast<uint16_t*>(a.out), a.cache, hkv, a.num_q_heads,
                      a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs,
-                     ns, a.segm_out, a.segm_max, a.segm_sum, a.window);
+                     ns, a.segm_out, a.segm_max, a.segm_sum, a.window, cap2,
+                     cap2 > 0.f ? 1.0f / cap2 : 0.f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   return launch_reduce(a, stream);

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     float* __restrict__ segm_max, float* __restrict__ segm_sum,
     const uint16_t* __restrict__ key_new, int64_t key_new_stride,
     const uint16_t* __restrict__ value_new, int64_t value_new_stride,
-    const int64_t* __restrict__ slot_new, int32_t window) {
+    const int64_t* __restrict__ slot_new, int32_t window, float cap2, float inv_cap2) {
   using GG = Geo<D, HPW>;
   using WG = WGeo<G>;
   constexpr uint32_t R = GG::R;
@@ -563,8 +563,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         const float sf = fmaf((float)acc[n][2][v], 65536.0f,
                               (float)((acc[n][1][v] << 8) + acc[n][0][v]));
         const float tt = fmaf(-zK, qsf[v], sf);  // sum_i q_i (code_i - zp)
+        float zz = tt * (sK * c0[v]);
+        if (cap2 > 0.f) zz = soft_cap(zz, cap2, inv_cap2);  // uniform
         // masked keys become -inf through a bitwise select (never a branch)
-        z[v][n] = as_float(and_or(as_uint(tt * (sK * c0[v])), keep, ninf));
+        z[v][n] = as_float(and_or(as_uint(zz), keep, ninf));
       }
     }
     phase_end(0, kb, nxt);
@@ -762,13 +764,14 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
   }
   dim3 grid(a.num_segments, a.num_seqs, a.num_kv_heads / HPW), block(64 * HPW);
   const float scale_log2 = a.softmax_scale * kLog2e / (float)D;
+  const float cap2 = a.softcap > 0.f ? a.softcap * kLog2e : 0.f;  // base-2 units
   hipLaunchKernelGGL(kern, grid, block, lds, stream, reinterpret_cast<const uint16_t*>(a.q),
                      a.q_stride, reinterpret_cast<uint16_t*>(a.out), a.cache, a.num_kv_heads,
                      a.num_q_heads, a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride,
                      scale_log2, a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum,
                      reinterpret_cast<const uint16_t*>(a.key_new), a.key_new_stride,
                      reinterpret_cast<const uint16_t*>(a.value_new), a.value_new_stride,
-                     a.slot_new, a.window);
+                     a.slot_new, a.window, cap2, cap2 > 0.f ? 1.0f / cap2 : 0.f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_segments == 1) return e;
   return launch_reduce(a, stream);

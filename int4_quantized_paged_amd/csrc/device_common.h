@@ -94,6 +94,16 @@ __device__ __forceinline__ uint32_t nib_pair_f16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Logit soft cap in base-2 logit units: c * tanh(x / c), given c and 1 / c
+// (c > 0).  tanh(a) = 1 - 2 / (e^{2a} + 1) from one exp2 and one reciprocal;
+// large |x| gives exactly +-c, and the absolute error is a few 2^-24 of c.
+__device__ __forceinline__ float soft_cap(float x, float c, float inv_c) {
+  const float a = fabsf(x) * inv_c;
+  const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);  // e^(2a)
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return copysignf(c * t, x);
+}
+
 // A value the compiler cannot trace back to the expression that made it.
 // The f16 hi + lo split of a softmax weight w = p * s needs lo computed
 // against the hi that is stored.  Left visible, hi = f16(p * s) may be formed

@@ -32,6 +32,9 @@ struct AttnArgs {
   // sliding window: the query at position pos sees keys [pos - window + 1,
   // pos]; <= 0 is no window
   int32_t window = 0;
+  // logit soft cap c (natural-log units): scores z become c * tanh(z / c)
+  // before the softmax; <= 0 is none
+  float softcap = 0.f;
   // fused decode step only: the new token of each sequence (token b belongs to
   // sequence b and is its last key), encoded into the cache by the workgroup
   // that reads its block; null otherwise

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
-    const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq, int32_t window) {
+    const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq, int32_t window,
+    float cap2, float inv_cap2) {
   using PG = PGeo<D, G>;
   constexpr int R = PG::R, RW = PG::RW, DW = PG::DW, NIB = PG::NIB;
   constexpr int NCH = D / 32;   // f16 MFMA k-chunks of the score
@@ -379,6 +380,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     // which is detected per logit against thr = m + kLazy; the row maxima are
     // only reduced on the rare tiles where that happens
     float z[2][4][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) z[i][v][n] = fmaf(-zK[n], qsum[i][v], sacc[i][n][v]) * sKc[n];
+    if (cap2 > 0.f) {  // uniform: soft cap before the mask, so masked keys stay -inf
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) z[i][v][n] = soft_cap(z[i][v][n], cap2, inv_cap2);
+    }
     bool over = false;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -386,7 +401,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          float zz = fmaf(-zK[n], qsum[i][v], sacc[i][n][v]) * sKc[n];
+          float zz = z[i][v][n];
           if (masked) {
             const int key = 32 * t + 16 * n + col;
             zz = (key <= pos[i][v] && (window <= 0 || key > pos[i][v] - window)) ? zz : -INFINITY;
@@ -575,11 +590,12 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t nwg = (groups + 7) / 8 * 8 * a.num_kv_heads;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float scale_log2 = a.softmax_scale * kLog2e / (float)D;
+  const float cap2 = a.softcap > 0.f ? a.softcap * kLog2e : 0.f;  // base-2 units
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(512), PG::TOTAL, stream,
                      reinterpret_cast<const uint16_t*>(a.q), a.q_stride,
                      reinterpret_cast<uint16_t*>(a.out), a.cache, a.num_kv_heads, a.num_q_heads,
                      a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs,
-                     a.num_seqs, tiles_per_seq, a.window);
+                     a.num_seqs, tiles_per_seq, a.window, cap2, cap2 > 0.f ? 1.0f / cap2 : 0.f);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ def oracle_cache(orc, w, which="all", fill=SENTINEL, token_subset=None):
     return cache
 
 
-def gpu_attention(w, t, cache, num_segments=1, query=None, window=0):
+def gpu_attention(w, t, cache, num_segments=1, query=None, window=0, softcap=0.0):
     q = t["query"] if query is None else query
     segs = (None, None, None)
     if num_segments > 1 and w.max_seqlen_q == 1:
@@ -61,13 +61,14 @@ def gpu_attention(w, t, cache, num_segments=1, query=None, window=0):
     return ik.int4_paged_attention(q, cache, t["cu"], t["su"], w.max_seqlen_q, w.max_seqlen_k,
                                    t["block_table"], w.softmax_scale, t["signs"],
                                    num_segments=num_segments, segm_output=segs[0],
-                                   segm_max=segs[1], segm_expsum=segs[2], sliding_window=window)
+                                   segm_max=segs[1], segm_expsum=segs[2], sliding_window=window,
+                                   softcap=softcap)
 
 
-def oracle_attention(orc, w, cache, window=0):
+def oracle_attention(orc, w, cache, window=0, softcap=0.0):
     return orc.attention_plain(wl.bits16(w.query), dt_name(w), cache, w.cu_seqlens_q().numpy(),
                                w.seqused_k().numpy(), w.block_table.numpy(), w.softmax_scale,
-                               w.signs.numpy(), w.num_q_heads, window=window)
+                               w.signs.numpy(), w.num_q_heads, window=window, softcap=softcap)
 
 
 def assert_attention_close(got, ref, what=""):

@@ -87,20 +87,22 @@ def test_write_zero_tokens_is_a_no_op():
 def _attn(**kw):
     a = dict(q=FAKE, qs=4096, out=FAKE, dtype=1, cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32,
              cu=FAKE, su=FAKE, S=4, mq=1, mk=1024, bt=FAKE, bts=64, scale=0.088, win=0,
-             signs=FAKE, ns=1, so=None, sm=None, ss=None, stream=None)
+             cap=0.0, signs=FAKE, ns=1, so=None, sm=None, ss=None, stream=None)
     a.update(kw)
     lib = ik.load_library()
     return lib.int4_paged_attention(a["q"], a["qs"], a["out"], a["dtype"], a["cache"], a["nb"],
                                     a["bs"], a["hkv"], a["d"], a["hq"], a["cu"], a["su"], a["S"],
                                     a["mq"], a["mk"], a["bt"], a["bts"], a["scale"], a["win"],
-                                    a["signs"], a["ns"], a["so"], a["sm"], a["ss"], a["stream"])
+                                    a["cap"], a["signs"], a["ns"], a["so"], a["sm"], a["ss"],
+                                    a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hq=30), 1), (dict(hq=24, hkv=8), 2), (dict(hq=256, hkv=8, qs=32768), 2),
     (dict(d=80), 2), (dict(bs=8), 2), (dict(ns=0), 1), (dict(ns=16), 3), (dict(bts=10), 1),
     (dict(qs=100), 1), (dict(out=None), 1), (dict(scale=float("inf")), 1), (dict(S=-1), 1),
-    (dict(cache=FAKE + 4), 1),
+    (dict(cache=FAKE + 4), 1), (dict(cap=float("nan")), 1), (dict(cap=float("inf")), 1),
+    (dict(cap=1e-45), 1),
 ])
 def test_attention_rejects_invalid_host_arguments(kw, status):
     assert _attn(**kw) == status
@@ -115,14 +117,14 @@ def test_attention_empty_batch_is_a_no_op():
 def _step(**kw):
     a = dict(kn=FAKE, ks=1024, vn=FAKE, vs=1024, slots=FAKE, q=FAKE, qs=4096, out=FAKE, dtype=1,
              cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32, cu=FAKE, su=FAKE, S=4, mq=1, mk=1024,
-             bt=FAKE, bts=64, scale=0.088, win=0, signs=FAKE, ns=1, so=None, sm=None, ss=None,
-             stream=None)
+             bt=FAKE, bts=64, scale=0.088, win=0, cap=0.0, signs=FAKE, ns=1, so=None, sm=None,
+             ss=None, stream=None)
     a.update(kw)
     lib = ik.load_library()
     return lib.int4_decode_step(a["kn"], a["ks"], a["vn"], a["vs"], a["slots"], a["q"], a["qs"],
                                 a["out"], a["dtype"], a["cache"], a["nb"], a["bs"], a["hkv"],
                                 a["d"], a["hq"], a["cu"], a["su"], a["S"], a["mq"], a["mk"],
-                                a["bt"], a["bts"], a["scale"], a["win"], a["signs"], a["ns"],
+                                a["bt"], a["bts"], a["scale"], a["win"], a["cap"], a["signs"], a["ns"],
                                 a["so"], a["sm"], a["ss"], a["stream"])
 
 
@@ -144,16 +146,17 @@ def test_decode_step_empty_batch_is_a_no_op():
 @pytest.mark.parametrize("S,hkv,L,ns", [
     (4, 8, 131072, 64),  # long-context decode: one workgroup per CU
     (64, 8, 4096, 4),    # Llama-3-8B-shaped decode: 256 workgroups
-    (1, 8, 100, 1),      # shorter than one minimum segment
-    (8, 8, 1024, 2),     # capped by the 16-tile minimum segment
+    (1, 8, 40, 1),       # shorter than two minimum segments
+    (1, 8, 100, 2),      # capped by the 2-tile minimum segment
+    (8, 8, 1024, 16),    # GQA decode: capped by the minimum segment
     (32, 3, 5000, 3),    # register-path head count (one head per workgroup)
     (2, 16, 65536, 64),  # two workgroups per segment index
     (1, 1, 10 ** 7, 256),
 ])
 def test_decode_num_segments_heuristic(S, hkv, L, ns):
-    """Enough segments for one workgroup per CU, none shorter than 16 tiles of
-    32 keys, at most 256; the two benchmark shapes get the split counts that
-    measured fastest (64 and 4)."""
+    """Enough segments for one workgroup per CU, none shorter than 2 tiles of
+    32 keys, at most 256; the two large benchmark shapes get the split counts
+    that measured fastest (64 and 4)."""
     assert ik.int4kv_decode_num_segments(S, hkv, L) == ns
 
 
