@@ -6,9 +6,10 @@
  * validates its host-side arguments first and returns a status without
  * enqueuing anything when they are invalid; on success the work is enqueued on
  * `stream` and the call returns at once (no synchronisation).  The library
- * allocates no memory and keeps no global mutable state apart from a
- * thread-local error string, so it is re-entrant; buffers are owned by the
- * caller.  Device-resident metadata (slot numbers, block ids, lengths) is the
+ * allocates no device memory and keeps no global mutable state apart from a
+ * thread-local error string and a lock-protected record of the (kernel,
+ * device) pairs whose LDS limit it has raised, so it is re-entrant; buffers
+ * are owned by the caller.  Device-resident metadata (slot numbers, block ids, lengths) is the
  * caller's contract and is not checked: out-of-range values there are
  * undefined behaviour.
  *

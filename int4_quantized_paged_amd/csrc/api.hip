@@ -3,6 +3,9 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "../../include/int4kv.h"
 #include "launch.h"
@@ -116,6 +119,27 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
 }
 
 }  // namespace
+
+namespace int4kv {
+
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> raised;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (raised.count({kernel, dev})) return hipSuccess;
+  }
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  raised.insert({kernel, dev});
+  return hipSuccess;
+}
+
+}  // namespace int4kv
 
 extern "C" {
 

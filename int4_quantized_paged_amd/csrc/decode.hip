@@ -585,6 +585,80 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e] * signs[lane * EPL + e] / (float)D);
 }
 
+// Segment reduction for few segments (at most kSmallSegments): one wave per
+// (sequence, query head), four per workgroup.  All of a row's partials are
+// loaded at once and merged in registers in segment order (the same
+// log-sum-exp as above), then rotated back; no LDS and no barrier, which is
+// what a launch of thousands of short rows is bound by.
+constexpr int kSmallSegments = 16;
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void reduce_small_kernel(
+    uint16_t* __restrict__ out, int32_t num_q_heads, int32_t num_rows,
+    const int32_t* __restrict__ cu_seqlens_q, const float* __restrict__ signs,
+    int32_t num_segments, const float* __restrict__ segm_out, const float* __restrict__ segm_max,
+    const float* __restrict__ segm_sum) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= num_rows) return;  // uniform over the wave; nothing below synchronises waves
+  const int b = row / num_q_heads, qg = row % num_q_heads;
+  const int q0 = cu_seqlens_q[b];
+  if (cu_seqlens_q[b + 1] - q0 <= 0) return;
+  const int64_t base = (int64_t)row * num_segments;
+  float mk[kSmallSegments], lk[kSmallSegments], src[kSmallSegments][EPL];
+#pragma unroll
+  for (int j = 0; j < kSmallSegments; ++j) {
+    const bool ok = j < num_segments;
+    const int64_t k = base + (ok ? j : num_segments - 1);  // always a valid address
+    const float m = segm_max[k], l = segm_sum[k];
+    mk[j] = ok ? m : -INFINITY;
+    lk[j] = ok ? l : 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) src[j][e] = segm_out[k * D + lane * EPL + e];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kSmallSegments; ++j) M = fmaxf(M, mk[j]);
+  float Lsum = 0.f, o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  if (M != -INFINITY) {  // uniform over the wave
+#pragma unroll
+    for (int j = 0; j < kSmallSegments; ++j) {
+      const float f = mk[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[j] - M);
+      Lsum = fmaf(lk[j], f, Lsum);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(src[j][e], f, o[e]);
+    }
+  }
+  const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] *= inv;
+#pragma unroll
+  for (int span = 1; span < EPL; span <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      if (e & span) continue;
+      const float x = o[e], y = o[e + span];
+      o[e] = x + y;
+      o[e + span] = x - y;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float p = shfl_xor_rt(o[e], m);
+      o[e] = upper ? p - o[e] : o[e] + p;
+    }
+  }
+  uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e] * signs[lane * EPL + e] / (float)D);
+}
+
 template <bool BF16, int D, int G>
 hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
   const int hkv = a.num_kv_heads;
@@ -609,6 +683,13 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
 
 template <bool BF16, int D>
 hipError_t launch_reduce_t(const AttnArgs& a, hipStream_t stream) {
+  if (a.num_segments <= kSmallSegments) {
+    const int rows = a.num_seqs * a.num_q_heads;
+    hipLaunchKernelGGL((reduce_small_kernel<BF16, D>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+                       reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, rows, a.cu_seqlens_q,
+                       a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((reduce_kernel<BF16, D>), dim3(a.num_seqs * a.num_q_heads), dim3(256), 0,
                      stream, reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, a.cu_seqlens_q,
                      a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum);

@@ -758,8 +758,7 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
   static_assert((Lay<D, G, HPW>::S - 2) * Geo<D, HPW>::NI <= 63, "vmcnt range");
   auto kern = decode_lds_kernel<BF16, D, G, HPW>;
   if (lds > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per CU)
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid(a.num_segments, a.num_seqs, a.num_kv_heads / HPW), block(64 * HPW);

@@ -45,6 +45,11 @@ struct AttnArgs {
   const int64_t* slot_new = nullptr;
 };
 
+// Raises a kernel's dynamic LDS limit above the 64 KiB default, once per
+// (kernel, device): the attribute call is a runtime round trip that a
+// launch repeated every decode step should not pay each time.
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream);
 bool decode_lds_supported(const AttnArgs& a);

@@ -581,8 +581,7 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   static_assert(PG::TOTAL <= 160 * 1024, "LDS of a gfx950 CU");
   auto kern = prefill_kernel<BF16, D, G>;
   if (PG::TOTAL > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)PG::TOTAL);
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)PG::TOTAL);
     if (e != hipSuccess) return e;
   }
   const int tiles_per_seq = (a.max_seqlen_q + PG::TQ - 1) / PG::TQ;
