@@ -460,7 +460,7 @@ def main():
         "write_tokens_per_s": round(wr_tps, 1),
         "write_bulk": {"tokens": wr_T, "seconds": wr_t,
                        "GB_per_s": round(w.write_bytes("all") / wr_t / 1e9, 1)},
-        "roofline": {"kernel": "decode_lds_kernel + reduce_kernel (one int4_paged_attention call)",
+        "roofline": {"kernel": "decode_lds_kernel + reduce_wave_kernel (one int4_paged_attention call)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kv_bytes,

@@ -585,15 +585,19 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e] * signs[lane * EPL + e] / (float)D);
 }
 
-// Segment reduction for few segments (at most kSmallSegments): one wave per
-// (sequence, query head), four per workgroup.  All of a row's partials are
-// loaded at once and merged in registers in segment order (the same
-// log-sum-exp as above), then rotated back; no LDS and no barrier, which is
-// what a launch of thousands of short rows is bound by.
-constexpr int kSmallSegments = 16;
+// Segment reduction for up to 64 segments: one wave per (sequence, query
+// head), four per workgroup.  Lane k holds segment k's maximum and exp-sum;
+// all of the row's partial accumulators are loaded at once and merged in
+// registers in segment order (the same log-sum-exp as below), then rotated
+// back; no LDS and no barrier, which is what a launch of many short rows is
+// bound by.
+constexpr int kWaveSegments = 64;
 
-template <bool BF16, int D>
-__global__ __launch_bounds__(256) void reduce_small_kernel(
+// NSB >= num_segments: the accumulators of segments past the last one are
+// loaded from the last one's address (so every load is issued at once,
+// without a branch) and enter with weight 0
+template <bool BF16, int D, int NSB>
+__global__ __launch_bounds__(256) void reduce_wave_kernel(
     uint16_t* __restrict__ out, int32_t num_q_heads, int32_t num_rows,
     const int32_t* __restrict__ cu_seqlens_q, const float* __restrict__ signs,
     int32_t num_segments, const float* __restrict__ segm_out, const float* __restrict__ segm_max,
@@ -606,31 +610,33 @@ __global__ __launch_bounds__(256) void reduce_small_kernel(
   const int q0 = cu_seqlens_q[b];
   if (cu_seqlens_q[b + 1] - q0 <= 0) return;
   const int64_t base = (int64_t)row * num_segments;
-  float mk[kSmallSegments], lk[kSmallSegments], src[kSmallSegments][EPL];
+  const int ns = num_segments;  // 2 .. NSB
+  float src[NSB][EPL];
 #pragma unroll
-  for (int j = 0; j < kSmallSegments; ++j) {
-    const bool ok = j < num_segments;
-    const int64_t k = base + (ok ? j : num_segments - 1);  // always a valid address
-    const float m = segm_max[k], l = segm_sum[k];
-    mk[j] = ok ? m : -INFINITY;
-    lk[j] = ok ? l : 0.f;
+  for (int k = 0; k < NSB; ++k) {
+    const int64_t kk = base + min(k, ns - 1);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) src[j][e] = segm_out[k * D + lane * EPL + e];
+    for (int e = 0; e < EPL; ++e) src[k][e] = segm_out[kk * D + lane * EPL + e];
   }
-  float M = -INFINITY;
+  const int64_t kl = base + min(lane, ns - 1);
+  const float m_ld = segm_max[kl], l_ld = segm_sum[kl];
+  const float mk = lane < ns ? m_ld : -INFINITY;  // weight 0 past the last segment
+  const float lk = lane < ns ? l_ld : 0.f;
+  float M = mk;
 #pragma unroll
-  for (int j = 0; j < kSmallSegments; ++j) M = fmaxf(M, mk[j]);
-  float Lsum = 0.f, o[EPL];
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor_rt(M, m));
+  const float f = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+  float Lsum = f * lk;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) Lsum += shfl_xor_rt(Lsum, m);
+  float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  if (M != -INFINITY) {  // uniform over the wave
 #pragma unroll
-    for (int j = 0; j < kSmallSegments; ++j) {
-      const float f = mk[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[j] - M);
-      Lsum = fmaf(lk[j], f, Lsum);
+  for (int k = 0; k < NSB; ++k) {
+    const float fk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), k));
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(src[j][e], f, o[e]);
-    }
+    for (int e = 0; e < EPL; ++e) o[e] = fmaf(src[k][e], fk, o[e]);
   }
   const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
 #pragma unroll
@@ -683,9 +689,11 @@ hipError_t launch_decode_t(const AttnArgs& a, hipStream_t stream) {
 
 template <bool BF16, int D>
 hipError_t launch_reduce_t(const AttnArgs& a, hipStream_t stream) {
-  if (a.num_segments <= kSmallSegments) {
+  if (a.num_segments <= kWaveSegments) {
     const int rows = a.num_seqs * a.num_q_heads;
-    hipLaunchKernelGGL((reduce_small_kernel<BF16, D>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+    auto kern = a.num_segments <= 16 ? reduce_wave_kernel<BF16, D, 16>
+                                     : reduce_wave_kernel<BF16, D, kWaveSegments>;
+    hipLaunchKernelGGL(kern, dim3((rows + 3) / 4), dim3(256), 0, stream,
                        reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, rows, a.cu_seqlens_q,
                        a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum);
     return hipGetLastError();
