@@ -1,4 +1,4 @@
-"""CPU oracle for the INT4 per-token-head paged KV cache: TEST INFRASTRUCTURE.
+"""CPU oracle for the INT4 (and INT8) per-token-head paged KV cache: TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg
 may import this package.  The product path (``int4_quantized_paged_amd``) never
@@ -51,6 +51,11 @@ def _load():
                                            P, P, i32, P, i32, f64, P, i32, f64, P]
     lib.oracle_attention_method.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i32,
                                             P, P, i32, P, i32, f64, P, i32, i32, f64, P]
+    lib.oracle_quantize_row_int8.argtypes = [P, i32, P, P]
+    lib.oracle_kv_write_int8.argtypes = [P, i64, P, i64, i32, P, i32, P, i32, i32, i32, i32]
+    lib.oracle_decode_row_int8.argtypes = [P, i32, P]
+    lib.oracle_attention_plain_int8.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i32,
+                                                P, P, i32, P, i32, f64, i32, f64, P]
     _lib = lib
     return lib
 
@@ -204,4 +209,63 @@ def attention_method(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table,
                                     bt.shape[1], float(softmax_scale),
                                     _p(_c(signs, np.float32)), int(num_segments),
                                     int(window), float(softcap), _p(out))
+    return out
+
+
+# ---- INT8 per-token-head mode: rows of d int8 codes + an fp32 scale, no rotation
+
+
+def cache_shape_int8(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int):
+    return (num_blocks, 2, block_size, num_kv_heads, head_size + 4)
+
+
+def quantize_row_int8(x: np.ndarray) -> tuple[np.ndarray, float]:
+    """Quantize one fp32 row: (int8 codes, fp32 scale)."""
+    x = _c(x, np.float32)
+    codes = np.zeros(x.size, dtype=np.int8)
+    s = np.zeros(1, dtype=np.float32)
+    _load().oracle_quantize_row_int8(_p(x), x.size, _p(codes), _p(s))
+    return codes, float(s[0])
+
+
+def kv_write_int8(key_bits: np.ndarray, value_bits: np.ndarray, dtype: str,
+                  slot_mapping: np.ndarray, cache: np.ndarray) -> None:
+    """Write tokens into ``cache`` (uint8 [NB, 2, B, Hkv, d+4]) in place."""
+    assert cache.dtype == np.uint8 and cache.flags.c_contiguous and cache.ndim == 5
+    nb, two, bs, hkv, r = cache.shape
+    k = _c(key_bits, np.uint16)
+    v = _c(value_bits, np.uint16)
+    T, hk, d = k.shape
+    assert two == 2 and hk == hkv and r == d + 4 and v.shape == k.shape
+    sm = _c(slot_mapping, np.int64)
+    assert sm.shape == (T,)
+    _load().oracle_kv_write_int8(_p(k), hkv * d, _p(v), hkv * d, _DT[dtype], _p(sm), T,
+                                 _p(cache), nb, bs, hkv, d)
+
+
+def decode_row_int8(row: np.ndarray, head_size: int) -> np.ndarray:
+    row = _c(row, np.uint8)
+    out = np.zeros(head_size, np.float64)
+    _load().oracle_decode_row_int8(_p(row), head_size, _p(out))
+    return out
+
+
+def attention_plain_int8(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table,
+                         softmax_scale, num_q_heads, window: int = 0,
+                         softcap: float = 0.0) -> np.ndarray:
+    """Causal softmax attention over the dequantised INT8 cache, fp64 [Tq, Hq, d]."""
+    q = _c(q_bits, np.uint16)
+    nb, two, bs, hkv, r = cache.shape
+    d = r - 4
+    Tq = q.shape[0]
+    assert q.shape == (Tq, num_q_heads, d)
+    cu = _c(cu_seqlens_q, np.int32)
+    su = _c(seqused_k, np.int32)
+    bt = _c(block_table, np.int32)
+    out = np.zeros((Tq, num_q_heads, d), np.float64)
+    cache = _c(cache, np.uint8)
+    _load().oracle_attention_plain_int8(_p(q), num_q_heads * d, _DT[dtype], _p(cache), nb, bs,
+                                        hkv, d, num_q_heads, _p(cu), _p(su), su.shape[0],
+                                        _p(bt), bt.shape[1], float(softmax_scale), int(window),
+                                        float(softcap), _p(out))
     return out

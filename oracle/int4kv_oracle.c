@@ -466,3 +466,160 @@ void oracle_attention_method(const uint16_t* q, int64_t q_stride, int dtype,
   free(seg_m);
   free(seg_l);
 }
+
+/* ==========================================================================
+ * INT8 per-token-head mode (the sibling mode on the same cache family).
+ *
+ * Readings (listed with the INT4 ones in the design notes):
+ *   R8-layout cache uint8 [num_blocks][2][block_size][num_kv_heads][d + 4]:
+ *             d int8 codes (two's complement bytes), then the fp32 scale,
+ *             little-endian.  ([report] key snippets: get_kv_cache_shape keeps
+ *             data_head_size = head_size for modes other than INT4 and adds a
+ *             scale pad of 4 bytes for a 1-byte cache dtype.)
+ *   R8-quant  no rotation; s = max(fl(absmax / 127), 1e-6f); inv = fl(1 / s);
+ *             v = fl(x * inv).  ([testfile] helpers: per-token-head
+ *             reference quantizer, data * (1.0 / scales), quant_max 127.)
+ *   R8-round  q = trunc(fl(v + 0.5)) for v >= 0, trunc(fl(v - 0.5)) for
+ *             v < 0, then clamped to [-128, 127]: round half away from zero
+ *             the way the INT8 write-kernel fix describes it ([pr40633]
+ *             commit on the INT8 reshape kernel: +0.5 / -0.5, then to int32).
+ *             The test reference's torch.round (half to even) differs only at
+ *             exact .5 ties and where fl(v + 0.5) rounds up to an integer.
+ *   R8-deq    x_hat = q * s.
+ * ========================================================================== */
+
+static int64_t or8_row_offset(int64_t blk, int kv, int64_t off, int h, int block_size,
+                              int num_kv_heads, int d) {
+  int64_t R = d + 4;
+  return (((blk * 2 + kv) * block_size + off) * num_kv_heads + h) * R;
+}
+
+/* Quantizes one row of d fp32 values: d codes and the scale. */
+void oracle_quantize_row_int8(const float* x, int d, int8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < d; ++i) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 127.0f;
+  if (!(s > 1e-6f)) s = 1e-6f; /* clamp(min=1e-6) */
+  float inv = 1.0f / s;
+  for (int i = 0; i < d; ++i) {
+    float v = x[i] * inv;
+    float t = v >= 0.0f ? v + 0.5f : v - 0.5f; /* one rounded fp32 add */
+    long q = (long)t;                          /* C conversion truncates toward zero */
+    if (q < -128) q = -128;
+    if (q > 127) q = 127;
+    codes[i] = (int8_t)q;
+  }
+  *scale = s;
+}
+
+/* The INT8 write: every (token, head, K|V) row with slot >= 0 goes to block
+ * slot / block_size, offset slot % block_size; other rows are untouched. */
+void oracle_kv_write_int8(const uint16_t* key, int64_t key_stride, const uint16_t* value,
+                          int64_t value_stride, int dtype, const int64_t* slot_mapping,
+                          int num_tokens, uint8_t* cache, int num_blocks, int block_size,
+                          int num_kv_heads, int d) {
+  (void)num_blocks;
+  float* x = (float*)malloc(sizeof(float) * (size_t)d);
+  int8_t* codes = (int8_t*)malloc((size_t)d);
+  for (int t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    int64_t blk = slot / block_size, off = slot % block_size;
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = kv == 0 ? key + (int64_t)t * key_stride
+                                    : value + (int64_t)t * value_stride;
+      for (int h = 0; h < num_kv_heads; ++h) {
+        for (int i = 0; i < d; ++i) x[i] = or_load(src + (int64_t)h * d + i, dtype);
+        float s;
+        oracle_quantize_row_int8(x, d, codes, &s);
+        uint8_t* row = cache + or8_row_offset(blk, kv, off, h, block_size, num_kv_heads, d);
+        memcpy(row, codes, (size_t)d);
+        uint32_t w = or_f32_bits(s);
+        row[d + 0] = (uint8_t)(w & 0xFF);
+        row[d + 1] = (uint8_t)((w >> 8) & 0xFF);
+        row[d + 2] = (uint8_t)((w >> 16) & 0xFF);
+        row[d + 3] = (uint8_t)((w >> 24) & 0xFF);
+      }
+    }
+  }
+  free(codes);
+  free(x);
+}
+
+/* Dequantised row x_hat_i = q_i * s (R8-deq), fp64. */
+void oracle_decode_row_int8(const uint8_t* row, int d, double* out) {
+  uint32_t w = (uint32_t)row[d] | ((uint32_t)row[d + 1] << 8) | ((uint32_t)row[d + 2] << 16) |
+               ((uint32_t)row[d + 3] << 24);
+  double s = (double)or_bits_f32(w);
+  for (int i = 0; i < d; ++i) out[i] = (double)(int8_t)row[i] * s;
+}
+
+/* Plain causal softmax attention over the dequantised INT8 cache (fp64), with
+ * the same positions, GQA mapping, window and soft cap as the INT4 oracle
+ * (R-pos, R-gqa, R-win, R-cap). */
+void oracle_attention_plain_int8(const uint16_t* q, int64_t q_stride, int dtype,
+                                 const uint8_t* cache, int num_blocks, int block_size,
+                                 int num_kv_heads, int d, int num_q_heads,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                 int num_seqs, const int32_t* block_table, int bt_stride,
+                                 double softmax_scale, int window, double softcap, double* out) {
+  (void)num_blocks;
+  int G = num_q_heads / num_kv_heads;
+  for (int b = 0; b < num_seqs; ++b) {
+    int q0 = cu_seqlens_q[b], qlen = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+    int64_t L = seqused_k[b];
+    if (qlen <= 0 || L <= 0) continue;
+    for (int h = 0; h < num_kv_heads; ++h) {
+      double* K = (double*)malloc(sizeof(double) * (size_t)(L * d));
+      double* V = (double*)malloc(sizeof(double) * (size_t)(L * d));
+      for (int64_t j = 0; j < L; ++j) {
+        int64_t blk = block_table[(int64_t)b * bt_stride + j / block_size];
+        oracle_decode_row_int8(
+            cache + or8_row_offset(blk, 0, j % block_size, h, block_size, num_kv_heads, d), d,
+            K + j * d);
+        oracle_decode_row_int8(
+            cache + or8_row_offset(blk, 1, j % block_size, h, block_size, num_kv_heads, d), d,
+            V + j * d);
+      }
+      double* z = (double*)malloc(sizeof(double) * (size_t)L);
+      double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+      for (int i = 0; i < qlen; ++i) {
+        int64_t pos = L - qlen + i;
+        for (int gg = 0; gg < G; ++gg) {
+          int g = h * G + gg;
+          const uint16_t* qrow = q + (int64_t)(q0 + i) * q_stride + (int64_t)g * d;
+          for (int k = 0; k < d; ++k) qv[k] = (double)or_load(qrow + k, dtype);
+          double* o = out + ((int64_t)(q0 + i) * num_q_heads + g) * d;
+          for (int k = 0; k < d; ++k) o[k] = 0.0;
+          if (pos < 0) continue;
+          int64_t jlo = 0;
+          if (window > 0 && pos - window + 1 > 0) jlo = pos - window + 1;
+          double zmax = -INFINITY;
+          for (int64_t j = jlo; j <= pos; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += qv[k] * K[j * d + k];
+            z[j] = softmax_scale * acc;
+            if (softcap > 0.0) z[j] = softcap * tanh(z[j] / softcap);
+            if (z[j] > zmax) zmax = z[j];
+          }
+          double den = 0.0;
+          for (int64_t j = jlo; j <= pos; ++j) {
+            z[j] = exp(z[j] - zmax);
+            den += z[j];
+          }
+          for (int64_t j = jlo; j <= pos; ++j) {
+            double w = z[j] / den;
+            for (int k = 0; k < d; ++k) o[k] += w * V[j * d + k];
+          }
+        }
+      }
+      free(qv);
+      free(z);
+      free(K);
+      free(V);
+    }
+  }
+}
