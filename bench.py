@@ -311,6 +311,18 @@ def other_rows(dev):
         "step_64_tokens_us": round(step_write_us, 2),
         "step_64_tokens_timing": "20 writes replayed from one HIP graph, per write"}
     del cache, fill, step_write, g20
+    # the INT8 per-token-head mode's bulk fill of the same tokens (rows of d + 4 bytes)
+    cache8 = ik.empty_cache_int8(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)
+    fill8 = lambda: ik.int8_kv_write(w.key, w.value, slots_all, cache8)  # noqa: E731
+    for _ in range(2):
+        fill8()
+    fill8_us = _median_event_us(fill8, 3)
+    bytes8 = T * w.num_kv_heads * 2 * (2 * w.head_size + (w.head_size + 4)) + 8 * T
+    rows["llama3_8b_write_int8"] = {
+        "workload": "INT8 per-token-head bulk fill of the same 262144 tokens (rows of 132 bytes)",
+        "bulk_us": round(fill8_us, 1), "bulk_tokens_per_s": round(T / fill8_us * 1e6, 1),
+        "bulk_GBps": round(bytes8 / fill8_us / 1e3, 1)}
+    del cache8, fill8
     best = None
     for ns in (1, 2, 4, 8):
         call = _attention_setup(w, dev, ns, ncaches=2)

@@ -206,6 +206,38 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
  */
 int32_t int4kv_decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seqlen_k);
 
+/* ---------------------------------------------------------------------------
+ * INT8 per-token-head mode: the sibling mode on the same cache family
+ * ([report] key snippets: get_kv_cache_shape keeps the data dimension at
+ * head_size for per-token-head modes other than INT4 and adds a 4-byte scale
+ * pad for a 1-byte cache dtype; [pr40633] description and commits: INT8
+ * per-token-head scales, its write kernel rounding to nearest).
+ *
+ * Cache layout: uint8 [num_blocks][2][block_size][num_kv_heads][head_size + 4];
+ * index 0 of dim 1 is K, 1 is V; a row holds head_size int8 codes (two's
+ * complement) and then the fp32 scale, little-endian.  No rotation.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of an INT8 cache of the given shape, or -1 if a dimension is < 1. */
+int64_t int8kv_cache_bytes(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_size);
+
+/*
+ * int8_kv_write: quantize and store K and V of `num_tokens` tokens.
+ * For each token t with slot = slot_mapping[t] >= 0, each KV head, K and V:
+ *   x = input row in fp32; s = max(fl(max |x| / 127), 1e-6f); inv = fl(1 / s);
+ *   q_i = clamp(trunc(fl(fl(x_i * inv) +- 0.5)), -128, 127), the sign of the
+ *   0.5 that of fl(x_i * inv) (round half away from zero: [pr40633] commit on
+ *   the INT8 reshape kernel; the quantizer of the [testfile] per-token-head
+ *   reference: absmax / 127, clamp(min=1e-6), data * (1 / scale)).
+ * Bit-for-bit reproducible.  Arguments as for int4_kv_write (no sign vector).
+ */
+int4kv_status_t int8_kv_write(const void* key, int64_t key_token_stride, const void* value,
+                              int64_t value_token_stride, int4kv_dtype_t dtype,
+                              const int64_t* slot_mapping, int32_t num_tokens, uint8_t* kv_cache,
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_size, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* int4kv_status_string(int4kv_status_t s);
 

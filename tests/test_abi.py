@@ -18,14 +18,15 @@ HDR = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "int4k
 def declared_functions():
     text = open(HDR).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(int4[a-z_0-9]*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(int[48][a-z_0-9]*)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = ik.load_library()
     names = declared_functions()
     assert {"int4_kv_write", "int4_paged_attention", "int4kv_cache_bytes",
-            "int4kv_status_string", "int4kv_last_error"} <= set(names)
+            "int4kv_status_string", "int4kv_last_error", "int8_kv_write",
+            "int8kv_cache_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(ik.library_path())
@@ -46,7 +47,8 @@ def test_cache_bytes_rejects_bad_dims():
 def test_memory_ratio_vs_int8_and_bf16():
     # packed row d/2 + 4 bytes vs d + 4 (int8 per-token-head) and 2d (bf16)
     for d, r8 in [(128, 0.515), (64, 0.529)]:
-        r = ik.int4kv_cache_bytes(1, 16, 1, d) / (2 * 16 * (d + 4))
+        assert ik.int8kv_cache_bytes(1, 16, 1, d) == 2 * 16 * (d + 4)
+        r = ik.int4kv_cache_bytes(1, 16, 1, d) / ik.int8kv_cache_bytes(1, 16, 1, d)
         assert abs(r - r8) < 1e-3
     assert abs(ik.int4kv_cache_bytes(1, 16, 1, 128) / (2 * 16 * 256) - 0.2656) < 1e-3
 
@@ -163,3 +165,26 @@ def test_decode_num_segments_heuristic(S, hkv, L, ns):
 def test_decode_num_segments_degenerate_inputs():
     for args in ((0, 8, 100), (4, 0, 100), (4, 8, 0), (-1, 8, 100)):
         assert ik.int4kv_decode_num_segments(*args) == 1
+
+
+def _w8(**kw):
+    a = dict(k=FAKE, ks=1024, v=FAKE, vs=1024, dtype=1, slots=FAKE, T=4, cache=FAKE, nb=64, bs=16,
+             hkv=8, d=128, stream=None)
+    a.update(kw)
+    return ik.load_library().int8_kv_write(a["k"], a["ks"], a["v"], a["vs"], a["dtype"],
+                                           a["slots"], a["T"], a["cache"], a["nb"], a["bs"],
+                                           a["hkv"], a["d"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), 1), (dict(slots=None), 1), (dict(cache=None), 1), (dict(ks=100), 1),
+    (dict(d=96), 2), (dict(bs=32), 2), (dict(dtype=7), 1), (dict(T=-1), 1),
+    (dict(cache=FAKE + 8), 1), (dict(nb=0), 1),
+])
+def test_int8_write_rejects_invalid_host_arguments(kw, status):
+    assert _w8(**kw) == status
+    assert ik.int4kv_last_error() != ""
+
+
+def test_int8_write_empty_is_a_no_op():
+    assert _w8(T=0) == 0
