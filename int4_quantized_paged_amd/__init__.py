@@ -74,6 +74,10 @@ def load_library():
     lib.int8kv_cache_bytes.restype = i64
     lib.int8_kv_write.argtypes = [P, i64, P, i64, ctypes.c_int, P, i32, P, i32, i32, i32, i32, P]
     lib.int8_kv_write.restype = ctypes.c_int
+    lib.int8_paged_attention.argtypes = [P, i64, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P, P,
+                                         i32, i32, i32, P, i32, ctypes.c_float, i32,
+                                         ctypes.c_float, i32, P, P, P, P]
+    lib.int8_paged_attention.restype = ctypes.c_int
     lib.int4kv_decode_num_segments.argtypes = [i32, i32, i32]
     lib.int4kv_decode_num_segments.restype = i32
     _lib = lib
@@ -175,6 +179,43 @@ def int8_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Te
     _check(lib.int8_kv_write(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
                              _dtype_code(key.dtype), _ptr(slot_mapping.contiguous()), T,
                              _ptr(kv_cache), nb, bs, hkv, key.shape[2], _stream(key.device)))
+
+
+def int8_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         seqused_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                         block_table: torch.Tensor, softmax_scale: float,
+                         out: torch.Tensor | None = None, num_segments: int = 1,
+                         segm_output: torch.Tensor | None = None,
+                         segm_max: torch.Tensor | None = None,
+                         segm_expsum: torch.Tensor | None = None,
+                         sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
+    """Causal decode attention of ``q`` [S, Hq, d] over the INT8 per-token-head cache
+    (uint8 [NB, 2, B, Hkv, d + 4]); returns ``out``."""
+    lib = load_library()
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [Tq, Hq, d] with contiguous heads")
+    Tq, hq, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, hq, d), dtype=q.dtype, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous with q's shape and dtype")
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 5 or kv_cache.shape[4] != d + 4:
+        raise ValueError("kv_cache must be a uint8 [NB, 2, B, Hkv, d+4] tensor")
+    nb, two, bs, hkv, _ = kv_cache.shape
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k),
+                    ("block_table", block_table)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [S, max_blocks] with unit column stride")
+    S = seqused_k.shape[0]
+    _check(lib.int8_paged_attention(
+        _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype), _ptr(kv_cache), nb, bs, hkv, d, hq,
+        _ptr(cu_seqlens_q.contiguous()), _ptr(seqused_k.contiguous()), S, int(max_seqlen_q),
+        int(max_seqlen_k), _ptr(block_table), block_table.stride(0), float(softmax_scale),
+        int(sliding_window), float(softcap), int(num_segments), _ptr(segm_output),
+        _ptr(segm_max), _ptr(segm_expsum), _stream(q.device)))
+    return out
 
 
 def int4_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,

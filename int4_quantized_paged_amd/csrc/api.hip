@@ -240,6 +240,50 @@ int4kv_status_t int8_kv_write(const void* key, int64_t key_token_stride, const v
   return ok();
 }
 
+int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void* out,
+                                     int4kv_dtype_t dtype, const uint8_t* kv_cache,
+                                     int32_t num_blocks, int32_t block_size,
+                                     int32_t num_kv_heads, int32_t head_size,
+                                     int32_t num_q_heads, const int32_t* cu_seqlens_q,
+                                     const int32_t* seqused_k, int32_t num_seqs,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     const int32_t* block_table, int32_t block_table_stride,
+                                     float softmax_scale, int32_t sliding_window, float softcap,
+                                     int32_t num_segments, float* segm_output, float* segm_max,
+                                     float* segm_expsum, void* stream) {
+  if (!kv_cache) return fail(INT4KV_ERR_INVALID_ARG, "null cache pointer");
+  if (num_blocks < 1 || num_kv_heads < 1)
+    return fail(INT4KV_ERR_INVALID_ARG, "num_blocks (%d) and num_kv_heads (%d) must be >= 1",
+                num_blocks, num_kv_heads);
+  if (head_size != 64 && head_size != 128)
+    return fail(INT4KV_ERR_UNSUPPORTED, "head_size %d: supported sizes are 64 and 128", head_size);
+  if (block_size != 16)
+    return fail(INT4KV_ERR_UNSUPPORTED, "block_size %d: only 16 is supported", block_size);
+  if (!aligned16(kv_cache)) return fail(INT4KV_ERR_INVALID_ARG, "cache must be 16-byte aligned");
+  if (dtype != INT4KV_F16 && dtype != INT4KV_BF16)
+    return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
+  if (num_seqs == 0 || max_seqlen_q == 0) return ok();
+  if (max_seqlen_q != 1)
+    return fail(INT4KV_ERR_UNSUPPORTED, "INT8 mode: decode batches only (max_seqlen_q == 1)");
+  if (!(num_kv_heads == 1 || num_kv_heads == 2 || num_kv_heads % 4 == 0))
+    return fail(INT4KV_ERR_UNSUPPORTED, "INT8 mode: num_kv_heads %d must be 1, 2 or a multiple of 4",
+                num_kv_heads);
+  int4kv::AttnArgs a;
+  int4kv_status_t s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads,
+                                      head_size, num_q_heads, cu_seqlens_q, seqused_k, num_seqs,
+                                      max_seqlen_q, max_seqlen_k, block_table, block_table_stride,
+                                      block_size, softmax_scale, sliding_window, softcap, nullptr,
+                                      num_segments, segm_output, segm_max, segm_expsum, a);
+  if (s != INT4KV_OK) return s;
+  a.q8 = true;
+  hipError_t e = int4kv::launch_decode_lds(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void* out,
                                      int4kv_dtype_t dtype, const uint8_t* kv_cache,
                                      int32_t num_blocks, int32_t block_size,

@@ -561,6 +561,12 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     const int d = lane * EPL + e;
     o[e] = ((part[0][d] * f[0] + part[1][d] * f[1]) + (part[2][d] * f[2] + part[3][d] * f[3])) * inv;
   }
+  uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D + lane * EPL;
+  if (signs == nullptr) {  // INT8 rows: the original domain already (uniform)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e]);
+    return;
+  }
 #pragma unroll
   for (int span = 1; span < EPL; span <<= 1) {
 #pragma unroll
@@ -580,7 +586,6 @@ __global__ __launch_bounds__(256) void reduce_kernel(
       o[e] = upper ? p - o[e] : o[e] + p;
     }
   }
-  uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D + lane * EPL;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e] * signs[lane * EPL + e] / (float)D);
 }
@@ -641,6 +646,12 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(
   const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] *= inv;
+  uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D + lane * EPL;
+  if (signs == nullptr) {  // INT8 rows: the original domain already (uniform)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e]);
+    return;
+  }
 #pragma unroll
   for (int span = 1; span < EPL; span <<= 1) {
 #pragma unroll
@@ -660,7 +671,6 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(
       o[e] = upper ? p - o[e] : o[e] + p;
     }
   }
-  uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D + lane * EPL;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) dst[e] = from_f32<BF16>(o[e] * signs[lane * EPL + e] / (float)D);
 }
@@ -695,12 +705,14 @@ hipError_t launch_reduce_t(const AttnArgs& a, hipStream_t stream) {
                                      : reduce_wave_kernel<BF16, D, kWaveSegments>;
     hipLaunchKernelGGL(kern, dim3((rows + 3) / 4), dim3(256), 0, stream,
                        reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, rows, a.cu_seqlens_q,
-                       a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum);
+                       a.q8 ? nullptr : a.signs, a.num_segments, a.segm_out, a.segm_max,
+                       a.segm_sum);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((reduce_kernel<BF16, D>), dim3(a.num_seqs * a.num_q_heads), dim3(256), 0,
                      stream, reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, a.cu_seqlens_q,
-                     a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum);
+                     a.q8 ? nullptr : a.signs, a.num_segments, a.segm_out, a.segm_max,
+                     a.segm_sum);
   return hipGetLastError();
 }
 

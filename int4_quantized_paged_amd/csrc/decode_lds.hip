@@ -95,9 +95,9 @@ __device__ __forceinline__ float max16(float x) {
 }
 
 // Compile-time geometry of the LDS image of one tile (two cache blocks).
-template <int D, int HPW>
+template <int D, int HPW, bool Q8 = false>
 struct Geo {
-  static constexpr uint32_t R = D / 2 + 4;
+  static constexpr uint32_t R = Q8 ? D + 4 : D / 2 + 4;  // row bytes (INT8: d codes + scale)
   static constexpr uint32_t run = HPW * R;                 // bytes of the group's heads per token
   static constexpr bool kTokenRows = run % 16 == 0;        // token runs are whole chunks
   static constexpr uint32_t TS =                           // LDS token stride
@@ -131,9 +131,9 @@ struct WGeo {
 // deepest ring that fits the 160 KiB of a gfx950 CU, at most 6 for a full
 // 8-head workgroup (one per CU) and at most 4 for smaller ones (several per CU
 // share the LDS).
-template <int D, int G, int HPW>
+template <int D, int G, int HPW, bool Q8 = false>
 struct Lay {
-  using GG = Geo<D, HPW>;
+  using GG = Geo<D, HPW, Q8>;
   static constexpr uint32_t qstage = HPW * (G * D * 4 + 2 * G * 4);
   static constexpr uint32_t last = GG::stage > qstage ? GG::stage : qstage;
   static constexpr uint32_t bytes(int s) {
@@ -146,7 +146,7 @@ struct Lay {
   static constexpr uint32_t total = wbase + HPW * WGeo<G>::wtile;
 };
 
-template <bool BF16, int D, int G, int HPW>
+template <bool BF16, int D, int G, int HPW, bool Q8>
 __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, uint16_t* __restrict__ out,
     const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
@@ -157,10 +157,11 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const uint16_t* __restrict__ key_new, int64_t key_new_stride,
     const uint16_t* __restrict__ value_new, int64_t value_new_stride,
     const int64_t* __restrict__ slot_new, int32_t window, float cap2, float inv_cap2) {
-  using GG = Geo<D, HPW>;
+  using GG = Geo<D, HPW, Q8>;
   using WG = WGeo<G>;
+  using LY = Lay<D, G, HPW, Q8>;
   constexpr uint32_t R = GG::R;
-  constexpr int DW = D / 8;      // code dwords per row
+  constexpr int DW = Q8 ? D / 4 : D / 8;  // code dwords per row
   constexpr int DWG = DW / 4;    // code dwords per lane group in the score operand
   constexpr int NCK = D / 64;    // int8 MFMA k-chunks
   constexpr int NCOL = D / 16;   // P.V column tiles
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int EPL = G * D / 64;
   constexpr int LPQ = 64 / G;
   constexpr int NI = GG::NI;
-  constexpr int S = Lay<D, G, HPW>::S;
+  constexpr int S = LY::S;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // barrier at which tile 0 has landed.  The block is read only by this
   // workgroup, through L2.
   bool store_pending = false;  // this wave stored rows whose completion is still to be awaited
-  if (slot_new != nullptr) {
+  if (!Q8 && slot_new != nullptr) {  // (the INT8 mode has no fused step)
     const int64_t slot = slot_new[b];
     if (slot >= 0 && L > 0 && ((L - 1) / kBlockSize - blo) / per == seg) {  // uniform over the workgroup
       constexpr int WE = 16, WLPR = D / WE, WRPW = kWave / WLPR;  // rows of 8 or 4 lanes
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   const uint32_t pair_g = 2 * half_g;  // bytes per cache block (K and V halves)
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
   const int32_t* bt = block_table + (int64_t)b * bt_stride;
-  unsigned char* wt = smem + Lay<D, G, HPW>::wbase + wave * WG::wtile;  // this wave's W tile
+  unsigned char* wt = smem + LY::wbase + wave * WG::wtile;  // this wave's W tile
 
   // ---- per-lane DMA sources (loop invariant).  Instruction i of wave w copies
   // unit u = i*HPW + w < U; units [0, UPB) hold block 0, [UPB, U) block 1; the
@@ -302,32 +303,37 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   };
 
   // ---- prologue: q' = H (signs * q) as fixed point below 2^22, staged in the last stage
-  int32_t* q24 = reinterpret_cast<int32_t*>(smem + Lay<D, G, HPW>::qbase) + wave * G * D;
+  int32_t* q24 = reinterpret_cast<int32_t*>(smem + LY::qbase) + wave * G * D;
   float* qinfo =
-      reinterpret_cast<float*>(smem + Lay<D, G, HPW>::qbase + HPW * G * D * 4) + wave * 2 * G;
+      reinterpret_cast<float*>(smem + LY::qbase + HPW * G * D * 4) + wave * 2 * G;
   {
     const int i = lane / LPQ, s = lane % LPQ;
     const uint16_t* qp = q + (int64_t)q0 * q_stride + (int64_t)(h * G + i) * D + s * EPL;
     float x[EPL];
+    if constexpr (Q8) {  // no rotation: the INT8 rows hold the original domain
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = to_f32<BF16>(qp[e]) * signs[s * EPL + e];
+      for (int e = 0; e < EPL; ++e) x[e] = to_f32<BF16>(qp[e]);
+    } else {
 #pragma unroll
-    for (int span = 1; span < EPL; span <<= 1) {
+      for (int e = 0; e < EPL; ++e) x[e] = to_f32<BF16>(qp[e]) * signs[s * EPL + e];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        if (e & span) continue;
-        const float u = x[e], v = x[e + span];
-        x[e] = u + v;
-        x[e + span] = u - v;
+      for (int span = 1; span < EPL; span <<= 1) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          if (e & span) continue;
+          const float u = x[e], v = x[e + span];
+          x[e] = u + v;
+          x[e + span] = u - v;
+        }
       }
-    }
 #pragma unroll
-    for (int m = 1; m < LPQ; m <<= 1) {
-      const bool upper = (s & m) != 0;
+      for (int m = 1; m < LPQ; m <<= 1) {
+        const bool upper = (s & m) != 0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float p = shfl_xor_rt(x[e], m);
-        x[e] = upper ? p - x[e] : x[e] + p;
+        for (int e = 0; e < EPL; ++e) {
+          const float p = shfl_xor_rt(x[e], m);
+          x[e] = upper ? p - x[e] : x[e] + p;
+        }
       }
     }
     float mx = 0.f;
@@ -371,7 +377,9 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // int8 planes of Q in the score MFMA's A layout.  Lane group g reads its K
   // segment dwords in the rotated order j = (q + g) % DWG (spreads LDS banks);
   // slot (rho, beta) of chunk k then holds element
-  // 8 * (g*DWG + (2k + rho/2 + g) % DWG) + 2*beta + rho%2.
+  // 8 * (g*DWG + (2k + rho/2 + g) % DWG) + 2*beta + rho%2 (INT4: low nibbles are
+  // the even elements), or 4 * (g*DWG + (4k + rho + g) % DWG) + beta (INT8:
+  // byte beta of a dword is its element).
   i32x4_t qa[3][NCK];
   {
     const int r = col, grp = r >> 2, vv = r & 3;
@@ -384,8 +392,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         uint32_t pw[3] = {0u, 0u, 0u};
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta) {
-          const int j = (2 * k + (rho >> 1) + g) % DWG;
-          const int d = 8 * (g * DWG + j) + 2 * beta + (rho & 1);
+          const int j = Q8 ? (4 * k + rho + g) % DWG : (2 * k + (rho >> 1) + g) % DWG;
+          const int d = Q8 ? 4 * (g * DWG + j) + beta : 8 * (g * DWG + j) + 2 * beta + (rho & 1);
           const int v = ok ? q24[qh * D + d] : 0;
           const int p0 = ((v + 128) & 0xFF) - 128, r1 = (v - p0) >> 8;
           const int p1 = ((r1 + 128) & 0xFF) - 128, p2 = (r1 - p1) >> 8;
@@ -423,11 +431,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
   const int noff = (D == 64) ? 4 * (col >> 3) : 0;  // nibble offset of this lane's V dword
   // O (rotated domain, zero point not yet removed) of column tile c: the low
-  // nibble directly, the high nibble as (byte - low) / 16
+  // nibble directly, the high nibble as (byte - low) / 16 (INT4); INT8: every
+  // tile holds whole codes offset by 128
   auto o_of = [&](int c, int v) -> float {
+    if constexpr (Q8) return oacc[c][v] * 16777216.0f;  // 2^24
     return (c & 1) ? (oacc[c][v] - oacc[c - 1][v]) * 1048576.0f  // 2^20
                    : oacc[c][v] * 16777216.0f;                   // 2^24
   };
+  // INT8 V: the lane's elements NCOL * col .. + NCOL - 1 are NVD dwords of a row
+  constexpr int NVD = Q8 ? NCOL / 4 : 1;
+  constexpr int NVA = 8 * NVD;  // V dwords per lane per tile
   // v_perm selectors: byte beta (+ noff / 2) of two slot keys' dwords, each
   // zero-extended into one f16 half
   uint32_t vsel[NCOL / 2];
@@ -443,12 +456,15 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   uint32_t k_off[DWG];
 #pragma unroll
   for (int qq = 0; qq < DWG; ++qq) k_off[qq] = row_off + 4 * (g * DWG + (qq + g) % DWG);
-  const uint32_t ks_off = row_off + D / 2;  // + n*BLK (+ lhalf for V)
-  uint32_t v_off[8];
+  const uint32_t ks_off = row_off + (Q8 ? D : D / 2);  // + n*BLK (+ lhalf for V)
+  uint32_t v_off[NVA];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int kk = ((j & 1) << 4) + 4 * g + (j >> 1);  // key of P.V slot j (pairs 4g+i, 16+4g+i)
-    v_off[j] = (kk >> 4) * GG::BLK + GG::lhalf + (kk & 15) * GG::TS + hoff + 4 * (col % DW);
+    const uint32_t kb0 = (kk >> 4) * GG::BLK + GG::lhalf + (kk & 15) * GG::TS + hoff;
+#pragma unroll
+    for (int w = 0; w < NVD; ++w)
+      v_off[j * NVD + w] = kb0 + 4 * (Q8 ? NVD * col + w : col % DW);
   }
   // W tile addressing: writer (col, g) -> row qh, dword col; reader (row r, g)
   // -> 16 bytes at dword 4g of its query head's row (or the zero row).  Rows
@@ -474,11 +490,16 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         segw[qq] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + k_off[qq]);
 #pragma unroll
       for (int k = 0; k < NCK; ++k) {
-        const uint32_t w0 = segw[2 * k], w1 = segw[2 * k + 1];
-        kb[n][k][0] = (int)(w0 & 0x0F0F0F0Fu);
-        kb[n][k][1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
-        kb[n][k][2] = (int)(w1 & 0x0F0F0F0Fu);
-        kb[n][k][3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
+        if constexpr (Q8) {  // int8 codes as they are
+#pragma unroll
+          for (int rho = 0; rho < 4; ++rho) kb[n][k][rho] = (int)segw[4 * k + rho];
+        } else {
+          const uint32_t w0 = segw[2 * k], w1 = segw[2 * k + 1];
+          kb[n][k][0] = (int)(w0 & 0x0F0F0F0Fu);
+          kb[n][k][1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
+          kb[n][k][2] = (int)(w1 & 0x0F0F0F0Fu);
+          kb[n][k][3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
+        }
       }
     }
   };
@@ -512,7 +533,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // O += W V for tile t.
   // LDS words of a tile needed after its scores: scale words and V bytes
   struct TileWords {
-    uint32_t kw[2], vw[2], va[8];
+    uint32_t kw[2], vw[2], va[NVA];
   };
   auto tile_words = [&](const unsigned char* st, TileWords& w) {
 #pragma unroll
@@ -521,7 +542,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       w.vw[n] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + GG::lhalf + ks_off);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w.va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
+    for (int j = 0; j < NVA; ++j) w.va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
   };
 
   auto step = [&](int t, const i32x4_t (&acc)[2][3], i32x4_t (&nxt)[2][3],
@@ -552,10 +573,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int n = 0; n < 2; ++n) {
       const int key = tb * kBlockSize + 16 * n + col;
       kval[n] = (tb + n < b1) && key < L && key >= lo;
-      const float sK = as_float(cw.kw[n] & 0xFFFFFFF0u);
-      const float zK = (float)(cw.kw[n] & 0xFu);
-      sV[n] = kval[n] ? as_float(cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked keys get zero weight
-      zV[n] = (float)(cw.vw[n] & 0xFu);
+      // INT4: zero point in the scale word's low 4 bits; INT8: a plain fp32
+      // scale, no K zero point, and V codes offset by 128 (see the V operands)
+      const float sK = as_float(Q8 ? cw.kw[n] : cw.kw[n] & 0xFFFFFFF0u);
+      const float zK = Q8 ? 0.f : (float)(cw.kw[n] & 0xFu);
+      sV[n] = kval[n] ? as_float(Q8 ? cw.vw[n] : cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked: 0
+      zV[n] = Q8 ? 128.f : (float)(cw.vw[n] & 0xFu);
       const uint32_t keep = kval[n] ? 0xFFFFFFFFu : 0u;
       const uint32_t ninf = kval[n] ? 0u : 0xFF800000u;
 #pragma unroll
@@ -619,6 +642,28 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const half8_t wop_lo = *reinterpret_cast<const half8_t*>(wt + rd_lo);
     phase_end(1, kb, nxt);
 
+    if constexpr (Q8) {
+      // phase 3 (INT8): column tile c takes byte c % 4 of the lane's dword
+      // c / 4 of two slot keys, each zero-extended into an f16 half with its
+      // top bit flipped: the subnormal (code + 128) * 2^-24, exact in the
+      // products; the 128 leaves through the zero-point term (zV = 128).
+      uint32_t vx8[NCOL][4];
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) {
+        const uint32_t bsel = 0x0C000C00u | (uint32_t)(c & 3) | ((4u + (c & 3)) << 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vx8[c][i] = __builtin_amdgcn_perm(cw.va[(2 * i + 1) * NVD + (c >> 2)],
+                                            cw.va[2 * i * NVD + (c >> 2)], bsel) ^ 0x00800080u;
+      }
+      phase_end(2, kb, nxt);
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) {
+        const half8_t xb = __builtin_bit_cast(half8_t, vx8[c]);
+        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, xb, oacc[c], 0, 0, 0);
+        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, xb, oacc[c], 0, 0, 0);
+      }
+    } else {
     // phase 3: V operands.  Byte beta of the lane's dword of two slot keys,
     // each zero-extended into an f16 half: the subnormal (low + 16 * high) *
     // 2^-24, exact in the products.
@@ -645,6 +690,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, xb, ox, 0, 0, 0);
       ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, lb, ol, 0, 0, 0);
       ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, lb, ol, 0, 0, 0);
+    }
     }
     // the remaining score groups of tile t+1 share this region: one MFMA per
     // vector instruction of the low-nibble masks
@@ -697,6 +743,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
   // column tile c holds element dof(c) of this lane
   auto dof = [&](int c) -> int {
+    if constexpr (Q8) return NCOL * col + c;  // the V bytes the lane read
     return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
   };
 
@@ -723,6 +770,14 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     float o[NCOL];
 #pragma unroll
     for (int c = 0; c < NCOL; ++c) o[c] = (o_of(c, v) - corr[v]) * inv_l;
+    if constexpr (Q8) {  // the original domain already
+      if (!qok[v]) continue;
+      const int qg = h * G + g * RPG + v;
+      uint16_t* dst = out + ((int64_t)q0 * num_q_heads + qg) * D;
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) dst[dof(c)] = from_f32<BF16>(o[c]);
+      continue;
+    }
 #pragma unroll
     for (int span = 1; span < (D == 128 ? 8 : 4); span <<= 1) {
 #pragma unroll
@@ -751,18 +806,20 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
 }
 
-template <bool BF16, int D, int G, int HPW>
+template <bool BF16, int D, int G, int HPW, bool Q8>
 hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
-  constexpr size_t lds = Lay<D, G, HPW>::total;
+  using LY = Lay<D, G, HPW, Q8>;
+  constexpr size_t lds = LY::total;
   static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 CU");
-  static_assert((Lay<D, G, HPW>::S - 2) * Geo<D, HPW>::NI <= 63, "vmcnt range");
-  auto kern = decode_lds_kernel<BF16, D, G, HPW>;
+  static_assert((LY::S - 2) * Geo<D, HPW, Q8>::NI <= 63, "vmcnt range");
+  auto kern = decode_lds_kernel<BF16, D, G, HPW, Q8>;
   if (lds > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per CU)
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid(a.num_segments, a.num_seqs, a.num_kv_heads / HPW), block(64 * HPW);
-  const float scale_log2 = a.softmax_scale * kLog2e / (float)D;
+  // INT4: q . x_hat = q' . y_hat / D in the rotated domain; INT8: no rotation
+  const float scale_log2 = a.softmax_scale * kLog2e / (Q8 ? 1.0f : (float)D);
   const float cap2 = a.softcap > 0.f ? a.softcap * kLog2e : 0.f;  // base-2 units
   hipLaunchKernelGGL(kern, grid, block, lds, stream, reinterpret_cast<const uint16_t*>(a.q),
                      a.q_stride, reinterpret_cast<uint16_t*>(a.out), a.cache, a.num_kv_heads,
@@ -776,25 +833,38 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
   return launch_reduce(a, stream);
 }
 
-template <bool BF16, int D, int G>
+// KV heads per workgroup: up to 8 for INT4; up to 4 for INT8, whose rows are
+// twice as long (a two-block tile of 4 heads is 34 KiB: a four-stage ring)
+template <bool BF16, int D, int G, bool Q8>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-  switch (a.num_kv_heads >= 8 ? 8 : a.num_kv_heads) {
-    case 1: return launch_h<BF16, D, G, 1>(a, stream);
-    case 2: return launch_h<BF16, D, G, 2>(a, stream);
-    case 4: return launch_h<BF16, D, G, 4>(a, stream);
-    default: return launch_h<BF16, D, G, 8>(a, stream);
+  const int cap = Q8 ? 4 : 8;
+  switch (a.num_kv_heads >= cap ? cap : a.num_kv_heads) {
+    case 1: return launch_h<BF16, D, G, 1, Q8>(a, stream);
+    case 2: return launch_h<BF16, D, G, 2, Q8>(a, stream);
+    case 4: return launch_h<BF16, D, G, 4, Q8>(a, stream);
+    default:
+      if constexpr (Q8) return hipErrorInvalidValue;  // not reached: cap is 4
+      else return launch_h<BF16, D, G, 8, Q8>(a, stream);
   }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool Q8>
 hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_t<BF16, D, 1>(a, stream);
-    case 2: return launch_t<BF16, D, 2>(a, stream);
-    case 4: return launch_t<BF16, D, 4>(a, stream);
-    case 8: return launch_t<BF16, D, 8>(a, stream);
-    default: return launch_t<BF16, D, 16>(a, stream);
+    case 1: return launch_t<BF16, D, 1, Q8>(a, stream);
+    case 2: return launch_t<BF16, D, 2, Q8>(a, stream);
+    case 4: return launch_t<BF16, D, 4, Q8>(a, stream);
+    case 8: return launch_t<BF16, D, 8, Q8>(a, stream);
+    default: return launch_t<BF16, D, 16, Q8>(a, stream);
   }
+}
+
+template <bool Q8>
+hipError_t launch_q(const AttnArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.head_size == 128 ? launch_d<true, 128, Q8>(a, stream)
+                                        : launch_d<true, 64, Q8>(a, stream);
+  return a.head_size == 128 ? launch_d<false, 128, Q8>(a, stream)
+                            : launch_d<false, 64, Q8>(a, stream);
 }
 
 }  // namespace
@@ -805,9 +875,7 @@ bool decode_lds_supported(const AttnArgs& a) {
 }
 
 hipError_t launch_decode_lds(const AttnArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.head_size == 128 ? launch_d<true, 128>(a, stream)
-                                        : launch_d<true, 64>(a, stream);
-  return a.head_size == 128 ? launch_d<false, 128>(a, stream) : launch_d<false, 64>(a, stream);
+  return a.q8 ? launch_q<true>(a, stream) : launch_q<false>(a, stream);
 }
 
 }  // namespace int4kv

@@ -41,6 +41,9 @@ struct AttnArgs {
   // logit soft cap c (natural-log units): scores z become c * tanh(z / c)
   // before the softmax; <= 0 is none
   float softcap = 0.f;
+  // INT8 per-token-head cache (rows of head_size int8 codes + fp32 scale, no
+  // rotation; signs unused) instead of the INT4 one
+  bool q8 = false;
   // fused decode step only: the new token of each sequence (token b belongs to
   // sequence b and is its last key), encoded into the cache by the workgroup
   // that reads its block; null otherwise

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"int4_kv_write", "int4_paged_attention", "int4kv_cache_bytes",
             "int4kv_status_string", "int4kv_last_error", "int8_kv_write",
-            "int8kv_cache_bytes"} <= set(names)
+            "int8kv_cache_bytes", "int8_paged_attention"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(ik.library_path())
@@ -188,3 +188,29 @@ def test_int8_write_rejects_invalid_host_arguments(kw, status):
 
 def test_int8_write_empty_is_a_no_op():
     assert _w8(T=0) == 0
+
+
+def _a8(**kw):
+    a = dict(q=FAKE, qs=4096, out=FAKE, dtype=1, cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32,
+             cu=FAKE, su=FAKE, S=4, mq=1, mk=1024, bt=FAKE, bts=64, scale=0.088, win=0, cap=0.0,
+             ns=1, so=None, sm=None, ss=None, stream=None)
+    a.update(kw)
+    return ik.load_library().int8_paged_attention(
+        a["q"], a["qs"], a["out"], a["dtype"], a["cache"], a["nb"], a["bs"], a["hkv"], a["d"],
+        a["hq"], a["cu"], a["su"], a["S"], a["mq"], a["mk"], a["bt"], a["bts"], a["scale"],
+        a["win"], a["cap"], a["ns"], a["so"], a["sm"], a["ss"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mq=7), 2), (dict(hkv=3, hq=6), 2), (dict(hkv=6, hq=12), 2), (dict(d=96), 2),
+    (dict(bs=8), 2), (dict(hq=30), 1), (dict(ns=16), 3), (dict(cache=None), 1),
+    (dict(cap=float("nan")), 1), (dict(bts=10), 1),
+])
+def test_int8_attention_rejects_invalid_host_arguments(kw, status):
+    assert _a8(**kw) == status
+    assert ik.int4kv_last_error() != ""
+
+
+def test_int8_attention_empty_batch_is_a_no_op():
+    assert _a8(S=0) == 0
+    assert _a8(mq=0) == 0
