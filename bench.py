@@ -375,6 +375,8 @@ def other_rows(dev):
     rows["llama3_8b_decode_int8"] = {
         "workload": "the same 64 x 4096 batch over the INT8 per-token-head cache (132-byte rows)",
         "num_segments": ns8, "us": round(us8, 2),
+        "num_segments_library_choice": ik.int8kv_decode_num_segments(w.num_seqs, w.num_kv_heads,
+                                                                     w.max_seqlen_k),
         "timing": "20 calls (two caches alternating) replayed from one HIP graph, per call",
         "GBps": round(kv8 / us8 / 1e3, 1), "hbm_frac": round(kv8 / us8 / 1e3 / HBM_PEAK_GBS, 4),
         "kv_bytes_vs_int4": round(kv8 / kv, 3)}

@@ -261,6 +261,10 @@ int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void
                                      int32_t num_segments, float* segm_output, float* segm_max,
                                      float* segm_expsum, void* stream);
 
+/* int8kv_decode_num_segments: the split count for int8_paged_attention, by the
+ * rule of int4kv_decode_num_segments for its workgroups of up to 4 KV heads. */
+int32_t int8kv_decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seqlen_k);
+
 /* Human-readable name of a status code (static storage). */
 const char* int4kv_status_string(int4kv_status_t s);
 

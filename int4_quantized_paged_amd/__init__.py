@@ -78,6 +78,8 @@ def load_library():
                                          i32, i32, i32, P, i32, ctypes.c_float, i32,
                                          ctypes.c_float, i32, P, P, P, P]
     lib.int8_paged_attention.restype = ctypes.c_int
+    lib.int8kv_decode_num_segments.argtypes = [i32, i32, i32]
+    lib.int8kv_decode_num_segments.restype = i32
     lib.int4kv_decode_num_segments.argtypes = [i32, i32, i32]
     lib.int4kv_decode_num_segments.restype = i32
     _lib = lib
@@ -120,6 +122,11 @@ def int4kv_last_error() -> str:
 def int4kv_decode_num_segments(num_seqs: int, num_kv_heads: int, max_seqlen_k: int) -> int:
     """The library's split-K segment count for a decode batch (host only)."""
     return int(load_library().int4kv_decode_num_segments(num_seqs, num_kv_heads, max_seqlen_k))
+
+
+def int8kv_decode_num_segments(num_seqs: int, num_kv_heads: int, max_seqlen_k: int) -> int:
+    """The library's split-K segment count for an INT8 decode batch (host only)."""
+    return int(load_library().int8kv_decode_num_segments(num_seqs, num_kv_heads, max_seqlen_k))
 
 
 def cache_shape(num_blocks: int, num_kv_heads: int, head_size: int, block_size: int = 16):

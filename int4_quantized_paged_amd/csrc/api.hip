@@ -38,6 +38,28 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kDecodeTargetWorkgroups = 256;
 constexpr int64_t kDecodeMinTilesPerSegment = 2;
 
+// the split-count rule for workgroups of up to `hpw_cap` KV heads (8 for the
+// INT4 decode kernel, 4 for the INT8 one)
+int32_t decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seqlen_k,
+                            int hpw_cap) {
+  if (num_seqs < 1 || num_kv_heads < 1 || max_seqlen_k < 1) return 1;
+  // KV heads per workgroup of the decode kernels
+  int hpw = hpw_cap;
+  const int hkv = num_kv_heads;
+  if (hkv < hpw_cap && (hkv == 1 || hkv == 2 || hkv == 4))
+    hpw = hkv;
+  else if (hkv % hpw_cap != 0)
+    while (hkv % hpw) hpw >>= 1;
+  const int64_t wgs = (int64_t)num_seqs * (hkv / hpw);  // workgroups per segment index
+  const int64_t fill = (kDecodeTargetWorkgroups + wgs - 1) / wgs;
+  const int64_t tiles = ((int64_t)max_seqlen_k + 31) / 32;  // 32-key tiles of the longest sequence
+  const int64_t cap = tiles / kDecodeMinTilesPerSegment;
+  int64_t ns = fill < cap ? fill : cap;
+  if (ns < 1) ns = 1;
+  if (ns > 256) ns = 256;
+  return (int32_t)ns;
+}
+
 int4kv_status_t check_common(const void* cache, int32_t num_blocks, int32_t block_size,
                              int32_t num_kv_heads, int32_t head_size, const float* signs) {
   if (!cache || !signs) return fail(INT4KV_ERR_INVALID_ARG, "null cache or rht_signs pointer");
@@ -164,22 +186,11 @@ const char* int4kv_status_string(int4kv_status_t s) {
 const char* int4kv_last_error(void) { return g_last_error; }
 
 int32_t int4kv_decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seqlen_k) {
-  if (num_seqs < 1 || num_kv_heads < 1 || max_seqlen_k < 1) return 1;
-  // KV heads per workgroup of the decode kernels
-  int hpw = 8;
-  const int hkv = num_kv_heads;
-  if (hkv == 1 || hkv == 2 || hkv == 4)
-    hpw = hkv;
-  else if (hkv % 8 != 0)
-    while (hkv % hpw) hpw >>= 1;
-  const int64_t wgs = (int64_t)num_seqs * (hkv / hpw);  // workgroups per segment index
-  const int64_t fill = (kDecodeTargetWorkgroups + wgs - 1) / wgs;
-  const int64_t tiles = ((int64_t)max_seqlen_k + 31) / 32;  // 32-key tiles of the longest sequence
-  const int64_t cap = tiles / kDecodeMinTilesPerSegment;
-  int64_t ns = fill < cap ? fill : cap;
-  if (ns < 1) ns = 1;
-  if (ns > 256) ns = 256;
-  return (int32_t)ns;
+  return decode_num_segments(num_seqs, num_kv_heads, max_seqlen_k, 8);
+}
+
+int32_t int8kv_decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seqlen_k) {
+  return decode_num_segments(num_seqs, num_kv_heads, max_seqlen_k, 4);
 }
 
 int4kv_status_t int4_kv_write(const void* key, int64_t key_token_stride, const void* value,

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"int4_kv_write", "int4_paged_attention", "int4kv_cache_bytes",
             "int4kv_status_string", "int4kv_last_error", "int8_kv_write",
-            "int8kv_cache_bytes", "int8_paged_attention"} <= set(names)
+            "int8kv_cache_bytes", "int8_paged_attention", "int8kv_decode_num_segments"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(ik.library_path())
@@ -214,3 +214,13 @@ def test_int8_attention_rejects_invalid_host_arguments(kw, status):
 def test_int8_attention_empty_batch_is_a_no_op():
     assert _a8(S=0) == 0
     assert _a8(mq=0) == 0
+
+
+@pytest.mark.parametrize("S,hkv,L,ns", [
+    (64, 8, 4096, 2),    # Llama-3-8B-shaped: 4-head workgroups, 128 per segment index
+    (4, 8, 131072, 32),
+    (8, 8, 1024, 16),
+    (1, 2, 100, 2),
+])
+def test_int8_decode_num_segments(S, hkv, L, ns):
+    assert ik.int8kv_decode_num_segments(S, hkv, L) == ns

@@ -184,7 +184,7 @@ def test_int8_decode_llama3_full_size_sampled(oracle_mod):
     """64 x 4096, 32 q / 8 KV heads, in the launch the benchmark times (the
     library's split count); 3 sampled sequences against the oracle."""
     w = wl.llama3_8b_decode(device="cuda")
-    ns = ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads, w.max_seqlen_k)
+    ns = ik.int8kv_decode_num_segments(w.num_seqs, w.num_kv_heads, w.max_seqlen_k)
     header(f"int8 Llama-3-8B-shaped decode full size NS={ns}")
     t = to_dev(w)
     c = torch.empty(ik.cache_shape_int8(w.num_blocks, 8, 128), dtype=torch.uint8, device="cuda")
