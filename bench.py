@@ -247,6 +247,28 @@ def other_rows(dev):
             "algorithmic_gflop": round(fl / 1e9, 2),
             "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
         del w, call
+    # the same mix over the INT8 per-token-head cache (d 128)
+    w = wl.chunked_prefill(device=dev, head_size=128)
+    c8 = torch.empty(ik.cache_shape_int8(w.num_blocks, w.num_kv_heads, 128), dtype=torch.uint8,
+                     device=dev)
+    _, slots = w.token_set("all")
+    ik.int8_kv_write(w.key, w.value, slots.to(dev), c8)
+    q, cu, su, bt = w.query, w.cu_seqlens_q().to(dev), w.seqused_k().to(dev), w.block_table.to(dev)
+    out = torch.empty_like(q)
+
+    def call8():
+        ik.int8_paged_attention(q, c8, cu, su, w.max_seqlen_q, w.max_seqlen_k, bt,
+                                w.softmax_scale, out=out)
+    for _ in range(3):
+        call8()
+    us = _median_event_us(call8, 10)
+    fl = w.attention_flops()
+    rows["prefill_int8_d128"] = {
+        "workload": f"chunked-prefill mix over the INT8 cache: {sum(w.query_lens)} query tokens, "
+                    f"{sum(w.kv_lens)} keys, 32 q / 8 KV heads, d 128",
+        "us": round(us, 2), "tflops": round(fl / us / 1e6, 1),
+        "mfma_frac": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)}
+    del w, c8, q, out
     # GQA decode: 8 sequences of 1..1024 keys, one new token each, in one
     # int4_decode_step (latency-bound: reported in us and GB/s, not against HBM peak)
     w = wl.gqa_decode(device=dev)

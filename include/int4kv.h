@@ -239,15 +239,16 @@ int4kv_status_t int8_kv_write(const void* key, int64_t key_token_stride, const v
                               int32_t head_size, void* stream);
 
 /*
- * int8_paged_attention: causal decode attention (one query row per sequence)
- * over the INT8 per-token-head cache: softmax(softmax_scale * q . k_hat) .
- * v_hat with k_hat, v_hat = codes * scale ([pr40633] description: the INT8
- * per-token-head read side is the common attention kernel with per-token-head
- * scales).  Arguments, window, soft cap, split-K segments and errors as for
- * int4_paged_attention, without the sign vector.  Supported: max_seqlen_q == 1
- * (decode batches; a larger value returns INT4KV_ERR_UNSUPPORTED), head_size
- * 64 or 128, block_size 16, num_kv_heads 1, 2 or a multiple of 4, query heads
- * per KV head in {1, 2, 4, 8, 16}.
+ * int8_paged_attention: causal attention over the INT8 per-token-head cache:
+ * softmax(softmax_scale * q . k_hat) . v_hat with k_hat, v_hat = codes *
+ * scale ([pr40633] description: the INT8 per-token-head read side is the
+ * common attention kernel with per-token-head scales).  Arguments, batches
+ * (decode and prefill / mixed, as for int4_paged_attention: the segments are
+ * used only when max_seqlen_q == 1), window, soft cap and errors as for
+ * int4_paged_attention, without the sign vector.  Supported: head_size 64 or
+ * 128, block_size 16, query heads per KV head in {1, 2, 4, 8, 16}; decode
+ * batches (max_seqlen_q == 1) also need num_kv_heads 1, 2 or a multiple of 4
+ * (else INT4KV_ERR_UNSUPPORTED).
  */
 int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void* out,
                                      int4kv_dtype_t dtype, const uint8_t* kv_cache,

@@ -276,11 +276,11 @@ int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
   if (num_seqs == 0 || max_seqlen_q == 0) return ok();
-  if (max_seqlen_q != 1)
-    return fail(INT4KV_ERR_UNSUPPORTED, "INT8 mode: decode batches only (max_seqlen_q == 1)");
-  if (!(num_kv_heads == 1 || num_kv_heads == 2 || num_kv_heads % 4 == 0))
-    return fail(INT4KV_ERR_UNSUPPORTED, "INT8 mode: num_kv_heads %d must be 1, 2 or a multiple of 4",
-                num_kv_heads);
+  const bool decode = max_seqlen_q == 1;
+  // the decode kernel's workgroups take 1, 2 or 4 KV heads
+  if (decode && !(num_kv_heads == 1 || num_kv_heads == 2 || num_kv_heads % 4 == 0))
+    return fail(INT4KV_ERR_UNSUPPORTED,
+                "INT8 decode: num_kv_heads %d must be 1, 2 or a multiple of 4", num_kv_heads);
   int4kv::AttnArgs a;
   int4kv_status_t s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads,
                                       head_size, num_q_heads, cu_seqlens_q, seqused_k, num_seqs,
@@ -289,7 +289,8 @@ int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void
                                       num_segments, segm_output, segm_max, segm_expsum, a);
   if (s != INT4KV_OK) return s;
   a.q8 = true;
-  hipError_t e = int4kv::launch_decode_lds(a, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = decode ? int4kv::launch_decode_lds(a, st) : int4kv::launch_prefill(a, st);
   if (e != hipSuccess)
     return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
   return ok();

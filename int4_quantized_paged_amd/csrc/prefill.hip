@@ -30,6 +30,10 @@
 //  * Workgroups are numbered so that the KV heads of one (sequence, tile) run
 //    on the same XCD (the heads of a token share 128-byte lines in L2), and
 //    later query tiles, which see more keys, are dispatched first.
+//  * The INT8 per-token-head cache (the same kernel with Q8 set) has no
+//    rotation and d + 4 byte rows: K and V codes enter as bytes with the top
+//    bit flipped, (code + 128) * 2^-24, the 128 leaving through the same
+//    zero-point terms, and Q is staged unrotated.
 #include "device_common.h"
 #include "launch.h"
 
@@ -74,11 +78,11 @@ __device__ __forceinline__ float max16(float x) {
   return x;
 }
 
-template <int D, int G>
+template <int D, int G, bool Q8 = false>
 struct PGeo {
-  static constexpr int R = D / 2 + 4;             // packed row bytes
-  static constexpr int RW = R / 4;                // dwords per row (17 or 9)
-  static constexpr int DW = D / 8;                // code dwords per row
+  static constexpr int R = Q8 ? D + 4 : D / 2 + 4;  // row bytes (INT8: d codes + scale)
+  static constexpr int RW = R / 4;                  // dwords per row (INT4 17 or 9, INT8 33 or 17)
+  static constexpr int DW = Q8 ? D / 4 : D / 8;     // code dwords per row
   static constexpr int NIB = (16 * RW + 63) / 64; // copies per (block, K|V) image
   static constexpr uint32_t HALF = NIB * 256;     // LDS bytes of one (block, K|V) image
   static constexpr uint32_t STAGE = 4 * HALF;     // two blocks, K and V
@@ -96,7 +100,7 @@ struct PGeo {
   static constexpr int TQ = 128 / G;              // query tokens per workgroup
 };
 
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool Q8>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, uint16_t* __restrict__ out,
     const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
     const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq, int32_t window,
     float cap2, float inv_cap2) {
-  using PG = PGeo<D, G>;
+  using PG = PGeo<D, G, Q8>;
   constexpr int R = PG::R, RW = PG::RW, DW = PG::DW, NIB = PG::NIB;
   constexpr int NCH = D / 32;   // f16 MFMA k-chunks of the score
   constexpr int NCOL = D / 16;  // P.V column tiles
@@ -152,22 +156,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const int qh = row % G;
     const uint16_t* qp = q + (int64_t)(q0 + tq) * q_stride + (int64_t)(h * G + qh) * D + s * EPL;
     float x[EPL];
+    if constexpr (Q8) {  // no rotation: the INT8 rows hold the original domain
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = to_f32<BF16>(qp[e]) * signs[s * EPL + e];
+      for (int e = 0; e < EPL; ++e) x[e] = to_f32<BF16>(qp[e]);
+    } else {
 #pragma unroll
-    for (int span = 1; span < EPL; span <<= 1) {
+      for (int e = 0; e < EPL; ++e) x[e] = to_f32<BF16>(qp[e]) * signs[s * EPL + e];
+#pragma unroll
+      for (int span = 1; span < EPL; span <<= 1) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          if (e & span) continue;
+          const float u = x[e], v = x[e + span];
+          x[e] = u + v;
+          x[e + span] = u - v;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        if (e & span) continue;
-        const float u = x[e], v = x[e + span];
-        x[e] = u + v;
-        x[e + span] = u - v;
+        const float p = shfl_xor<1>(x[e]);
+        x[e] = s ? p - x[e] : x[e] + p;
       }
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float p = shfl_xor<1>(x[e]);
-      x[e] = s ? p - x[e] : x[e] + p;
     }
     // one exponent for the wave's 32 rows, so the logit scale is one constant
     // per wave (a row far below the wave's maximum keeps fewer significant
@@ -191,9 +200,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         const _Float16 hv = (_Float16)v;
         const _Float16 lv = (_Float16)(v - (float)hv);
         sum += (float)hv + (float)lv;
-        const int slot = ((j & 3) << 1) | (j >> 2);
-        hi8[slot] = (j & 1) ? (_Float16)((float)hv * 0.0625f) : hv;
-        lo8[slot] = (j & 1) ? (_Float16)((float)lv * 0.0625f) : lv;
+        // INT4 operand order [e0 e4 e1 e5 e2 e6 e3 e7], odd elements against
+        // codes scaled by 16; INT8 [e0 e2 e1 e3 e4 e6 e5 e7], codes as they are
+        const int slot = Q8 ? (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1) : ((j & 3) << 1) | (j >> 2);
+        hi8[slot] = (!Q8 && (j & 1)) ? (_Float16)((float)hv * 0.0625f) : hv;
+        lo8[slot] = (!Q8 && (j & 1)) ? (_Float16)((float)lv * 0.0625f) : lv;
       }
       const int el = s * EPL + 8 * e8;
       const int off = ((row * 2 + 0) * NCH + el / 32) * 32 + ((el % 32) / 8) * 8;
@@ -277,13 +288,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const uint32_t krow = (uint32_t)col * RW * 4;  // key col's record in a (block, K) image
   uint32_t k_off[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) k_off[c] = krow + (uint32_t)(4 * c + g) * 4;
+  for (int c = 0; c < NCH; ++c)  // INT8: two dwords (8 codes) per lane group and chunk
+    k_off[c] = krow + (uint32_t)(4 * c + g) * (Q8 ? 8 : 4);
   const uint32_t s_off = krow + (uint32_t)(RW - 1) * 4;  // scale word
-  uint32_t v_off[8];  // slot j = 2i + n <-> key 16n + g + 4i
+  // INT8 V: the lane's elements NCOL * col .. + NCOL - 1 are NVD dwords of a row
+  constexpr int NVD = Q8 ? NCOL / 4 : 1;
+  uint32_t v_off[8 * NVD];  // slot j = 2i + n <-> key 16n + g + 4i
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int n = j & 1, t = g + 4 * (j >> 1);
-    v_off[j] = (uint32_t)(2 * n + 1) * PG::HALF + (uint32_t)t * RW * 4 + (uint32_t)(col % DW) * 4;
+#pragma unroll
+    for (int w = 0; w < NVD; ++w)
+      v_off[j * NVD + w] = (uint32_t)(2 * n + 1) * PG::HALF + (uint32_t)t * RW * 4 +
+                           (uint32_t)(Q8 ? NVD * col + w : col % DW) * 4;
   }
   unsigned char* wt = smem + PG::LOW + wave * PG::WTILE;
   // W tile: the f16 pair of key col (blocks 0 and 1) of row r sits at dword
@@ -336,18 +353,26 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         const uint32_t w = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + k_off[c]);
         const uint32_t w8 = w >> 8;
         u32x4_t r;
-        r[0] = w & 0x000F000Fu;
-        r[1] = w & 0x00F000F0u;
-        r[2] = w8 & 0x000F000Fu;
-        r[3] = w8 & 0x00F000F0u;
+        if constexpr (Q8) {  // bytes zero-extended with the top bit flipped: code + 128
+          const uint32_t x = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + k_off[c] + 4);
+          r[0] = (w & 0x00FF00FFu) ^ 0x00800080u;
+          r[1] = (w8 & 0x00FF00FFu) ^ 0x00800080u;
+          r[2] = (x & 0x00FF00FFu) ^ 0x00800080u;
+          r[3] = ((x >> 8) & 0x00FF00FFu) ^ 0x00800080u;
+        } else {
+          r[0] = w & 0x000F000Fu;
+          r[1] = w & 0x00F000F0u;
+          r[2] = w8 & 0x000F000Fu;
+          r[3] = w8 & 0x00F000F0u;
+        }
         kb[n][c] = __builtin_bit_cast(half8_t, r);
       }
       kw[n] = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + s_off);
       vw[n] = *reinterpret_cast<const uint32_t*>(st + (2 * n + 1) * PG::HALF + s_off);
     }
-    uint32_t va[8];
+    uint32_t va[8 * NVD];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
+    for (int j = 0; j < 8 * NVD; ++j) va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
 
     // scores: S[i][n] for row tile i, keys 16n + col (sum of q' * code * 2^-24)
     float4_t sacc[2][2];
@@ -370,10 +395,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     float sKc[2], zK[2], sV[2], zV[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      sKc[n] = as_float(kw[n] & 0xFFFFFFF0u) * c0;
-      zK[n] = (float)(kw[n] & 0xFu);
-      sV[n] = as_float(vw[n] & 0xFFFFFFF0u);
-      zV[n] = (float)(vw[n] & 0xFu);
+      // INT4: zero points in the scale words' low 4 bits; INT8: plain fp32
+      // scales, and the codes enter offset by 128 (K and V alike)
+      sKc[n] = as_float(Q8 ? kw[n] : kw[n] & 0xFFFFFFF0u) * c0;
+      zK[n] = Q8 ? 128.f : (float)(kw[n] & 0xFu);
+      sV[n] = as_float(Q8 ? vw[n] : vw[n] & 0xFFFFFFF0u);
+      zV[n] = Q8 ? 128.f : (float)(vw[n] & 0xFu);
     }
     // logits in base-2 units; the reference maximum m of a row only moves
     // when a logit exceeds it by more than kLazy (so p = 2^(z - m) <= 2^kLazy),
@@ -456,7 +483,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     // of the lane's dword of two slot keys, zero-extended into f16 halves, is
     // the subnormal (low + 16 high) * 2^-24; masked, the low nibble alone.
     // Column tile 2bb takes the low nibbles, 2bb + 1 the whole bytes; the
-    // high nibble's column is their difference / 16.
+    // high nibble's column is their difference / 16.  INT8: column tile c
+    // takes byte c % 4 of the lane's dword c / 4 of two slot keys, top bit
+    // flipped: the subnormal (code + 128) * 2^-24 (the 128 leaves through the
+    // zero-point term, zV = 128).
+    if constexpr (Q8) {
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) {
+        const uint32_t bsel = 0x0C000C00u | (uint32_t)(c & 3) | ((4u + (c & 3)) << 16);
+        u32x4_t vx;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          vx[k] = __builtin_amdgcn_perm(va[(2 * k + 1) * NVD + (c >> 2)],
+                                        va[2 * k * NVD + (c >> 2)], bsel) ^ 0x00800080u;
+        const half8_t xb = __builtin_bit_cast(half8_t, vx);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], xb, oacc[i][c], 0, 0, 0);
+          oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo[i], xb, oacc[i][c], 0, 0, 0);
+        }
+      }
+    } else
 #pragma unroll
     for (int bb = 0; bb < NCOL / 2; ++bb) {
       u32x4_t vx, vl;
@@ -521,6 +568,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   // lane: even tiles directly in units of 2^-24, odd ones as (bytes - low) in
   // units of 2^-20.
   auto dof = [&](int c) -> int {
+    if constexpr (Q8) return NCOL * col + c;  // the V bytes the lane read
     return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
   };
 #pragma unroll
@@ -540,9 +588,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       float o[NCOL];
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) {
-        const float oc = (c & 1) ? (oacc[i][c][v] - oacc[i][c - 1][v]) * 1048576.0f  // 2^20
-                                 : oacc[i][c][v] * 16777216.0f;                      // 2^24
+        const float oc = (!Q8 && (c & 1)) ? (oacc[i][c][v] - oacc[i][c - 1][v]) * 1048576.0f
+                                          : oacc[i][c][v] * 16777216.0f;  // 2^20 / 2^24
         o[c] = (oc - cv) * inv_l;
+      }
+      if constexpr (Q8) {  // the original domain already
+        const int row = 32 * wq + 16 * i + 4 * g + v;
+        const int tq = qt * TQ + row / G;
+        if (tq < qlen) {
+          const int qg = h * G + row % G;
+          uint16_t* dst = out + ((int64_t)(q0 + tq) * num_q_heads + qg) * D;
+#pragma unroll
+          for (int c = 0; c < NCOL; ++c) dst[dof(c)] = from_f32<BF16>(o[c]);
+        }
+        continue;
       }
 #pragma unroll
       for (int span = 1; span < (D == 128 ? 8 : 4); span <<= 1) {
@@ -575,11 +634,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }
 }
 
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool Q8>
 hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
-  using PG = PGeo<D, G>;
+  using PG = PGeo<D, G, Q8>;
   static_assert(PG::TOTAL <= 160 * 1024, "LDS of a gfx950 CU");
-  auto kern = prefill_kernel<BF16, D, G>;
+  auto kern = prefill_kernel<BF16, D, G, Q8>;
   if (PG::TOTAL > 65536) {
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)PG::TOTAL);
     if (e != hipSuccess) return e;
@@ -588,7 +647,9 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t groups = (int64_t)a.num_seqs * tiles_per_seq;
   const int64_t nwg = (groups + 7) / 8 * 8 * a.num_kv_heads;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const float scale_log2 = a.softmax_scale * kLog2e / (float)D;
+  // INT4: the rotation is an unnormalised Hadamard transform on both sides,
+  // so q' . k' carries a factor D
+  const float scale_log2 = a.softmax_scale * kLog2e / (Q8 ? 1.0f : (float)D);
   const float cap2 = a.softcap > 0.f ? a.softcap * kLog2e : 0.f;  // base-2 units
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(512), PG::TOTAL, stream,
                      reinterpret_cast<const uint16_t*>(a.q), a.q_stride,
@@ -598,24 +659,29 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool Q8>
 hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_prefill_t<BF16, D, 1>(a, stream);
-    case 2: return launch_prefill_t<BF16, D, 2>(a, stream);
-    case 4: return launch_prefill_t<BF16, D, 4>(a, stream);
-    case 8: return launch_prefill_t<BF16, D, 8>(a, stream);
-    default: return launch_prefill_t<BF16, D, 16>(a, stream);
+    case 1: return launch_prefill_t<BF16, D, 1, Q8>(a, stream);
+    case 2: return launch_prefill_t<BF16, D, 2, Q8>(a, stream);
+    case 4: return launch_prefill_t<BF16, D, 4, Q8>(a, stream);
+    case 8: return launch_prefill_t<BF16, D, 8, Q8>(a, stream);
+    default: return launch_prefill_t<BF16, D, 16, Q8>(a, stream);
   }
+}
+
+template <bool Q8>
+hipError_t launch_prefill_q(const AttnArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.head_size == 128 ? launch_prefill_d<true, 128, Q8>(a, stream)
+                                        : launch_prefill_d<true, 64, Q8>(a, stream);
+  return a.head_size == 128 ? launch_prefill_d<false, 128, Q8>(a, stream)
+                            : launch_prefill_d<false, 64, Q8>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.head_size == 128 ? launch_prefill_d<true, 128>(a, stream)
-                                        : launch_prefill_d<true, 64>(a, stream);
-  return a.head_size == 128 ? launch_prefill_d<false, 128>(a, stream)
-                            : launch_prefill_d<false, 64>(a, stream);
+  return a.q8 ? launch_prefill_q<true>(a, stream) : launch_prefill_q<false>(a, stream);
 }
 
 }  // namespace int4kv

@@ -1,6 +1,7 @@
 """GPU parity of the INT8 per-token-head mode: the cache write (codes and
 scale words bit for bit against the oracle over the whole cache buffer,
-sentinel bytes included)."""
+sentinel bytes included), and decode and prefill attention over that cache
+(|gpu - ref| <= 2e-3 + 1e-2 |ref| against the oracle's fp64 attention)."""
 import random
 
 import numpy as np
@@ -112,10 +113,10 @@ def _int8_cache(oracle_mod, w, t):
     return c, ref
 
 
-def _attn8(w, t, c, ns, window=0, softcap=0.0):
+def _attn8(w, t, c, ns=1, window=0, softcap=0.0):
     segs = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns, w.head_size) if ns > 1 else \
         (None, None, None)
-    return ik.int8_paged_attention(t["query"], c, t["cu"], t["su"], 1, w.max_seqlen_k,
+    return ik.int8_paged_attention(t["query"], c, t["cu"], t["su"], w.max_seqlen_q, w.max_seqlen_k,
                                    t["block_table"], w.softmax_scale, num_segments=ns,
                                    segm_output=segs[0], segm_max=segs[1], segm_expsum=segs[2],
                                    sliding_window=window, softcap=softcap)
@@ -202,10 +203,98 @@ def test_int8_decode_llama3_full_size_sampled(oracle_mod):
         assert_attention_close(out[seqs], _ref8(oracle_mod, ws, ref_cache), f"seq {seqs}")
 
 
-def test_int8_prefill_is_unsupported():
-    w = wl.custom([(4, 40)], 8, 2, 128, seed=1, write_all=True)
+# ---- prefill / mixed batches over the INT8 cache
+
+MIX = [(5, 48), (16, 16), (1, 100), (33, 33), (64, 200), (7, 301), (2, 2), (1, 1)]
+
+
+def _prefill8(oracle_mod, w, window=0, softcap=0.0):
     t = to_dev(w)
-    c = torch.zeros(ik.cache_shape_int8(w.num_blocks, 2, 128), dtype=torch.uint8, device="cuda")
-    with pytest.raises(ik.Int4KVError):
-        ik.int8_paged_attention(t["query"], c, t["cu"], t["su"], w.max_seqlen_q, w.max_seqlen_k,
-                                t["block_table"], w.softmax_scale)
+    c, ref_cache = _int8_cache(oracle_mod, w, t)
+    out = _attn8(w, t, c, 1, window, softcap)
+    torch.cuda.synchronize()
+    assert_attention_close(out, _ref8(oracle_mod, w, ref_cache, window, softcap), w.name)
+    return out
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_prefill_mixed_lengths(oracle_mod, G, d):
+    """Query lengths 1..64 over contexts 1..301 in one batch: ragged query
+    tiles, tiles that end mid-block and single-token rows."""
+    header(f"int8 prefill mixed G={G} d={d}")
+    hkv = 2 if G <= 8 else 1
+    w = wl.custom(MIX, G * hkv, hkv, d, seed=300 + G + d, write_all=True, extra_blocks=2)
+    _prefill8(oracle_mod, w)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(6, 3, 128, torch.float16), (32, 8, 64, torch.bfloat16)])
+def test_int8_prefill_window_softcap(oracle_mod, hq, hkv, d, dtype):
+    """Sliding windows shorter and longer than the query tile, soft caps, and a
+    KV head count (3) that the decode kernel does not take."""
+    w = wl.custom([(40, 120), (9, 300), (130, 130)], hq, hkv, d, dtype=dtype, seed=hq + d,
+                  write_all=True, scale=2.0)
+    for window, cap in ((0, 0.0), (17, 0.0), (100, 0.0), (0, 5.0), (50, 30.0)):
+        header(f"int8 prefill {hq}/{hkv} d{d} window={window} cap={cap}")
+        _prefill8(oracle_mod, w, window, cap)
+
+
+@pytest.mark.parametrize("scale", [1e-3, 30.0])
+def test_int8_prefill_scaled_inputs(oracle_mod, scale):
+    header(f"int8 prefill scale {scale}")
+    w = wl.custom([(40, 120), (9, 300)], 8, 2, 128, dtype=torch.float16, seed=17, write_all=True,
+                  scale=scale)
+    _prefill8(oracle_mod, w)
+
+
+def test_int8_prefill_empty_sequences_and_last_row_matches_decode(oracle_mod):
+    """Zero-length queries and contexts inside a prefill batch write nothing
+    to their rows; the last query row of a prefill equals the decode of the
+    same token."""
+    header("int8 prefill empty sequences / last row vs decode")
+    w = wl.custom([(30, 60), (0, 20), (3, 3), (40, 390)], 32, 8, 128, seed=21, write_all=True)
+    t = to_dev(w)
+    c, ref_cache = _int8_cache(oracle_mod, w, t)
+    pre = _attn8(w, t, c)
+    ref = _ref8(oracle_mod, w, ref_cache)
+    torch.cuda.synchronize()
+    assert_attention_close(pre, ref, "prefill")
+    last = sub_workload(w, [3])
+    dq = wl.Workload("last row", w.dtype, 32, 8, 128, w.num_blocks, [390], [1], [1],
+                     last.block_table, last.key, last.value, last.query[-1:], w.signs)
+    dec = _attn8(dq, to_dev(dq), c, 4)
+    torch.cuda.synchronize()
+    assert_attention_close(dec, ref[-1:], "decode of the last row")
+
+
+def test_int8_chunked_prefill_full_size_sampled(oracle_mod):
+    """The 32-sequence chunked-prefill mix (query lengths log-uniform in
+    [1, 512], contexts in [512, 16384], 32 q / 8 KV heads, d 128) in one
+    launch; 10 sampled (sequence, query row) pairs against the oracle, each
+    evaluated as a decode at that row's position."""
+    w = wl.chunked_prefill(device="cuda")
+    header(f"int8 chunked prefill full size: {sum(w.query_lens)} query tokens")
+    t = to_dev(w)
+    c = torch.empty(ik.cache_shape_int8(w.num_blocks, 8, 128), dtype=torch.uint8, device="cuda")
+    idx, slots = w.token_set("all")
+    ik.int8_kv_write(w.key, w.value, slots.cuda(), c)
+    out = _attn8(w, t, c)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(8)
+    off = w.token_offsets()
+    cuq = w.cu_seqlens_q().tolist()
+    for b in torch.randperm(w.num_seqs, generator=g)[:10].tolist():
+        ql, L = w.query_lens[b], w.kv_lens[b]
+        i = int(torch.randint(0, ql, (1,), generator=g))
+        pos = L - ql + i
+        kidx = torch.arange(off[b], off[b] + pos + 1).to(w.key.device)
+        sub = wl.Workload("row", w.dtype, 32, 8, 128, w.num_blocks, [pos + 1], [1], [1],
+                          w.block_table[[b]].clone(), w.key[kidx], w.value[kidx],
+                          w.query[cuq[b] + i:cuq[b] + i + 1], w.signs)
+        ref_cache = np.zeros(oracle_mod.cache_shape_int8(w.num_blocks, 16, 8, 128), np.uint8)
+        i2, s2 = sub.token_set("all")
+        oracle_mod.kv_write_int8(wl.bits16(sub.key[i2.to(sub.key.device)]),
+                                 wl.bits16(sub.value[i2.to(sub.key.device)]), "bf16", s2.numpy(),
+                                 ref_cache)
+        assert_attention_close(out[cuq[b] + i:cuq[b] + i + 1], _ref8(oracle_mod, sub, ref_cache),
+                               f"seq {b} row {i}")
