@@ -56,6 +56,12 @@ def _load():
     lib.oracle_decode_row_int8.argtypes = [P, i32, P]
     lib.oracle_attention_plain_int8.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i32,
                                                 P, P, i32, P, i32, f64, i32, f64, P]
+    lib.oracle_lloyd_max4.argtypes = [P, P, P]
+    lib.oracle_quantize_row_int2.argtypes = [P, i32, P, P]
+    lib.oracle_kv_write_int2.argtypes = [P, i64, P, i64, i32, P, i32, P, i32, i32, i32, i32, P]
+    lib.oracle_decode_row_int2.argtypes = [P, i32, P, P]
+    lib.oracle_attention_plain_int2.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i32,
+                                                P, P, i32, P, i32, f64, P, i32, f64, P]
     _lib = lib
     return lib
 
@@ -268,4 +274,75 @@ def attention_plain_int8(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_ta
                                         hkv, d, num_q_heads, _p(cu), _p(su), su.shape[0],
                                         _p(bt), bt.shape[1], float(softmax_scale), int(window),
                                         float(softcap), _p(out))
+    return out
+
+
+# ---- INT2 Lloyd-Max mode: rows of d/4 code bytes (4 codes each) + an fp32 scale,
+# over the same rotation as the INT4 mode
+
+
+def lloyd_max4() -> tuple[float, float, float]:
+    """The 4-level Lloyd-Max quantizer of N(0, 1): levels (a, b) and threshold t
+    (levels -b, -a, a, b; thresholds -t, 0, t)."""
+    v = np.zeros(3, np.float64)
+    _load().oracle_lloyd_max4(_p(v[0:1]), _p(v[1:2]), _p(v[2:3]))
+    return float(v[0]), float(v[1]), float(v[2])
+
+
+def cache_shape_int2(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int):
+    return (num_blocks, 2, block_size, num_kv_heads, head_size // 4 + 4)
+
+
+def quantize_row_int2(y: np.ndarray) -> tuple[np.ndarray, float]:
+    """Quantize one rotated fp32 row: (d/4 code bytes, fp32 scale)."""
+    y = _c(y, np.float32)
+    b = np.zeros(y.size // 4, dtype=np.uint8)
+    s = np.zeros(1, dtype=np.float32)
+    _load().oracle_quantize_row_int2(_p(y), y.size, _p(b), _p(s))
+    return b, float(s[0])
+
+
+def kv_write_int2(key_bits: np.ndarray, value_bits: np.ndarray, dtype: str,
+                  slot_mapping: np.ndarray, cache: np.ndarray, signs: np.ndarray) -> None:
+    """Write tokens into ``cache`` (uint8 [NB, 2, B, Hkv, d/4+4]) in place."""
+    assert cache.dtype == np.uint8 and cache.flags.c_contiguous and cache.ndim == 5
+    nb, two, bs, hkv, r = cache.shape
+    k = _c(key_bits, np.uint16)
+    v = _c(value_bits, np.uint16)
+    T, hk, d = k.shape
+    assert two == 2 and hk == hkv and r == d // 4 + 4 and v.shape == k.shape
+    sm = _c(slot_mapping, np.int64)
+    sg = _c(signs, np.float32)
+    assert sm.shape == (T,) and sg.shape == (d,)
+    _load().oracle_kv_write_int2(_p(k), hkv * d, _p(v), hkv * d, _DT[dtype], _p(sm), T,
+                                 _p(cache), nb, bs, hkv, d, _p(sg))
+
+
+def decode_row_int2(row: np.ndarray, head_size: int, signs: np.ndarray) -> np.ndarray:
+    row = _c(row, np.uint8)
+    sg = _c(signs, np.float32)
+    out = np.zeros(head_size, np.float64)
+    _load().oracle_decode_row_int2(_p(row), head_size, _p(sg), _p(out))
+    return out
+
+
+def attention_plain_int2(q_bits, dtype, cache, cu_seqlens_q, seqused_k, block_table,
+                         softmax_scale, signs, num_q_heads, window: int = 0,
+                         softcap: float = 0.0) -> np.ndarray:
+    """Causal softmax attention over the dequantised INT2 cache, fp64 [Tq, Hq, d]."""
+    q = _c(q_bits, np.uint16)
+    nb, two, bs, hkv, r = cache.shape
+    d = (r - 4) * 4
+    Tq = q.shape[0]
+    assert q.shape == (Tq, num_q_heads, d)
+    cu = _c(cu_seqlens_q, np.int32)
+    su = _c(seqused_k, np.int32)
+    bt = _c(block_table, np.int32)
+    sg = _c(signs, np.float32)
+    out = np.zeros((Tq, num_q_heads, d), np.float64)
+    cache = _c(cache, np.uint8)
+    _load().oracle_attention_plain_int2(_p(q), num_q_heads * d, _DT[dtype], _p(cache), nb, bs,
+                                        hkv, d, num_q_heads, _p(cu), _p(su), su.shape[0],
+                                        _p(bt), bt.shape[1], float(softmax_scale), _p(sg),
+                                        int(window), float(softcap), _p(out))
     return out

@@ -623,3 +623,189 @@ void oracle_attention_plain_int8(const uint16_t* q, int64_t q_stride, int dtype,
     }
   }
 }
+
+/* ==========================================================================
+ * INT2 Lloyd-Max mode ([pr40633] description and its commit on the packed
+ * modes: four 2-bit codes per byte, Hadamard pre-rotation, dequantisation by
+ * a lookup into four centroids fitted over N(0, 1); the mode was dropped from
+ * the merged PR, [report]).
+ *
+ * Readings (listed with the others in the design notes):
+ *   R2-layout cache uint8 [num_blocks][2][block_size][num_kv_heads][d/4 + 4]:
+ *             d/4 code bytes, element 4j + k in bits 2k, 2k+1 of byte j,
+ *             then the fp32 scale, little-endian.
+ *   R2-rot    the INT4 mode's rotation y = H (D x) (R-rht, R-fwht) with the
+ *             caller's signs; the pages' unrandomised "full" Hadamard is the
+ *             case D = I (all signs +1).
+ *   R2-lm     the 4-level Lloyd-Max quantizer of N(0, 1): levels -b, -a, a, b
+ *             for codes 0..3, thresholds -t, 0, t with t = (a + b) / 2
+ *             (nearest level; a value on a threshold takes the upper code).
+ *   R2-scale  s = max(sqrt(sum y_i^2 / d), 1e-6): the row's RMS in the
+ *             rotated domain, which brings a Gaussian-like row to N(0, 1).
+ *             fp32, squares summed pairwise (halves, recursively), then one
+ *             correctly rounded sqrt; inv = fl(1 / s), v = fl(y * inv).  The
+ *             pages' "d1.5 scale factor" is garbled: nothing else is folded
+ *             into the stored scale (parity unpinned for that phrase).
+ *   R2-deq    y_hat_i = s * level(code_i), then x_hat = D (H y_hat) / d.
+ * ========================================================================== */
+
+static double or_npdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846); }
+static double or_ncdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+/* Lloyd's iteration for four levels over N(0, 1), kept symmetric (the density
+ * is): with thresholds 0 and +-t, the levels are the conditional means of
+ * their cells, a = E[X | 0 <= X < t] and b = E[X | X >= t]; then t moves to
+ * the midpoint (a + b) / 2.  Repeated until t stops changing in fp64. */
+void oracle_lloyd_max4(double* a_out, double* b_out, double* t_out) {
+  double t = 1.0, a = 0.0, b = 0.0;
+  for (int it = 0; it < 100000; ++it) {
+    a = (or_npdf(0.0) - or_npdf(t)) / (or_ncdf(t) - 0.5);
+    b = or_npdf(t) / (1.0 - or_ncdf(t));
+    double tn = 0.5 * (a + b);
+    if (tn == t) break;
+    t = tn;
+  }
+  *a_out = a;
+  *b_out = b;
+  *t_out = t;
+}
+
+static int64_t or2_row_offset(int64_t blk, int kv, int64_t off, int h, int block_size,
+                              int num_kv_heads, int d) {
+  int64_t R = d / 4 + 4;
+  return (((blk * 2 + kv) * block_size + off) * num_kv_heads + h) * R;
+}
+
+/* fp32 sum of y_i^2 over [lo, lo + n), n a power of two, by halves. */
+static float or_pairwise_sq(const float* y, int lo, int n) {
+  if (n == 1) return y[lo] * y[lo];
+  return or_pairwise_sq(y, lo, n / 2) + or_pairwise_sq(y, lo + n / 2, n / 2);
+}
+
+/* Quantizes one rotated row: d/4 code bytes and the scale (R2-lm, R2-scale). */
+void oracle_quantize_row_int2(const float* y, int d, uint8_t* bytes, float* scale) {
+  double a, b, t;
+  oracle_lloyd_max4(&a, &b, &t);
+  const float tf = (float)t;
+  float s = sqrtf(or_pairwise_sq(y, 0, d) / (float)d);
+  if (!(s > 1e-6f)) s = 1e-6f;
+  float inv = 1.0f / s;
+  memset(bytes, 0, (size_t)(d / 4));
+  for (int i = 0; i < d; ++i) {
+    float v = y[i] * inv;
+    int code = (v >= -tf) + (v >= 0.0f) + (v >= tf);
+    bytes[i / 4] |= (uint8_t)(code << (2 * (i % 4)));
+  }
+  *scale = s;
+}
+
+/* The INT2 write: rotate (R2-rot) and quantize every (token, head, K|V) row
+ * with slot >= 0; rows of negative slots are untouched. */
+void oracle_kv_write_int2(const uint16_t* key, int64_t key_stride, const uint16_t* value,
+                          int64_t value_stride, int dtype, const int64_t* slot_mapping,
+                          int num_tokens, uint8_t* cache, int num_blocks, int block_size,
+                          int num_kv_heads, int d, const float* signs) {
+  (void)num_blocks;
+  float* y = (float*)malloc(sizeof(float) * (size_t)d);
+  for (int t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    int64_t blk = slot / block_size, off = slot % block_size;
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = kv == 0 ? key + (int64_t)t * key_stride
+                                    : value + (int64_t)t * value_stride;
+      for (int h = 0; h < num_kv_heads; ++h) {
+        for (int i = 0; i < d; ++i) y[i] = or_load(src + (int64_t)h * d + i, dtype);
+        oracle_rht_forward_f32(y, d, signs);
+        uint8_t* row = cache + or2_row_offset(blk, kv, off, h, block_size, num_kv_heads, d);
+        float s;
+        oracle_quantize_row_int2(y, d, row, &s);
+        uint32_t w = or_f32_bits(s);
+        row[d / 4 + 0] = (uint8_t)(w & 0xFF);
+        row[d / 4 + 1] = (uint8_t)((w >> 8) & 0xFF);
+        row[d / 4 + 2] = (uint8_t)((w >> 16) & 0xFF);
+        row[d / 4 + 3] = (uint8_t)((w >> 24) & 0xFF);
+      }
+    }
+  }
+  free(y);
+}
+
+/* Original-domain dequantised row (R2-deq), fp64. */
+void oracle_decode_row_int2(const uint8_t* row, int d, const float* signs, double* out) {
+  double a, b, t;
+  oracle_lloyd_max4(&a, &b, &t);
+  const double level[4] = {-b, -a, a, b};
+  uint32_t w = (uint32_t)row[d / 4] | ((uint32_t)row[d / 4 + 1] << 8) |
+               ((uint32_t)row[d / 4 + 2] << 16) | ((uint32_t)row[d / 4 + 3] << 24);
+  double s = (double)or_bits_f32(w);
+  for (int i = 0; i < d; ++i) out[i] = s * level[(row[i / 4] >> (2 * (i % 4))) & 3];
+  oracle_rht_inverse_f64(out, d, signs);
+}
+
+/* Plain causal softmax attention over the dequantised INT2 cache (fp64), with
+ * the positions, GQA mapping, window and soft cap of the INT4 oracle. */
+void oracle_attention_plain_int2(const uint16_t* q, int64_t q_stride, int dtype,
+                                 const uint8_t* cache, int num_blocks, int block_size,
+                                 int num_kv_heads, int d, int num_q_heads,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                 int num_seqs, const int32_t* block_table, int bt_stride,
+                                 double softmax_scale, const float* signs, int window,
+                                 double softcap, double* out) {
+  (void)num_blocks;
+  int G = num_q_heads / num_kv_heads;
+  for (int bq = 0; bq < num_seqs; ++bq) {
+    int q0 = cu_seqlens_q[bq], qlen = cu_seqlens_q[bq + 1] - cu_seqlens_q[bq];
+    int64_t L = seqused_k[bq];
+    if (qlen <= 0 || L <= 0) continue;
+    for (int h = 0; h < num_kv_heads; ++h) {
+      double* K = (double*)malloc(sizeof(double) * (size_t)(L * d));
+      double* V = (double*)malloc(sizeof(double) * (size_t)(L * d));
+      for (int64_t j = 0; j < L; ++j) {
+        int64_t blk = block_table[(int64_t)bq * bt_stride + j / block_size];
+        oracle_decode_row_int2(
+            cache + or2_row_offset(blk, 0, j % block_size, h, block_size, num_kv_heads, d), d,
+            signs, K + j * d);
+        oracle_decode_row_int2(
+            cache + or2_row_offset(blk, 1, j % block_size, h, block_size, num_kv_heads, d), d,
+            signs, V + j * d);
+      }
+      double* z = (double*)malloc(sizeof(double) * (size_t)L);
+      double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+      for (int i = 0; i < qlen; ++i) {
+        int64_t pos = L - qlen + i;
+        for (int gg = 0; gg < G; ++gg) {
+          int g = h * G + gg;
+          const uint16_t* qrow = q + (int64_t)(q0 + i) * q_stride + (int64_t)g * d;
+          for (int k = 0; k < d; ++k) qv[k] = (double)or_load(qrow + k, dtype);
+          double* o = out + ((int64_t)(q0 + i) * num_q_heads + g) * d;
+          for (int k = 0; k < d; ++k) o[k] = 0.0;
+          if (pos < 0) continue;
+          int64_t jlo = 0;
+          if (window > 0 && pos - window + 1 > 0) jlo = pos - window + 1;
+          double zmax = -INFINITY;
+          for (int64_t j = jlo; j <= pos; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += qv[k] * K[j * d + k];
+            z[j] = softmax_scale * acc;
+            if (softcap > 0.0) z[j] = softcap * tanh(z[j] / softcap);
+            if (z[j] > zmax) zmax = z[j];
+          }
+          double den = 0.0;
+          for (int64_t j = jlo; j <= pos; ++j) {
+            z[j] = exp(z[j] - zmax);
+            den += z[j];
+          }
+          for (int64_t j = jlo; j <= pos; ++j) {
+            double w = z[j] / den;
+            for (int k = 0; k < d; ++k) o[k] += w * V[j * d + k];
+          }
+        }
+      }
+      free(qv);
+      free(z);
+      free(K);
+      free(V);
+    }
+  }
+}
