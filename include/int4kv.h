@@ -266,6 +266,43 @@ int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void
  * rule of int4kv_decode_num_segments for its workgroups of up to 4 KV heads. */
 int32_t int8kv_decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seqlen_k);
 
+/* ---------------------------------------------------------------------------
+ * INT2 Lloyd-Max mode: the other packed mode of the same family ([pr40633]
+ * description and its commit on the packed modes: four 2-bit codes per byte,
+ * Hadamard pre-rotation, dequantisation through four centroids fitted over
+ * N(0, 1); dropped from the merged PR, [report]).
+ *
+ * Cache layout: uint8 [num_blocks][2][block_size][num_kv_heads][head_size/4 + 4];
+ * index 0 of dim 1 is K, 1 is V; a row holds head_size / 4 code bytes
+ * (element 4j + k in bits 2k, 2k+1 of byte j) and then the fp32 scale,
+ * little-endian.  Rows live in the rotated domain of the INT4 mode (same
+ * sign vector; all signs +1 give the plain Hadamard transform).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of an INT2 cache of the given shape, or -1 if a dimension is < 1 or
+ * head_size is not a multiple of 4. */
+int64_t int2kv_cache_bytes(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_size);
+
+/*
+ * int2_kv_write: rotate, quantize and store K and V of `num_tokens` tokens.
+ * For each token t with slot = slot_mapping[t] >= 0, each KV head, K and V,
+ * in fp32 with each operation rounded once:
+ *   y = H (signs * x) (the INT4 mode's rotation and butterfly order);
+ *   s = max(sqrt(sum_i y_i^2 / head_size), 1e-6), the squares summed by
+ *   halves (pairs, then pairs of pairs, ...); inv = fl(1 / s);
+ *   code_i = [v >= -t] + [v >= 0] + [v >= t] with v = fl(y_i * inv) and t =
+ *   0.9815988 (as fp32), the threshold of the 4-level Lloyd-Max quantizer of
+ *   N(0, 1), whose levels are -b, -a, a, b (a = 0.4527800, b = 1.5104176)
+ *   for codes 0..3.  Bit-for-bit reproducible.  Arguments, ownership and
+ *   errors as for int4_kv_write.
+ */
+int4kv_status_t int2_kv_write(const void* key, int64_t key_token_stride, const void* value,
+                              int64_t value_token_stride, int4kv_dtype_t dtype,
+                              const int64_t* slot_mapping, int32_t num_tokens, uint8_t* kv_cache,
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_size, const float* rht_signs, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* int4kv_status_string(int4kv_status_t s);
 

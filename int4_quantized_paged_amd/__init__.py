@@ -70,6 +70,10 @@ def load_library():
                                      i32, i32, P, P, i32, i32, i32, P, i32, ctypes.c_float, i32,
                                      ctypes.c_float, P, i32, P, P, P, P]
     lib.int4_decode_step.restype = ctypes.c_int
+    lib.int2kv_cache_bytes.argtypes = [i32, i32, i32, i32]
+    lib.int2kv_cache_bytes.restype = i64
+    lib.int2_kv_write.argtypes = [P, i64, P, i64, ctypes.c_int, P, i32, P, i32, i32, i32, i32, P,
+                                  P]
     lib.int8kv_cache_bytes.argtypes = [i32, i32, i32, i32]
     lib.int8kv_cache_bytes.restype = i64
     lib.int8_kv_write.argtypes = [P, i64, P, i64, ctypes.c_int, P, i32, P, i32, i32, i32, i32, P]
@@ -186,6 +190,48 @@ def int8_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Te
     _check(lib.int8_kv_write(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
                              _dtype_code(key.dtype), _ptr(slot_mapping.contiguous()), T,
                              _ptr(kv_cache), nb, bs, hkv, key.shape[2], _stream(key.device)))
+
+
+def int2kv_cache_bytes(num_blocks: int, block_size: int, num_kv_heads: int,
+                       head_size: int) -> int:
+    return int(load_library().int2kv_cache_bytes(num_blocks, block_size, num_kv_heads, head_size))
+
+
+def cache_shape_int2(num_blocks: int, num_kv_heads: int, head_size: int, block_size: int = 16):
+    """INT2 Lloyd-Max cache: [num_blocks, 2, block_size, num_kv_heads, head_size/4 + 4] uint8."""
+    return (num_blocks, 2, block_size, num_kv_heads, head_size // 4 + 4)
+
+
+def empty_cache_int2(num_blocks: int, num_kv_heads: int, head_size: int, device="cuda",
+                     block_size: int = 16) -> torch.Tensor:
+    return torch.empty(cache_shape_int2(num_blocks, num_kv_heads, head_size, block_size),
+                       dtype=torch.uint8, device=device)
+
+
+def int2_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                  kv_cache: torch.Tensor, rht_signs: torch.Tensor) -> None:
+    """INT2 Lloyd-Max write of ``key``/``value`` [T, Hkv, d] at ``slot_mapping`` into
+    ``kv_cache`` uint8 [NB, 2, B, Hkv, d/4 + 4], rotated with ``rht_signs`` (fp32 [d]).
+    Enqueued on the current stream."""
+    lib = load_library()
+    T = key.shape[0]
+    if key.dim() != 3 or value.shape != key.shape or key.dtype != value.dtype:
+        raise ValueError("key and value must both be [T, Hkv, d] of one dtype")
+    if key.stride(2) != 1 or key.stride(1) != key.shape[2] or value.stride(2) != 1 or \
+            value.stride(1) != value.shape[2]:
+        raise ValueError("key/value heads must be contiguous ([T, Hkv, d] with a token stride)")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 5 or not kv_cache.is_contiguous() or \
+            kv_cache.shape[4] != key.shape[2] // 4 + 4:
+        raise ValueError("kv_cache must be a contiguous uint8 [NB, 2, B, Hkv, d/4+4] tensor")
+    if rht_signs.dtype != torch.float32 or rht_signs.shape != (key.shape[2],):
+        raise ValueError("rht_signs must be float32 [d]")
+    nb, two, bs, hkv, _ = kv_cache.shape
+    _check(lib.int2_kv_write(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
+                             _dtype_code(key.dtype), _ptr(slot_mapping.contiguous()), T,
+                             _ptr(kv_cache), nb, bs, hkv, key.shape[2],
+                             _ptr(rht_signs.contiguous()), _stream(key.device)))
 
 
 def int8_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,

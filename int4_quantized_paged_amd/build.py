@@ -28,7 +28,8 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 # The LDS-staged decode kernel and the prefill kernel never produce NaN
 # logits (masked keys are selected as -inf, not computed), so their maxima
 # need no NaN quieting.
-PER_FILE = {"write.hip": ["-ffp-contract=off"], "write_int8.hip": ["-ffp-contract=off"], "decode_lds.hip": ["-fno-honor-nans"],
+PER_FILE = {"write.hip": ["-ffp-contract=off"], "write_int8.hip": ["-ffp-contract=off"],
+            "write_int2.hip": ["-ffp-contract=off"], "decode_lds.hip": ["-fno-honor-nans"],
             "prefill.hip": ["-fno-honor-nans"]}
 
 

@@ -251,6 +251,36 @@ int4kv_status_t int8_kv_write(const void* key, int64_t key_token_stride, const v
   return ok();
 }
 
+int64_t int2kv_cache_bytes(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_size) {
+  if (num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_size < 4 || head_size % 4)
+    return -1;
+  return (int64_t)num_blocks * 2 * block_size * num_kv_heads * (head_size / 4 + 4);
+}
+
+int4kv_status_t int2_kv_write(const void* key, int64_t key_token_stride, const void* value,
+                              int64_t value_token_stride, int4kv_dtype_t dtype,
+                              const int64_t* slot_mapping, int32_t num_tokens, uint8_t* kv_cache,
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_size, const float* rht_signs, void* stream) {
+  int4kv_status_t s =
+      check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
+  if (s != INT4KV_OK) return s;
+  if (dtype != INT4KV_F16 && dtype != INT4KV_BF16)
+    return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
+  if (num_tokens < 0) return fail(INT4KV_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  s = check_write_inputs(key, key_token_stride, value, value_token_stride, slot_mapping,
+                         num_kv_heads, head_size);
+  if (s != INT4KV_OK) return s;
+  hipError_t e = int4kv::launch_write_int2(key, key_token_stride, value, value_token_stride,
+                                           dtype == INT4KV_BF16, slot_mapping, num_tokens,
+                                           kv_cache, num_kv_heads, head_size, rht_signs,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void* out,
                                      int4kv_dtype_t dtype, const uint8_t* kv_cache,
                                      int32_t num_blocks, int32_t block_size,

@@ -17,6 +17,13 @@ hipError_t launch_write_int8(const void* key, int64_t key_stride, const void* va
                              int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
                              int32_t head_size, hipStream_t stream);
 
+// INT2 Lloyd-Max mode: rows of head_size / 4 code bytes and an fp32 scale,
+// over the INT4 mode's rotation
+hipError_t launch_write_int2(const void* key, int64_t key_stride, const void* value,
+                             int64_t value_stride, bool bf16, const int64_t* slot_mapping,
+                             int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
+                             int32_t head_size, const float* signs, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   int64_t q_stride;

@@ -657,13 +657,18 @@ static double or_ncdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
  * their cells, a = E[X | 0 <= X < t] and b = E[X | X >= t]; then t moves to
  * the midpoint (a + b) / 2.  Repeated until t stops changing in fp64. */
 void oracle_lloyd_max4(double* a_out, double* b_out, double* t_out) {
-  double t = 1.0, a = 0.0, b = 0.0;
-  for (int it = 0; it < 100000; ++it) {
-    a = (or_npdf(0.0) - or_npdf(t)) / (or_ncdf(t) - 0.5);
-    b = or_npdf(t) / (1.0 - or_ncdf(t));
-    double tn = 0.5 * (a + b);
-    if (tn == t) break;
-    t = tn;
+  static int done = 0; /* computed once per process */
+  static double a = 0.0, b = 0.0, t = 1.0;
+  if (!done) {
+    for (int it = 0; it < 100000; ++it) {
+      a = (or_npdf(0.0) - or_npdf(t)) / (or_ncdf(t) - 0.5);
+      b = or_npdf(t) / (1.0 - or_ncdf(t));
+      double tn = 0.5 * (a + b);
+      double step = fabs(tn - t);
+      t = tn;
+      if (step <= 1e-15) break; /* converged to fp64 resolution */
+    }
+    done = 1;
   }
   *a_out = a;
   *b_out = b;

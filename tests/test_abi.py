@@ -18,7 +18,7 @@ HDR = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "int4k
 def declared_functions():
     text = open(HDR).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(int[48][a-z_0-9]*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(int[248][a-z_0-9]*)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"int4_kv_write", "int4_paged_attention", "int4kv_cache_bytes",
             "int4kv_status_string", "int4kv_last_error", "int8_kv_write",
-            "int8kv_cache_bytes", "int8_paged_attention", "int8kv_decode_num_segments"} <= set(names)
+            "int8kv_cache_bytes", "int8_paged_attention", "int8kv_decode_num_segments",
+            "int2kv_cache_bytes", "int2_kv_write"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(ik.library_path())
@@ -224,3 +225,28 @@ def test_int8_attention_empty_batch_is_a_no_op():
 ])
 def test_int8_decode_num_segments(S, hkv, L, ns):
     assert ik.int8kv_decode_num_segments(S, hkv, L) == ns
+
+
+def _w2(**kw):
+    a = dict(k=FAKE, ks=1024, v=FAKE, vs=1024, dtype=1, slots=FAKE, T=4, cache=FAKE, nb=64, bs=16,
+             hkv=8, d=128, signs=FAKE, stream=None)
+    a.update(kw)
+    return ik.load_library().int2_kv_write(a["k"], a["ks"], a["v"], a["vs"], a["dtype"],
+                                           a["slots"], a["T"], a["cache"], a["nb"], a["bs"],
+                                           a["hkv"], a["d"], a["signs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), 1), (dict(slots=None), 1), (dict(cache=None), 1), (dict(signs=None), 1),
+    (dict(ks=100), 1), (dict(d=96), 2), (dict(bs=32), 2), (dict(dtype=7), 1), (dict(T=-1), 1),
+    (dict(cache=FAKE + 8), 1), (dict(nb=0), 1),
+])
+def test_int2_write_rejects_invalid_host_arguments(kw, status):
+    assert _w2(**kw) == status
+    assert ik.int4kv_last_error() != ""
+
+
+def test_int2_write_empty_is_a_no_op_and_cache_bytes():
+    assert _w2(T=0) == 0
+    assert ik.int2kv_cache_bytes(3, 16, 2, 128) == 3 * 2 * 16 * 2 * 36
+    assert ik.int2kv_cache_bytes(1, 16, 1, 66) == -1
