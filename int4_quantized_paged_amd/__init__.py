@@ -66,6 +66,8 @@ def load_library():
                                          i32, i32, i32, P, i32, ctypes.c_float, i32,
                                          ctypes.c_float, P, i32, P, P, P, P]
     lib.int4_paged_attention.restype = ctypes.c_int
+    lib.int2_paged_attention.argtypes = lib.int4_paged_attention.argtypes
+    lib.int2_paged_attention.restype = ctypes.c_int
     lib.int4_decode_step.argtypes = [P, i64, P, i64, P, P, i64, P, ctypes.c_int, P, i32, i32, i32,
                                      i32, i32, P, P, i32, i32, i32, P, i32, ctypes.c_float, i32,
                                      ctypes.c_float, P, i32, P, P, P, P]
@@ -330,6 +332,43 @@ def int4_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: 
         int(sliding_window), float(softcap), _ptr(rht_signs.contiguous()), int(num_segments),
         _ptr(segm_output),
         _ptr(segm_max), _ptr(segm_expsum), _stream(q.device)))
+    return out
+
+
+def int2_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         seqused_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                         block_table: torch.Tensor, softmax_scale: float,
+                         rht_signs: torch.Tensor, out: torch.Tensor | None = None,
+                         num_segments: int = 1, segm_output: torch.Tensor | None = None,
+                         segm_max: torch.Tensor | None = None,
+                         segm_expsum: torch.Tensor | None = None,
+                         sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
+    """Causal decode attention of ``q`` [S, Hq, d] over the INT2 Lloyd-Max cache
+    (uint8 [NB, 2, B, Hkv, d/4 + 4]); returns ``out``."""
+    lib = load_library()
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [Tq, Hq, d] with contiguous heads")
+    Tq, hq, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, hq, d), dtype=q.dtype, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous with q's shape and dtype")
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 5 or kv_cache.shape[4] != d // 4 + 4:
+        raise ValueError("kv_cache must be uint8 [NB, 2, B, Hkv, d/4+4]")
+    nb, two, bs, hkv, _ = kv_cache.shape
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k),
+                    ("block_table", block_table)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [S, max_blocks] with unit column stride")
+    S = seqused_k.shape[0]
+    _check(lib.int2_paged_attention(
+        _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype), _ptr(kv_cache), nb, bs, hkv, d, hq,
+        _ptr(cu_seqlens_q.contiguous()), _ptr(seqused_k.contiguous()), S, int(max_seqlen_q),
+        int(max_seqlen_k), _ptr(block_table), block_table.stride(0), float(softmax_scale),
+        int(sliding_window), float(softcap), _ptr(rht_signs.contiguous()), int(num_segments),
+        _ptr(segm_output), _ptr(segm_max), _ptr(segm_expsum), _stream(q.device)))
     return out
 
 

@@ -281,6 +281,44 @@ int4kv_status_t int2_kv_write(const void* key, int64_t key_token_stride, const v
   return ok();
 }
 
+int4kv_status_t int2_paged_attention(const void* q, int64_t q_token_stride, void* out,
+                                     int4kv_dtype_t dtype, const uint8_t* kv_cache,
+                                     int32_t num_blocks, int32_t block_size,
+                                     int32_t num_kv_heads, int32_t head_size,
+                                     int32_t num_q_heads, const int32_t* cu_seqlens_q,
+                                     const int32_t* seqused_k, int32_t num_seqs,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     const int32_t* block_table, int32_t block_table_stride,
+                                     float softmax_scale, int32_t sliding_window, float softcap,
+                                     const float* rht_signs, int32_t num_segments,
+                                     float* segm_output, float* segm_max, float* segm_expsum,
+                                     void* stream) {
+  int4kv_status_t s =
+      check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
+  if (s != INT4KV_OK) return s;
+  if (dtype != INT4KV_F16 && dtype != INT4KV_BF16)
+    return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
+  if (num_seqs == 0 || max_seqlen_q == 0) return ok();
+  if (max_seqlen_q != 1)
+    return fail(INT4KV_ERR_UNSUPPORTED, "INT2 mode: decode batches only (max_seqlen_q == 1)");
+  int4kv::AttnArgs a;
+  s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
+                      num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
+                      block_table, block_table_stride, block_size, softmax_scale, sliding_window,
+                      softcap, rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
+  if (s != INT4KV_OK) return s;
+  if (!int4kv::decode_lds_supported(a))
+    return fail(INT4KV_ERR_UNSUPPORTED,
+                "INT2 decode: num_kv_heads %d must be 1, 2, 4 or a multiple of 8", num_kv_heads);
+  a.q2 = true;
+  hipError_t e = int4kv::launch_decode_lds(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int4kv_status_t int8_paged_attention(const void* q, int64_t q_token_stride, void* out,
                                      int4kv_dtype_t dtype, const uint8_t* kv_cache,
                                      int32_t num_blocks, int32_t block_size,

@@ -95,9 +95,18 @@ __device__ __forceinline__ float max16(float x) {
 }
 
 // Compile-time geometry of the LDS image of one tile (two cache blocks).
-template <int D, int HPW, bool Q8 = false>
+// INT2 mode: the 4-level Lloyd-Max quantizer of N(0, 1) (Max, 1960, N = 4)
+// has levels -b, -a, a, b for codes 0..3.  With the code's bits (hi, lo),
+// level + b = (a + b) hi + (b - a) lo = u code + (2v - u) lo, u = (a + b)/2,
+// 2v = b - a: linear in bits, which is what the matrix cores take.
+constexpr float kLmA = 0.4527800346f, kLmB = 1.5104176085f;
+constexpr float kLm2u = kLmA + kLmB, kLm2v = kLmB - kLmA;
+constexpr float kLmU = 0.5f * kLm2u, kLmW = kLm2v - kLmU;
+
+template <int D, int HPW, bool Q8 = false, bool Q2 = false>
 struct Geo {
-  static constexpr uint32_t R = Q8 ? D + 4 : D / 2 + 4;  // row bytes (INT8: d codes + scale)
+  // row bytes (INT8: d codes + scale; INT2: d/4 code bytes + scale)
+  static constexpr uint32_t R = Q8 ? D + 4 : Q2 ? D / 4 + 4 : D / 2 + 4;
   static constexpr uint32_t run = HPW * R;                 // bytes of the group's heads per token
   static constexpr bool kTokenRows = run % 16 == 0;        // token runs are whole chunks
   static constexpr uint32_t TS =                           // LDS token stride
@@ -131,9 +140,9 @@ struct WGeo {
 // deepest ring that fits the 160 KiB of a gfx950 CU, at most 6 for a full
 // 8-head workgroup (one per CU) and at most 4 for smaller ones (several per CU
 // share the LDS).
-template <int D, int G, int HPW, bool Q8 = false>
+template <int D, int G, int HPW, bool Q8 = false, bool Q2 = false>
 struct Lay {
-  using GG = Geo<D, HPW, Q8>;
+  using GG = Geo<D, HPW, Q8, Q2>;
   static constexpr uint32_t qstage = HPW * (G * D * 4 + 2 * G * 4);
   static constexpr uint32_t last = GG::stage > qstage ? GG::stage : qstage;
   static constexpr uint32_t bytes(int s) {
@@ -146,7 +155,7 @@ struct Lay {
   static constexpr uint32_t total = wbase + HPW * WGeo<G>::wtile;
 };
 
-template <bool BF16, int D, int G, int HPW, bool Q8>
+template <bool BF16, int D, int G, int HPW, bool Q8, bool Q2>
 __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, uint16_t* __restrict__ out,
     const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
@@ -157,14 +166,15 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const uint16_t* __restrict__ key_new, int64_t key_new_stride,
     const uint16_t* __restrict__ value_new, int64_t value_new_stride,
     const int64_t* __restrict__ slot_new, int32_t window, float cap2, float inv_cap2) {
-  using GG = Geo<D, HPW, Q8>;
+  using GG = Geo<D, HPW, Q8, Q2>;
   using WG = WGeo<G>;
-  using LY = Lay<D, G, HPW, Q8>;
+  using LY = Lay<D, G, HPW, Q8, Q2>;
   constexpr uint32_t R = GG::R;
-  constexpr int DW = Q8 ? D / 4 : D / 8;  // code dwords per row
+  constexpr int DW = Q8 ? D / 4 : Q2 ? D / 16 : D / 8;  // code dwords per row
   constexpr int DWG = DW / 4;    // code dwords per lane group in the score operand
-  constexpr int NCK = D / 64;    // int8 MFMA k-chunks
-  constexpr int NCOL = D / 16;   // P.V column tiles
+  constexpr int NCK = Q2 ? D / 32 : D / 64;  // int8 MFMA k-chunks (INT2: two bit planes)
+  constexpr int NCOL = D / 16;   // P.V column tiles (INT2: elements per lane)
+  constexpr int NACC = Q2 ? 2 * NCOL : NCOL;  // P.V accumulators
   constexpr int RPG = G <= 4 ? 1 : G / 4;
   constexpr int EPL = G * D / 64;
   constexpr int LPQ = 64 / G;
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // barrier at which tile 0 has landed.  The block is read only by this
   // workgroup, through L2.
   bool store_pending = false;  // this wave stored rows whose completion is still to be awaited
-  if (!Q8 && slot_new != nullptr) {  // (the INT8 mode has no fused step)
+  if (!Q8 && !Q2 && slot_new != nullptr) {  // (the INT8 and INT2 modes have no fused step)
     const int64_t slot = slot_new[b];
     if (slot >= 0 && L > 0 && ((L - 1) / kBlockSize - blo) / per == seg) {  // uniform over the workgroup
       constexpr int WE = 16, WLPR = D / WE, WRPW = kWave / WLPR;  // rows of 8 or 4 lanes
@@ -344,7 +354,9 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const int ex = mx > 0.f ? ilogbf(mx) + 1 : 0;  // |q'| * 2^-ex < 1
     // |v| < 2^22: the centred planes p0, p1 in [-128, 127] then leave the top
     // plane p2 within [-65, 65], so no value is ever clamped
-    const float nrm = ldexpf(1.0f, 22 - ex);
+    // (INT2: below 2^21, so the bit-plane weights, < 2, keep it below 2^22)
+    constexpr int QB = Q2 ? 21 : 22;
+    const float nrm = ldexpf(1.0f, QB - ex);
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -356,7 +368,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     for (int m = 1; m < LPQ; m <<= 1) sum += shfl_xor_rt(sum, m);
     if (s == 0) {
       qinfo[2 * i + 0] = sum;
-      qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - 22);
+      qinfo[2 * i + 1] = scale_log2 * ldexpf(1.0f, ex - QB);
     }
   }
   // tiles 0 .. S-2 now; tile S-1 goes into the last stage once every wave has
@@ -392,9 +404,19 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         uint32_t pw[3] = {0u, 0u, 0u};
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta) {
-          const int j = Q8 ? (4 * k + rho + g) % DWG : (2 * k + (rho >> 1) + g) % DWG;
-          const int d = Q8 ? 4 * (g * DWG + j) + beta : 8 * (g * DWG + j) + 2 * beta + (rho & 1);
-          const int v = ok ? q24[qh * D + d] : 0;
+          int v;
+          if constexpr (Q2) {
+            // chunk k: code dword k / 2 of the lane group, bit plane k % 2
+            // (0: high bits, weight a + b; 1: low bits, weight b - a); slot
+            // (rho, beta) is element 4 beta + rho of that dword
+            const int j = (k / 2 + g) % DWG;
+            const int d = 16 * (g * DWG + j) + 4 * beta + rho;
+            v = ok ? (int)rintf((float)q24[qh * D + d] * ((k & 1) ? kLm2v : kLm2u)) : 0;
+          } else {
+            const int j = Q8 ? (4 * k + rho + g) % DWG : (2 * k + (rho >> 1) + g) % DWG;
+            const int d = Q8 ? 4 * (g * DWG + j) + beta : 8 * (g * DWG + j) + 2 * beta + (rho & 1);
+            v = ok ? q24[qh * D + d] : 0;
+          }
           const int p0 = ((v + 128) & 0xFF) - 128, r1 = (v - p0) >> 8;
           const int p1 = ((r1 + 128) & 0xFF) - 128, p2 = (r1 - p1) >> 8;
           pw[0] |= (uint32_t)(p0 & 0xFF) << (8 * beta);
@@ -419,7 +441,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   float m_run[RPG], thr[RPG], l_run[RPG], corr[RPG];
   // column tile 2*beta: sum of W * (low nibble of byte beta) in units of 2^-24;
   // tile 2*beta + 1: sum of W * (whole byte beta = low + 16 * high nibble)
-  float4_t oacc[NCOL];
+  float4_t oacc[NACC];
 #pragma unroll
   for (int v = 0; v < RPG; ++v) {
     m_run[v] = -INFINITY;  // an empty segment reports m = -inf, l = 0
@@ -428,13 +450,17 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     corr[v] = 0.f;
   }
 #pragma unroll
-  for (int c = 0; c < NCOL; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NACC; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
   const int noff = (D == 64) ? 4 * (col >> 3) : 0;  // nibble offset of this lane's V dword
   // O (rotated domain, zero point not yet removed) of column tile c: the low
   // nibble directly, the high nibble as (byte - low) / 16 (INT4); INT8: every
   // tile holds whole codes offset by 128
   auto o_of = [&](int c, int v) -> float {
     if constexpr (Q8) return oacc[c][v] * 16777216.0f;  // 2^24
+    if constexpr (Q2) {  // element c: u * sum W code + (2v - u) * sum W low bit, scaled by 4^k
+      const float sc = 16777216.0f / (float)(1 << (2 * (c & 3)));
+      return fmaf(kLmU, oacc[2 * c][v], kLmW * oacc[2 * c + 1][v]) * sc;
+    }
     return (c & 1) ? (oacc[c][v] - oacc[c - 1][v]) * 1048576.0f  // 2^20
                    : oacc[c][v] * 16777216.0f;                   // 2^24
   };
@@ -450,13 +476,22 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     vsel[bb] = 0x0C000C00u | by | ((4u + by) << 16);
   }
 
+  // INT2: byte bl of the lane's NCOL / 4 V bytes (elements NCOL * col ..),
+  // of two slot keys' dwords, each zero-extended into an f16 half
+  uint32_t vsel2[Q2 ? NCOL / 4 : 1];
+#pragma unroll
+  for (int bl = 0; bl < (Q2 ? NCOL / 4 : 1); ++bl) {
+    const uint32_t by = (uint32_t)((NCOL / 4) * col + bl) & 3u;
+    vsel2[bl] = 0x0C000C00u | by | ((4u + by) << 16);
+  }
+
   // per-lane LDS byte offsets inside a stage (loop invariant)
   const uint32_t hoff = (uint32_t)wave * R;
   const uint32_t row_off = col * GG::TS + hoff;
   uint32_t k_off[DWG];
 #pragma unroll
   for (int qq = 0; qq < DWG; ++qq) k_off[qq] = row_off + 4 * (g * DWG + (qq + g) % DWG);
-  const uint32_t ks_off = row_off + (Q8 ? D : D / 2);  // + n*BLK (+ lhalf for V)
+  const uint32_t ks_off = row_off + (Q8 ? D : Q2 ? D / 4 : D / 2);  // + n*BLK (+ lhalf for V)
   uint32_t v_off[NVA];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -464,7 +499,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const uint32_t kb0 = (kk >> 4) * GG::BLK + GG::lhalf + (kk & 15) * GG::TS + hoff;
 #pragma unroll
     for (int w = 0; w < NVD; ++w)
-      v_off[j * NVD + w] = kb0 + 4 * (Q8 ? NVD * col + w : col % DW);
+      v_off[j * NVD + w] = kb0 + 4 * (Q8 ? NVD * col + w : Q2 ? NCOL * col / 16 : col % DW);
   }
   // W tile addressing: writer (col, g) -> row qh, dword col; reader (row r, g)
   // -> 16 bytes at dword 4g of its query head's row (or the zero row).  Rows
@@ -490,7 +525,13 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         segw[qq] = *reinterpret_cast<const uint32_t*>(st + n * GG::BLK + k_off[qq]);
 #pragma unroll
       for (int k = 0; k < NCK; ++k) {
-        if constexpr (Q8) {  // int8 codes as they are
+        if constexpr (Q2) {  // one bit plane of a code dword: byte beta, position rho
+          const uint32_t w = segw[k / 2];
+          const int sh = (k & 1) ? 0 : 1;
+#pragma unroll
+          for (int rho = 0; rho < 4; ++rho)
+            kb[n][k][rho] = (int)((w >> (2 * rho + sh)) & 0x01010101u);
+        } else if constexpr (Q8) {  // int8 codes as they are
 #pragma unroll
           for (int rho = 0; rho < 4; ++rho) kb[n][k][rho] = (int)segw[4 * k + rho];
         } else {
@@ -575,10 +616,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       kval[n] = (tb + n < b1) && key < L && key >= lo;
       // INT4: zero point in the scale word's low 4 bits; INT8: a plain fp32
       // scale, no K zero point, and V codes offset by 128 (see the V operands)
-      const float sK = as_float(Q8 ? cw.kw[n] : cw.kw[n] & 0xFFFFFFF0u);
-      const float zK = Q8 ? 0.f : (float)(cw.kw[n] & 0xFu);
-      sV[n] = kval[n] ? as_float(Q8 ? cw.vw[n] : cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked: 0
-      zV[n] = Q8 ? 128.f : (float)(cw.vw[n] & 0xFu);
+      // INT2: plain fp32 scales; the planes give sum q (level + b), so b
+      // leaves through the zero-point terms (K and V alike)
+      const float sK = as_float((Q8 || Q2) ? cw.kw[n] : cw.kw[n] & 0xFFFFFFF0u);
+      const float zK = Q8 ? 0.f : Q2 ? kLmB : (float)(cw.kw[n] & 0xFu);
+      sV[n] = kval[n] ? as_float((Q8 || Q2) ? cw.vw[n] : cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked: 0
+      zV[n] = Q8 ? 128.f : Q2 ? kLmB : (float)(cw.vw[n] & 0xFu);
       const uint32_t keep = kval[n] ? 0xFFFFFFFFu : 0u;
       const uint32_t ninf = kval[n] ? 0u : 0xFF800000u;
 #pragma unroll
@@ -614,7 +657,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         l_run[v] *= alpha;
         corr[v] *= alpha;
 #pragma unroll
-        for (int c = 0; c < NCOL; ++c) oacc[c][v] *= alpha;
+        for (int c = 0; c < NACC; ++c) oacc[c][v] *= alpha;
       }
     }
 
@@ -642,7 +685,37 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const half8_t wop_lo = *reinterpret_cast<const half8_t*>(wt + rd_lo);
     phase_end(1, kb, nxt);
 
-    if constexpr (Q8) {
+    if constexpr (Q2) {
+      // phase 3 (INT2): byte bl of the lane's dword of two slot keys, zero-
+      // extended into f16 halves; element 4 bl + k takes the code (mask
+      // 3 << 2k) and its low bit (mask 1 << 2k), subnormals scaled by 4^k
+      uint32_t vx2[NCOL / 4][4];
+#pragma unroll
+      for (int bl = 0; bl < NCOL / 4; ++bl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vx2[bl][i] = __builtin_amdgcn_perm(cw.va[2 * i + 1], cw.va[2 * i], vsel2[bl]);
+      phase_end(2, kb, nxt);
+#pragma unroll
+      for (int bl = 0; bl < NCOL / 4; ++bl)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = 4 * bl + k;
+          u32x4_t xc, xl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xc[i] = vx2[bl][i] & (0x00030003u << (2 * k));
+            xl[i] = vx2[bl][i] & (0x00010001u << (2 * k));
+          }
+          const half8_t cb = __builtin_bit_cast(half8_t, xc);
+          const half8_t lb = __builtin_bit_cast(half8_t, xl);
+          oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, cb, oacc[2 * e], 0, 0, 0);
+          oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, cb, oacc[2 * e], 0, 0, 0);
+          oacc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, lb, oacc[2 * e + 1], 0, 0, 0);
+          oacc[2 * e + 1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, lb, oacc[2 * e + 1], 0, 0, 0);
+        }
+    } else if constexpr (Q8) {
       // phase 3 (INT8): column tile c takes byte c % 4 of the lane's dword
       // c / 4 of two slot keys, each zero-extended into an f16 half with its
       // top bit flipped: the subnormal (code + 128) * 2^-24, exact in the
@@ -697,7 +770,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
     for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
 #pragma unroll
-    for (int j = 0; j < 2 * NCOL + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
+    for (int j = 0; j < 2 * NACC + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
@@ -743,7 +816,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
   // column tile c holds element dof(c) of this lane
   auto dof = [&](int c) -> int {
-    if constexpr (Q8) return NCOL * col + c;  // the V bytes the lane read
+    if constexpr (Q8 || Q2) return NCOL * col + c;  // the V elements the lane read
     return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
   };
 
@@ -806,13 +879,13 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
 }
 
-template <bool BF16, int D, int G, int HPW, bool Q8>
+template <bool BF16, int D, int G, int HPW, bool Q8, bool Q2>
 hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
-  using LY = Lay<D, G, HPW, Q8>;
+  using LY = Lay<D, G, HPW, Q8, Q2>;
   constexpr size_t lds = LY::total;
   static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 CU");
-  static_assert((LY::S - 2) * Geo<D, HPW, Q8>::NI <= 63, "vmcnt range");
-  auto kern = decode_lds_kernel<BF16, D, G, HPW, Q8>;
+  static_assert((LY::S - 2) * Geo<D, HPW, Q8, Q2>::NI <= 63, "vmcnt range");
+  auto kern = decode_lds_kernel<BF16, D, G, HPW, Q8, Q2>;
   if (lds > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per CU)
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
     if (e != hipSuccess) return e;
@@ -835,36 +908,36 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
 
 // KV heads per workgroup: up to 8 for INT4; up to 4 for INT8, whose rows are
 // twice as long (a two-block tile of 4 heads is 34 KiB: a four-stage ring)
-template <bool BF16, int D, int G, bool Q8>
+template <bool BF16, int D, int G, bool Q8, bool Q2>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   const int cap = Q8 ? 4 : 8;
   switch (a.num_kv_heads >= cap ? cap : a.num_kv_heads) {
-    case 1: return launch_h<BF16, D, G, 1, Q8>(a, stream);
-    case 2: return launch_h<BF16, D, G, 2, Q8>(a, stream);
-    case 4: return launch_h<BF16, D, G, 4, Q8>(a, stream);
+    case 1: return launch_h<BF16, D, G, 1, Q8, Q2>(a, stream);
+    case 2: return launch_h<BF16, D, G, 2, Q8, Q2>(a, stream);
+    case 4: return launch_h<BF16, D, G, 4, Q8, Q2>(a, stream);
     default:
       if constexpr (Q8) return hipErrorInvalidValue;  // not reached: cap is 4
-      else return launch_h<BF16, D, G, 8, Q8>(a, stream);
+      else return launch_h<BF16, D, G, 8, Q8, Q2>(a, stream);
   }
 }
 
-template <bool BF16, int D, bool Q8>
+template <bool BF16, int D, bool Q8, bool Q2>
 hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_t<BF16, D, 1, Q8>(a, stream);
-    case 2: return launch_t<BF16, D, 2, Q8>(a, stream);
-    case 4: return launch_t<BF16, D, 4, Q8>(a, stream);
-    case 8: return launch_t<BF16, D, 8, Q8>(a, stream);
-    default: return launch_t<BF16, D, 16, Q8>(a, stream);
+    case 1: return launch_t<BF16, D, 1, Q8, Q2>(a, stream);
+    case 2: return launch_t<BF16, D, 2, Q8, Q2>(a, stream);
+    case 4: return launch_t<BF16, D, 4, Q8, Q2>(a, stream);
+    case 8: return launch_t<BF16, D, 8, Q8, Q2>(a, stream);
+    default: return launch_t<BF16, D, 16, Q8, Q2>(a, stream);
   }
 }
 
-template <bool Q8>
+template <bool Q8, bool Q2>
 hipError_t launch_q(const AttnArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.head_size == 128 ? launch_d<true, 128, Q8>(a, stream)
-                                        : launch_d<true, 64, Q8>(a, stream);
-  return a.head_size == 128 ? launch_d<false, 128, Q8>(a, stream)
-                            : launch_d<false, 64, Q8>(a, stream);
+  if (a.bf16) return a.head_size == 128 ? launch_d<true, 128, Q8, Q2>(a, stream)
+                                        : launch_d<true, 64, Q8, Q2>(a, stream);
+  return a.head_size == 128 ? launch_d<false, 128, Q8, Q2>(a, stream)
+                            : launch_d<false, 64, Q8, Q2>(a, stream);
 }
 
 }  // namespace
@@ -875,7 +948,9 @@ bool decode_lds_supported(const AttnArgs& a) {
 }
 
 hipError_t launch_decode_lds(const AttnArgs& a, hipStream_t stream) {
-  return a.q8 ? launch_q<true>(a, stream) : launch_q<false>(a, stream);
+  if (a.q8) return launch_q<true, false>(a, stream);
+  if (a.q2) return launch_q<false, true>(a, stream);
+  return launch_q<false, false>(a, stream);
 }
 
 }  // namespace int4kv

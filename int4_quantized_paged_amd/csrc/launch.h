@@ -51,6 +51,9 @@ struct AttnArgs {
   // INT8 per-token-head cache (rows of head_size int8 codes + fp32 scale, no
   // rotation; signs unused) instead of the INT4 one
   bool q8 = false;
+  // INT2 Lloyd-Max cache (rows of head_size / 4 code bytes + fp32 scale, in
+  // the rotated domain of the INT4 mode)
+  bool q2 = false;
   // fused decode step only: the new token of each sequence (token b belongs to
   // sequence b and is its last key), encoded into the cache by the workgroup
   // that reads its block; null otherwise

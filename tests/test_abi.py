@@ -250,3 +250,29 @@ def test_int2_write_empty_is_a_no_op_and_cache_bytes():
     assert _w2(T=0) == 0
     assert ik.int2kv_cache_bytes(3, 16, 2, 128) == 3 * 2 * 16 * 2 * 36
     assert ik.int2kv_cache_bytes(1, 16, 1, 66) == -1
+
+
+def _a2(**kw):
+    a = dict(q=FAKE, qs=4096, out=FAKE, dtype=1, cache=FAKE, nb=64, bs=16, hkv=8, d=128, hq=32,
+             cu=FAKE, su=FAKE, S=4, mq=1, mk=1024, bt=FAKE, bts=64, scale=0.088, win=0, cap=0.0,
+             signs=FAKE, ns=1, so=None, sm=None, ss=None, stream=None)
+    a.update(kw)
+    return ik.load_library().int2_paged_attention(
+        a["q"], a["qs"], a["out"], a["dtype"], a["cache"], a["nb"], a["bs"], a["hkv"], a["d"],
+        a["hq"], a["cu"], a["su"], a["S"], a["mq"], a["mk"], a["bt"], a["bts"], a["scale"],
+        a["win"], a["cap"], a["signs"], a["ns"], a["so"], a["sm"], a["ss"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mq=7), 2), (dict(hkv=3, hq=6), 2), (dict(hkv=12, hq=24), 2), (dict(d=96), 2),
+    (dict(bs=8), 2), (dict(hq=30), 1), (dict(ns=16), 3), (dict(cache=None), 1),
+    (dict(signs=None), 1), (dict(cap=float("nan")), 1), (dict(bts=10), 1),
+])
+def test_int2_attention_rejects_invalid_host_arguments(kw, status):
+    assert _a2(**kw) == status
+    assert ik.int4kv_last_error() != ""
+
+
+def test_int2_attention_empty_batch_is_a_no_op():
+    assert _a2(S=0) == 0
+    assert _a2(mq=0) == 0

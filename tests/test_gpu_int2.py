@@ -1,6 +1,7 @@
 """GPU parity of the INT2 Lloyd-Max mode: the cache write (codes and scale
 words bit for bit against the oracle over the whole cache buffer, sentinel
-bytes included)."""
+bytes included) and decode attention over that cache (|gpu - ref| <= 2e-3 +
+1e-2 |ref| against the oracle's fp64 attention over its own cache)."""
 import random
 
 import numpy as np
@@ -84,3 +85,121 @@ def test_int2_write_llama3_bulk_fill_sampled(oracle_mod):
     got = c.cpu().numpy()
     for s in sl.tolist():
         assert np.array_equal(got[s // 16, :, s % 16], ref[s // 16, :, s % 16]), s
+
+
+# ---- decode attention over the INT2 cache
+
+from tests.gpu_helpers import assert_attention_close, sub_workload, to_dev  # noqa: E402
+
+
+def _int2_cache(oracle_mod, w, t):
+    c = torch.full(ik.cache_shape_int2(w.num_blocks, w.num_kv_heads, w.head_size), SENTINEL,
+                   dtype=torch.uint8, device="cuda")
+    idx, slots = w.token_set("all")
+    ik.int2_kv_write(t["key"][idx.cuda()], t["value"][idx.cuda()], slots.cuda(), c, t["signs"])
+    ref = np.full(oracle_mod.cache_shape_int2(w.num_blocks, 16, w.num_kv_heads, w.head_size),
+                  SENTINEL, np.uint8)
+    oracle_mod.kv_write_int2(wl.bits16(w.key[idx.to(w.key.device)]),
+                             wl.bits16(w.value[idx.to(w.key.device)]),
+                             "bf16" if w.dtype == torch.bfloat16 else "f16", slots.numpy(), ref,
+                             w.signs.numpy())
+    return c, ref
+
+
+def _attn2(w, t, c, ns=1, window=0, softcap=0.0):
+    segs = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns, w.head_size) if ns > 1 else \
+        (None, None, None)
+    return ik.int2_paged_attention(t["query"], c, t["cu"], t["su"], w.max_seqlen_q, w.max_seqlen_k,
+                                   t["block_table"], w.softmax_scale, t["signs"], num_segments=ns,
+                                   segm_output=segs[0], segm_max=segs[1], segm_expsum=segs[2],
+                                   sliding_window=window, softcap=softcap)
+
+
+def _ref2(oracle_mod, w, ref_cache, window=0, softcap=0.0):
+    return oracle_mod.attention_plain_int2(
+        wl.bits16(w.query), "bf16" if w.dtype == torch.bfloat16 else "f16", ref_cache,
+        w.cu_seqlens_q().numpy(), w.seqused_k().numpy(), w.block_table.numpy(), w.softmax_scale,
+        w.signs.numpy(), w.num_q_heads, window=window, softcap=softcap)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_int2_decode_ragged_lengths(oracle_mod, G, d):
+    lens = [(1, 1), (1, 15), (1, 16), (1, 17), (1, 33), (1, 100), (1, 517)]
+    hkv = 4 if G <= 4 else 2
+    w = wl.custom(lens, G * hkv, hkv, d, seed=G * 17 + d, write_all=True, extra_blocks=3)
+    t = to_dev(w)
+    c, ref_cache = _int2_cache(oracle_mod, w, t)
+    assert np.array_equal(c.cpu().numpy(), ref_cache)
+    ref = _ref2(oracle_mod, w, ref_cache)
+    for ns in (1, 2, 5, 64):
+        header(f"int2 decode G={G} d={d} NS={ns}")
+        out = _attn2(w, t, c, ns)
+        torch.cuda.synchronize()
+        assert_attention_close(out, ref, f"int2 G={G} d={d} NS={ns}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 64), (8, 1, 128), (32, 16, 128)])
+def test_int2_decode_heads_window_softcap_large_values(oracle_mod, hq, hkv, d):
+    w = wl.custom([(1, 300), (1, 77), (1, 513), (1, 2000)], hq, hkv, d, seed=hq + hkv + d,
+                  write_all=True, scale=3.0)
+    t = to_dev(w)
+    c, ref_cache = _int2_cache(oracle_mod, w, t)
+    for window, cap in ((0, 0.0), (100, 0.0), (0, 5.0), (300, 30.0)):
+        ref = _ref2(oracle_mod, w, ref_cache, window, cap)
+        for ns in (1, 16):
+            header(f"int2 decode {hq}/{hkv} d{d} window={window} cap={cap} NS={ns}")
+            out = _attn2(w, t, c, ns, window, cap)
+            torch.cuda.synchronize()
+            assert_attention_close(out, ref, f"window {window} cap {cap} NS={ns}")
+    w30 = wl.custom([(1, 300), (1, 77), (1, 513), (1, 160)] * 2, hq, hkv, d, seed=5 + hq,
+                    write_all=True, scale=30.0, dtype=torch.float16)
+    t30 = to_dev(w30)
+    c30, ref30 = _int2_cache(oracle_mod, w30, t30)
+    for ns in (1, 7):
+        header(f"int2 decode large values {hq}/{hkv} d{d} NS={ns}")
+        assert_attention_close(_attn2(w30, t30, c30, ns), _ref2(oracle_mod, w30, ref30),
+                               f"large values NS={ns}")
+
+
+def test_int2_decode_empty_and_zero_length(oracle_mod):
+    w = wl.custom([(1, 40), (0, 20), (1, 0), (1, 9)], 8, 2, 128, seed=4, write_all=True)
+    t = to_dev(w)
+    c, ref_cache = _int2_cache(oracle_mod, w, t)
+    ref = _ref2(oracle_mod, w, ref_cache)
+    for ns in (1, 3):
+        header(f"int2 decode empty / zero-length NS={ns}")
+        out = _attn2(w, t, c, ns)
+        torch.cuda.synchronize()
+        assert_attention_close(out, ref, f"NS={ns}")
+        assert torch.all(out[1].float() == 0.0)
+
+
+def test_int2_decode_llama3_full_size_sampled(oracle_mod):
+    """64 x 4096, 32 q / 8 KV heads, in the launch the benchmark times (the
+    library's split count); 3 sampled sequences against the oracle."""
+    w = wl.llama3_8b_decode(device="cuda")
+    ns = ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads, w.max_seqlen_k)
+    header(f"int2 Llama-3-8B-shaped decode full size NS={ns}")
+    t = to_dev(w)
+    c = torch.empty(ik.cache_shape_int2(w.num_blocks, 8, 128), dtype=torch.uint8, device="cuda")
+    idx, slots = w.token_set("all")
+    ik.int2_kv_write(w.key, w.value, slots.cuda(), c, t["signs"])
+    out = _attn2(w, t, c, ns)
+    torch.cuda.synchronize()
+    for seqs in ([0], [37], [63]):
+        ws = sub_workload(w, seqs)
+        ref_cache = np.zeros(oracle_mod.cache_shape_int2(ws.num_blocks, 16, 8, 128), np.uint8)
+        i2, s2 = ws.token_set("all")
+        oracle_mod.kv_write_int2(wl.bits16(ws.key[i2.to(ws.key.device)]),
+                                 wl.bits16(ws.value[i2.to(ws.key.device)]), "bf16", s2.numpy(),
+                                 ref_cache, ws.signs.numpy())
+        assert_attention_close(out[seqs], _ref2(oracle_mod, ws, ref_cache), f"seq {seqs}")
+
+
+def test_int2_prefill_is_unsupported():
+    w = wl.custom([(4, 40)], 8, 2, 128, seed=1, write_all=True)
+    t = to_dev(w)
+    c = torch.zeros(ik.cache_shape_int2(w.num_blocks, 2, 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ik.Int4KVError):
+        _attn2(w, t, c)
