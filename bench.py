@@ -345,6 +345,19 @@ def other_rows(dev):
         "bulk_us": round(fill8_us, 1), "bulk_tokens_per_s": round(T / fill8_us * 1e6, 1),
         "bulk_GBps": round(bytes8 / fill8_us / 1e3, 1)}
     del cache8, fill8
+    # the INT2 Lloyd-Max mode's bulk fill (rows of d / 4 + 4 bytes, same rotation)
+    sg = w.signs.to(dev)
+    cache2 = ik.empty_cache_int2(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)
+    fill2 = lambda: ik.int2_kv_write(w.key, w.value, slots_all, cache2, sg)  # noqa: E731
+    for _ in range(2):
+        fill2()
+    fill2_us = _median_event_us(fill2, 3)
+    bytes2 = T * w.num_kv_heads * 2 * (2 * w.head_size + (w.head_size // 4 + 4)) + 8 * T
+    rows["llama3_8b_write_int2"] = {
+        "workload": "INT2 Lloyd-Max bulk fill of the same 262144 tokens (rows of 36 bytes)",
+        "bulk_us": round(fill2_us, 1), "bulk_tokens_per_s": round(T / fill2_us * 1e6, 1),
+        "bulk_GBps": round(bytes2 / fill2_us / 1e3, 1)}
+    del cache2, fill2
     best = None
     for ns in (1, 2, 4, 8):
         call = _attention_setup(w, dev, ns, ncaches=2)
@@ -402,6 +415,39 @@ def other_rows(dev):
         "timing": "20 calls (two caches alternating) replayed from one HIP graph, per call",
         "GBps": round(kv8 / us8 / 1e3, 1), "hbm_frac": round(kv8 / us8 / 1e3 / HBM_PEAK_GBS, 4),
         "kv_bytes_vs_int4": round(kv8 / kv, 3)}
+    del c8
+
+    # ... and over the INT2 Lloyd-Max cache (36-byte rows, same rotation and
+    # split rule as INT4)
+    c2 = [ik.empty_cache_int2(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)]
+    ik.int2_kv_write(w.key, w.value, slots8.to(dev), c2[0], sg)
+    c2.append(c2[0].clone())
+    st2 = {"i": 0}
+    best2 = None
+    for ns2 in (2, 4, 8):
+        segs2 = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns2, w.head_size, dev)
+
+        def call2():
+            c = c2[st2["i"] % 2]
+            st2["i"] += 1
+            ik.int2_paged_attention(w.query, c, cu, su, 1, w.max_seqlen_k, bt, w.softmax_scale, sg,
+                                    out=out8, num_segments=ns2, segm_output=segs2[0],
+                                    segm_max=segs2[1], segm_expsum=segs2[2])
+        for _ in range(3):
+            call2()
+        us2 = _graph_us(call2, 20)
+        if best2 is None or us2 < best2[1]:
+            best2 = (ns2, us2)
+    ns2, us2 = best2
+    kv2 = sum(w.kv_lens) * w.num_kv_heads * 2 * (w.head_size // 4 + 4)
+    rows["llama3_8b_decode_int2"] = {
+        "workload": "the same 64 x 4096 batch over the INT2 Lloyd-Max cache (36-byte rows)",
+        "num_segments": ns2, "us": round(us2, 2),
+        "num_segments_library_choice": ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads,
+                                                                     w.max_seqlen_k),
+        "timing": "20 calls (two caches alternating) replayed from one HIP graph, per call",
+        "GBps": round(kv2 / us2 / 1e3, 1), "hbm_frac": round(kv2 / us2 / 1e3 / HBM_PEAK_GBS, 4),
+        "kv_bytes_vs_int4": round(kv2 / kv, 3)}
     return rows
 
 
