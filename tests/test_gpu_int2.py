@@ -139,8 +139,11 @@ def test_int2_decode_ragged_lengths(oracle_mod, G, d):
         assert_attention_close(out, ref, f"int2 G={G} d={d} NS={ns}")
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 64), (8, 1, 128), (32, 16, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 64), (8, 1, 128), (32, 16, 128),
+                                      (128, 8, 128)])
 def test_int2_decode_heads_window_softcap_large_values(oracle_mod, hq, hkv, d):
+    """(128, 8, 128) is the instance with 8 heads of 16 query heads per
+    workgroup, which keeps part of its state in scratch."""
     w = wl.custom([(1, 300), (1, 77), (1, 513), (1, 2000)], hq, hkv, d, seed=hq + hkv + d,
                   write_all=True, scale=3.0)
     t = to_dev(w)
