@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
 }
 
 // Segment reduction for up to 64 segments: one wave per (sequence, query
-// head), four per workgroup.  Lane k holds segment k's maximum and exp-sum;
+// head), one per workgroup.  Lane k holds segment k's maximum and exp-sum;
 // all of the row's partial accumulators are loaded at once and merged in
 // registers in segment order (the same log-sum-exp as below), then rotated
 // back; no LDS and no barrier, which is what a launch of many short rows is
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(
     const float* __restrict__ segm_sum) {
   constexpr int EPL = D / 64;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= num_rows) return;  // uniform over the wave; nothing below synchronises waves
   const int b = row / num_q_heads, qg = row % num_q_heads;
   const int q0 = cu_seqlens_q[b];
@@ -703,7 +703,10 @@ hipError_t launch_reduce_t(const AttnArgs& a, hipStream_t stream) {
     const int rows = a.num_seqs * a.num_q_heads;
     auto kern = a.num_segments <= 16 ? reduce_wave_kernel<BF16, D, 16>
                                      : reduce_wave_kernel<BF16, D, kWaveSegments>;
-    hipLaunchKernelGGL(kern, dim3((rows + 3) / 4), dim3(256), 0, stream,
+    // one wave per workgroup, so the rows spread over the CUs (the same 4.6 us
+    // as four waves per workgroup on the long-context batch's 256 rows: each
+    // wave is bound by the latency of its own loads)
+    hipLaunchKernelGGL(kern, dim3(rows), dim3(64), 0, stream,
                        reinterpret_cast<uint16_t*>(a.out), a.num_q_heads, rows, a.cu_seqlens_q,
                        a.q8 ? nullptr : a.signs, a.num_segments, a.segm_out, a.segm_max,
                        a.segm_sum);

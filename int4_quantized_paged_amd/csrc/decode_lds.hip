@@ -910,13 +910,16 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
 // twice as long (a two-block tile of 4 heads is 34 KiB: a four-stage ring)
 template <bool BF16, int D, int G, bool Q8, bool Q2>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-  const int cap = Q8 ? 4 : 8;
+  // INT2 with 16 query heads per KV head at d = 128 also takes 4: its 8-head
+  // instance does not fit in 256 VGPRs (it spills to scratch)
+  const int cap = (Q8 || (Q2 && G == 16 && D == 128)) ? 4 : 8;
   switch (a.num_kv_heads >= cap ? cap : a.num_kv_heads) {
     case 1: return launch_h<BF16, D, G, 1, Q8, Q2>(a, stream);
     case 2: return launch_h<BF16, D, G, 2, Q8, Q2>(a, stream);
     case 4: return launch_h<BF16, D, G, 4, Q8, Q2>(a, stream);
     default:
-      if constexpr (Q8) return hipErrorInvalidValue;  // not reached: cap is 4
+      if constexpr (Q8 || (Q2 && G == 16 && D == 128))
+        return hipErrorInvalidValue;  // not reached: cap is 4
       else return launch_h<BF16, D, G, 8, Q8, Q2>(a, stream);
   }
 }

@@ -71,12 +71,17 @@ def oracle_attention(orc, w, cache, window=0, softcap=0.0):
                                w.signs.numpy(), w.num_q_heads, window=window, softcap=softcap)
 
 
-def assert_attention_close(got, ref, what=""):
+def assert_attention_close(got, ref, what="", data_scale=1.0):
+    """|got - ref| <= 2e-3 * data_scale + 1e-2 |ref|.  The absolute term is set
+    for unit-scale K/V; the kernels' fp32 rounding (the rotated-domain sums
+    and their inverse rotation, whose outputs can cancel to near zero) is
+    relative to the magnitude of the data, so inputs scaled by c pass c."""
     g = got.float().cpu().numpy().astype(np.float64)
     err = np.abs(g - ref)
-    bound = ATOL + RTOL * np.abs(ref)
+    bound = ATOL * data_scale + RTOL * np.abs(ref)
     bad = err > bound
-    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside 2e-3 + 1e-2|ref|; "
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside "
+                           f"{ATOL * data_scale:.3g} + 1e-2|ref|; "
                            f"max err {err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
     return float(err.max())
 
