@@ -268,7 +268,24 @@ def other_rows(dev):
                     f"{sum(w.kv_lens)} keys, 32 q / 8 KV heads, d 128",
         "us": round(us, 2), "tflops": round(fl / us / 1e6, 1),
         "mfma_frac": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)}
-    del w, c8, q, out
+    del c8
+    # ... and over the INT2 Lloyd-Max cache
+    sg2 = w.signs.to(dev)
+    c2 = ik.empty_cache_int2(w.num_blocks, w.num_kv_heads, 128, device=dev)
+    ik.int2_kv_write(w.key, w.value, slots.to(dev), c2, sg2)
+
+    def call2():
+        ik.int2_paged_attention(q, c2, cu, su, w.max_seqlen_q, w.max_seqlen_k, bt,
+                                w.softmax_scale, sg2, out=out)
+    for _ in range(3):
+        call2()
+    us = _median_event_us(call2, 10)
+    rows["prefill_int2_d128"] = {
+        "workload": f"chunked-prefill mix over the INT2 cache: {sum(w.query_lens)} query tokens, "
+                    f"{sum(w.kv_lens)} keys, 32 q / 8 KV heads, d 128",
+        "us": round(us, 2), "tflops": round(fl / us / 1e6, 1),
+        "mfma_frac": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)}
+    del w, c2, q, out
     # GQA decode: 8 sequences of 1..1024 keys, one new token each, in one
     # int4_decode_step (latency-bound: reported in us and GB/s, not against HBM peak)
     w = wl.gqa_decode(device=dev)

@@ -304,16 +304,16 @@ int4kv_status_t int2_kv_write(const void* key, int64_t key_token_stride, const v
                               int32_t head_size, const float* rht_signs, void* stream);
 
 /*
- * int2_paged_attention: causal decode attention (one query row per sequence)
+ * int2_paged_attention: causal attention (decode and prefill / mixed batches)
  * over the INT2 cache: softmax(softmax_scale * q . k_hat) . v_hat with k_hat,
  * v_hat = D H (s * level(code)) / head_size (levels -b, -a, a, b as in
  * int2_kv_write; [pr40633] description: centroid lookup on the read side,
  * scores over the rotated query).  Arguments, window, soft cap, split-K
  * segments (sized with int4kv_decode_num_segments) and errors as for
- * int4_paged_attention.  Supported: max_seqlen_q == 1 (decode batches; a
- * larger value returns INT4KV_ERR_UNSUPPORTED), head_size 64 or 128,
- * block_size 16, num_kv_heads 1, 2, 4 or a multiple of 8, query heads per KV
- * head in {1, 2, 4, 8, 16}.
+ * int4_paged_attention (the segments are used only when max_seqlen_q == 1).
+ * Supported: head_size 64 or 128, block_size 16, query heads per KV head in
+ * {1, 2, 4, 8, 16}; decode batches also need num_kv_heads 1, 2, 4 or a
+ * multiple of 8 (else INT4KV_ERR_UNSUPPORTED).
  */
 int4kv_status_t int2_paged_attention(const void* q, int64_t q_token_stride, void* out,
                                      int4kv_dtype_t dtype, const uint8_t* kv_cache,

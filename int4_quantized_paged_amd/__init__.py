@@ -343,8 +343,8 @@ def int2_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: 
                          segm_max: torch.Tensor | None = None,
                          segm_expsum: torch.Tensor | None = None,
                          sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
-    """Causal decode attention of ``q`` [S, Hq, d] over the INT2 Lloyd-Max cache
-    (uint8 [NB, 2, B, Hkv, d/4 + 4]); returns ``out``."""
+    """Causal attention of ``q`` [Tq, Hq, d] (decode or prefill / mixed batches) over
+    the INT2 Lloyd-Max cache (uint8 [NB, 2, B, Hkv, d/4 + 4]); returns ``out``."""
     lib = load_library()
     if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
         raise ValueError("q must be [Tq, Hq, d] with contiguous heads")

@@ -301,19 +301,19 @@ int4kv_status_t int2_paged_attention(const void* q, int64_t q_token_stride, void
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
   if (num_seqs == 0 || max_seqlen_q == 0) return ok();
-  if (max_seqlen_q != 1)
-    return fail(INT4KV_ERR_UNSUPPORTED, "INT2 mode: decode batches only (max_seqlen_q == 1)");
+  const bool decode = max_seqlen_q == 1;
   int4kv::AttnArgs a;
   s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
                       num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
                       block_table, block_table_stride, block_size, softmax_scale, sliding_window,
                       softcap, rht_signs, num_segments, segm_output, segm_max, segm_expsum, a);
   if (s != INT4KV_OK) return s;
-  if (!int4kv::decode_lds_supported(a))
+  if (decode && !int4kv::decode_lds_supported(a))
     return fail(INT4KV_ERR_UNSUPPORTED,
                 "INT2 decode: num_kv_heads %d must be 1, 2, 4 or a multiple of 8", num_kv_heads);
   a.q2 = true;
-  hipError_t e = int4kv::launch_decode_lds(a, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = decode ? int4kv::launch_decode_lds(a, st) : int4kv::launch_prefill(a, st);
   if (e != hipSuccess)
     return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
   return ok();

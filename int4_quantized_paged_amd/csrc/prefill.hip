@@ -34,6 +34,10 @@
 //    rotation and d + 4 byte rows: K and V codes enter as bytes with the top
 //    bit flipped, (code + 128) * 2^-24, the 128 leaving through the same
 //    zero-point terms, and Q is staged unrotated.
+//  * The INT2 Lloyd-Max cache (Q2 set) keeps the INT4 rotation; its 2-bit
+//    codes become their levels as f16 hi + lo pairs through a v_perm table
+//    lookup, so K and V enter the same MFMAs as signed values with no
+//    zero point (three products where the codes take two).
 #include "device_common.h"
 #include "launch.h"
 
@@ -78,11 +82,33 @@ __device__ __forceinline__ float max16(float x) {
   return x;
 }
 
-template <int D, int G, bool Q8 = false>
+// INT2 mode: f16 bits of the 4-level Lloyd-Max levels of N(0, 1) (Max, 1960,
+// N = 4: -b, -a, a, b for codes 0..3, a = 0.45278003, b = 1.51041761) as
+// hi + lo pairs, two codes' levels per dword through one v_perm.
+constexpr float kLmA = 0.4527800346f, kLmB = 1.5104176085f;
+constexpr _Float16 kLh0 = (_Float16)(-kLmB), kLh1 = (_Float16)(-kLmA), kLh2 = (_Float16)kLmA,
+                   kLh3 = (_Float16)kLmB;
+constexpr _Float16 kLl0 = (_Float16)(-kLmB - (float)kLh0), kLl1 = (_Float16)(-kLmA - (float)kLh1),
+                   kLl2 = (_Float16)(kLmA - (float)kLh2), kLl3 = (_Float16)(kLmB - (float)kLh3);
+constexpr uint32_t f16pair(_Float16 x, _Float16 y) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+constexpr uint32_t kTh0 = f16pair(kLh0, kLh1), kTh1 = f16pair(kLh2, kLh3);
+constexpr uint32_t kTl0 = f16pair(kLl0, kLl1), kTl1 = f16pair(kLl2, kLl3);
+
+// levels of codes c0 (half 0) and c1 (half 1), each 0..3: hi and lo f16 pairs
+__device__ __forceinline__ void lm_pair(uint32_t c0, uint32_t c1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t sel = 0x01000100u + (c0 | (c1 << 16)) * 0x0202u;  // bytes 2c, 2c + 1
+  hi = __builtin_amdgcn_perm(kTh1, kTh0, sel);
+  lo = __builtin_amdgcn_perm(kTl1, kTl0, sel);
+}
+
+template <int D, int G, bool Q8 = false, bool Q2 = false>
 struct PGeo {
-  static constexpr int R = Q8 ? D + 4 : D / 2 + 4;  // row bytes (INT8: d codes + scale)
-  static constexpr int RW = R / 4;                  // dwords per row (INT4 17 or 9, INT8 33 or 17)
-  static constexpr int DW = Q8 ? D / 4 : D / 8;     // code dwords per row
+  // row bytes (INT8: d codes + scale; INT2: d/4 code bytes + scale)
+  static constexpr int R = Q8 ? D + 4 : Q2 ? D / 4 + 4 : D / 2 + 4;
+  static constexpr int RW = R / 4;                  // dwords per row
+  static constexpr int DW = Q8 ? D / 4 : Q2 ? D / 16 : D / 8;  // code dwords per row
   static constexpr int NIB = (16 * RW + 63) / 64; // copies per (block, K|V) image
   static constexpr uint32_t HALF = NIB * 256;     // LDS bytes of one (block, K|V) image
   static constexpr uint32_t STAGE = 4 * HALF;     // two blocks, K and V
@@ -100,7 +126,7 @@ struct PGeo {
   static constexpr int TQ = 128 / G;              // query tokens per workgroup
 };
 
-template <bool BF16, int D, int G, bool Q8>
+template <bool BF16, int D, int G, bool Q8, bool Q2>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, uint16_t* __restrict__ out,
     const uint8_t* __restrict__ cache, int32_t num_kv_heads, int32_t num_q_heads,
@@ -108,7 +134,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
     const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq, int32_t window,
     float cap2, float inv_cap2) {
-  using PG = PGeo<D, G, Q8>;
+  using PG = PGeo<D, G, Q8, Q2>;
   constexpr int R = PG::R, RW = PG::RW, DW = PG::DW, NIB = PG::NIB;
   constexpr int NCH = D / 32;   // f16 MFMA k-chunks of the score
   constexpr int NCOL = D / 16;  // P.V column tiles
@@ -202,9 +228,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         sum += (float)hv + (float)lv;
         // INT4 operand order [e0 e4 e1 e5 e2 e6 e3 e7], odd elements against
         // codes scaled by 16; INT8 [e0 e2 e1 e3 e4 e6 e5 e7], codes as they are
-        const int slot = Q8 ? (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1) : ((j & 3) << 1) | (j >> 2);
-        hi8[slot] = (!Q8 && (j & 1)) ? (_Float16)((float)hv * 0.0625f) : hv;
-        lo8[slot] = (!Q8 && (j & 1)) ? (_Float16)((float)lv * 0.0625f) : lv;
+        // (INT2: natural order, against the levels of 8 consecutive codes)
+        const int slot = Q2 ? j : Q8 ? (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1)
+                                     : ((j & 3) << 1) | (j >> 2);
+        hi8[slot] = (!Q8 && !Q2 && (j & 1)) ? (_Float16)((float)hv * 0.0625f) : hv;
+        lo8[slot] = (!Q8 && !Q2 && (j & 1)) ? (_Float16)((float)lv * 0.0625f) : lv;
       }
       const int el = s * EPL + 8 * e8;
       const int off = ((row * 2 + 0) * NCH + el / 32) * 32 + ((el % 32) / 8) * 8;
@@ -213,7 +241,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }
     sum += shfl_xor<1>(sum);
     if (s == 0) sinfo[row] = sum * 5.9604644775390625e-08f;  // sum(q') in 2^-24 code units
-    if (lane == 0) sinfo[128 + wq] = scale_log2 * ldexpf(1.0f, ex - 10 + 24);
+    // codes enter as 2^-24 units, INT2 levels as themselves
+    if (lane == 0) sinfo[128 + wq] = scale_log2 * ldexpf(1.0f, ex - 10 + (Q2 ? 0 : 24));
   }
   __syncthreads();
 
@@ -288,8 +317,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const uint32_t krow = (uint32_t)col * RW * 4;  // key col's record in a (block, K) image
   uint32_t k_off[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c)  // INT8: two dwords (8 codes) per lane group and chunk
-    k_off[c] = krow + (uint32_t)(4 * c + g) * (Q8 ? 8 : 4);
+  for (int c = 0; c < NCH; ++c)  // INT8: two dwords (8 codes) per lane group and chunk;
+    // INT2: half a dword (8 codes), dword 2c + g/2
+    k_off[c] = krow + (Q2 ? (uint32_t)(2 * c + g / 2) * 4 : (uint32_t)(4 * c + g) * (Q8 ? 8 : 4));
   const uint32_t s_off = krow + (uint32_t)(RW - 1) * 4;  // scale word
   // INT8 V: the lane's elements NCOL * col .. + NCOL - 1 are NVD dwords of a row
   constexpr int NVD = Q8 ? NCOL / 4 : 1;
@@ -300,7 +330,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 #pragma unroll
     for (int w = 0; w < NVD; ++w)
       v_off[j * NVD + w] = (uint32_t)(2 * n + 1) * PG::HALF + (uint32_t)t * RW * 4 +
-                           (uint32_t)(Q8 ? NVD * col + w : col % DW) * 4;
+                           (uint32_t)(Q8 ? NVD * col + w : Q2 ? NCOL * col / 16 : col % DW) * 4;
   }
   unsigned char* wt = smem + PG::LOW + wave * PG::WTILE;
   // W tile: the f16 pair of key col (blocks 0 and 1) of row r sits at dword
@@ -344,8 +374,46 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const unsigned char* st = smem + (uint32_t)(t % kStages) * PG::STAGE;
 
     // K operands: raw code dword (block n, chunk c) -> 4 dwords of f16 subnormals
-    half8_t kb[2][NCH];
+    uint32_t va[8 * NVD];
+#pragma unroll
+    for (int j = 0; j < 8 * NVD; ++j) va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
+    half8_t kb[2][Q2 ? 1 : NCH];
     uint32_t kw[2], vw[2];
+    float4_t sacc[2][2];
+    if constexpr (Q2) {
+      // INT2: each chunk's level operands (hi, lo) feed the score MFMAs at
+      // once: S = q_hi L_hi + q_lo L_hi + q_hi L_lo (L_lo q_lo is 2^-22 below)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) sacc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + k_off[c]);
+          const uint32_t u = w >> (16 * (g & 1));
+          u32x4_t lh, ll;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            uint32_t h2, l2;
+            lm_pair((u >> (4 * m)) & 3u, (u >> (4 * m + 2)) & 3u, h2, l2);
+            lh[m] = h2;
+            ll[m] = l2;
+          }
+          const half8_t kh = __builtin_bit_cast(half8_t, lh);
+          const half8_t kl = __builtin_bit_cast(half8_t, ll);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            sacc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[i][c], kh, sacc[i][n], 0, 0, 0);
+            sacc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[i][c], kh, sacc[i][n], 0, 0, 0);
+            sacc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[i][c], kl, sacc[i][n], 0, 0, 0);
+          }
+        }
+        kw[n] = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + s_off);
+        vw[n] = *reinterpret_cast<const uint32_t*>(st + (2 * n + 1) * PG::HALF + s_off);
+      }
+    } else {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
 #pragma unroll
@@ -370,12 +438,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       kw[n] = *reinterpret_cast<const uint32_t*>(st + 2 * n * PG::HALF + s_off);
       vw[n] = *reinterpret_cast<const uint32_t*>(st + (2 * n + 1) * PG::HALF + s_off);
     }
-    uint32_t va[8 * NVD];
-#pragma unroll
-    for (int j = 0; j < 8 * NVD; ++j) va[j] = *reinterpret_cast<const uint32_t*>(st + v_off[j]);
 
     // scores: S[i][n] for row tile i, keys 16n + col (sum of q' * code * 2^-24)
-    float4_t sacc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -388,6 +452,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         }
         sacc[i][n] = a;
       }
+    }
 
     // online softmax (base 2) per row; keys past a row's position are masked
     // uniform: only tiles near the diagonal, or near a row's window start
@@ -397,10 +462,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     for (int n = 0; n < 2; ++n) {
       // INT4: zero points in the scale words' low 4 bits; INT8: plain fp32
       // scales, and the codes enter offset by 128 (K and V alike)
-      sKc[n] = as_float(Q8 ? kw[n] : kw[n] & 0xFFFFFFF0u) * c0;
-      zK[n] = Q8 ? 128.f : (float)(kw[n] & 0xFu);
-      sV[n] = as_float(Q8 ? vw[n] : vw[n] & 0xFFFFFFF0u);
-      zV[n] = Q8 ? 128.f : (float)(vw[n] & 0xFu);
+      // (INT2: plain scales and signed levels, no zero point)
+      sKc[n] = as_float((Q8 || Q2) ? kw[n] : kw[n] & 0xFFFFFFF0u) * c0;
+      zK[n] = Q8 ? 128.f : Q2 ? 0.f : (float)(kw[n] & 0xFu);
+      sV[n] = as_float((Q8 || Q2) ? vw[n] : vw[n] & 0xFFFFFFF0u);
+      zV[n] = Q8 ? 128.f : Q2 ? 0.f : (float)(vw[n] & 0xFu);
     }
     // logits in base-2 units; the reference maximum m of a row only moves
     // when a logit exceeds it by more than kLazy (so p = 2^(z - m) <= 2^kLazy),
@@ -487,7 +553,30 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     // takes byte c % 4 of the lane's dword c / 4 of two slot keys, top bit
     // flipped: the subnormal (code + 128) * 2^-24 (the 128 leaves through the
     // zero-point term, zV = 128).
-    if constexpr (Q8) {
+    if constexpr (Q2) {
+      // INT2: column tile c is element NCOL col + c of 8 slot keys; their
+      // levels as hi + lo f16 pairs: O += W_hi L_hi + W_lo L_hi + W_hi L_lo
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) {
+        const int sh = 2 * ((NCOL * col + c) & 15);
+        u32x4_t lh, ll;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t h2, l2;
+          lm_pair((va[2 * k] >> sh) & 3u, (va[2 * k + 1] >> sh) & 3u, h2, l2);
+          lh[k] = h2;
+          ll[k] = l2;
+        }
+        const half8_t vh = __builtin_bit_cast(half8_t, lh);
+        const half8_t vl = __builtin_bit_cast(half8_t, ll);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], vh, oacc[i][c], 0, 0, 0);
+          oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo[i], vh, oacc[i][c], 0, 0, 0);
+          oacc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[i], vl, oacc[i][c], 0, 0, 0);
+        }
+      }
+    } else if constexpr (Q8) {
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) {
         const uint32_t bsel = 0x0C000C00u | (uint32_t)(c & 3) | ((4u + (c & 3)) << 16);
@@ -568,7 +657,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   // lane: even tiles directly in units of 2^-24, odd ones as (bytes - low) in
   // units of 2^-20.
   auto dof = [&](int c) -> int {
-    if constexpr (Q8) return NCOL * col + c;  // the V bytes the lane read
+    if constexpr (Q8 || Q2) return NCOL * col + c;  // the V elements the lane read
     return D == 128 ? 8 * col + c : 8 * (col & 7) + 4 * (col >> 3) + c;
   };
 #pragma unroll
@@ -588,8 +677,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       float o[NCOL];
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) {
-        const float oc = (!Q8 && (c & 1)) ? (oacc[i][c][v] - oacc[i][c - 1][v]) * 1048576.0f
-                                          : oacc[i][c][v] * 16777216.0f;  // 2^20 / 2^24
+        const float oc = Q2 ? oacc[i][c][v]  // levels as themselves
+                         : (!Q8 && (c & 1)) ? (oacc[i][c][v] - oacc[i][c - 1][v]) * 1048576.0f
+                                            : oacc[i][c][v] * 16777216.0f;  // 2^20 / 2^24
         o[c] = (oc - cv) * inv_l;
       }
       if constexpr (Q8) {  // the original domain already
@@ -634,11 +724,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }
 }
 
-template <bool BF16, int D, int G, bool Q8>
+template <bool BF16, int D, int G, bool Q8, bool Q2>
 hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
-  using PG = PGeo<D, G, Q8>;
+  using PG = PGeo<D, G, Q8, Q2>;
   static_assert(PG::TOTAL <= 160 * 1024, "LDS of a gfx950 CU");
-  auto kern = prefill_kernel<BF16, D, G, Q8>;
+  auto kern = prefill_kernel<BF16, D, G, Q8, Q2>;
   if (PG::TOTAL > 65536) {
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)PG::TOTAL);
     if (e != hipSuccess) return e;
@@ -659,29 +749,31 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, int D, bool Q8>
+template <bool BF16, int D, bool Q8, bool Q2>
 hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_prefill_t<BF16, D, 1, Q8>(a, stream);
-    case 2: return launch_prefill_t<BF16, D, 2, Q8>(a, stream);
-    case 4: return launch_prefill_t<BF16, D, 4, Q8>(a, stream);
-    case 8: return launch_prefill_t<BF16, D, 8, Q8>(a, stream);
-    default: return launch_prefill_t<BF16, D, 16, Q8>(a, stream);
+    case 1: return launch_prefill_t<BF16, D, 1, Q8, Q2>(a, stream);
+    case 2: return launch_prefill_t<BF16, D, 2, Q8, Q2>(a, stream);
+    case 4: return launch_prefill_t<BF16, D, 4, Q8, Q2>(a, stream);
+    case 8: return launch_prefill_t<BF16, D, 8, Q8, Q2>(a, stream);
+    default: return launch_prefill_t<BF16, D, 16, Q8, Q2>(a, stream);
   }
 }
 
-template <bool Q8>
+template <bool Q8, bool Q2>
 hipError_t launch_prefill_q(const AttnArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.head_size == 128 ? launch_prefill_d<true, 128, Q8>(a, stream)
-                                        : launch_prefill_d<true, 64, Q8>(a, stream);
-  return a.head_size == 128 ? launch_prefill_d<false, 128, Q8>(a, stream)
-                            : launch_prefill_d<false, 64, Q8>(a, stream);
+  if (a.bf16) return a.head_size == 128 ? launch_prefill_d<true, 128, Q8, Q2>(a, stream)
+                                        : launch_prefill_d<true, 64, Q8, Q2>(a, stream);
+  return a.head_size == 128 ? launch_prefill_d<false, 128, Q8, Q2>(a, stream)
+                            : launch_prefill_d<false, 64, Q8, Q2>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
-  return a.q8 ? launch_prefill_q<true>(a, stream) : launch_prefill_q<false>(a, stream);
+  if (a.q8) return launch_prefill_q<true, false>(a, stream);
+  if (a.q2) return launch_prefill_q<false, true>(a, stream);
+  return launch_prefill_q<false, false>(a, stream);
 }
 
 }  // namespace int4kv

@@ -264,7 +264,7 @@ def _a2(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(mq=7), 2), (dict(hkv=3, hq=6), 2), (dict(hkv=12, hq=24), 2), (dict(d=96), 2),
+    (dict(mq=7, hq=24), 2), (dict(hkv=3, hq=6), 2), (dict(hkv=12, hq=24), 2), (dict(d=96), 2),
     (dict(bs=8), 2), (dict(hq=30), 1), (dict(ns=16), 3), (dict(cache=None), 1),
     (dict(signs=None), 1), (dict(cap=float("nan")), 1), (dict(bts=10), 1),
 ])

@@ -1,6 +1,6 @@
 """GPU parity of the INT2 Lloyd-Max mode: the cache write (codes and scale
 words bit for bit against the oracle over the whole cache buffer, sentinel
-bytes included) and decode attention over that cache (|gpu - ref| <= 2e-3 +
+bytes included) and decode and prefill attention over that cache (|gpu - ref| <= 2e-3 +
 1e-2 |ref| against the oracle's fp64 attention over its own cache)."""
 import random
 
@@ -207,9 +207,94 @@ def test_int2_decode_llama3_full_size_sampled(oracle_mod):
         assert_attention_close(out[seqs], _ref2(oracle_mod, ws, ref_cache), f"seq {seqs}")
 
 
-def test_int2_prefill_is_unsupported():
-    w = wl.custom([(4, 40)], 8, 2, 128, seed=1, write_all=True)
+# ---- prefill / mixed batches over the INT2 cache
+
+MIX = [(5, 48), (16, 16), (1, 100), (33, 33), (64, 200), (7, 301), (2, 2), (1, 1)]
+
+
+def _prefill2(oracle_mod, w, window=0, softcap=0.0, data_scale=1.0):
     t = to_dev(w)
-    c = torch.zeros(ik.cache_shape_int2(w.num_blocks, 2, 128), dtype=torch.uint8, device="cuda")
-    with pytest.raises(ik.Int4KVError):
-        _attn2(w, t, c)
+    c, ref_cache = _int2_cache(oracle_mod, w, t)
+    out = _attn2(w, t, c, 1, window, softcap)
+    torch.cuda.synchronize()
+    assert_attention_close(out, _ref2(oracle_mod, w, ref_cache, window, softcap), w.name,
+                           data_scale=data_scale)
+    return out
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_int2_prefill_mixed_lengths(oracle_mod, G, d):
+    header(f"int2 prefill mixed G={G} d={d}")
+    hkv = 2 if G <= 8 else 1
+    w = wl.custom(MIX, G * hkv, hkv, d, seed=500 + G + d, write_all=True, extra_blocks=2)
+    _prefill2(oracle_mod, w)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(6, 3, 128, torch.float16), (32, 8, 64, torch.bfloat16)])
+def test_int2_prefill_window_softcap(oracle_mod, hq, hkv, d, dtype):
+    """Windows shorter and longer than the query tile, soft caps, and a KV
+    head count (3) that the decode kernel does not take."""
+    w = wl.custom([(40, 120), (9, 300), (130, 130)], hq, hkv, d, dtype=dtype, seed=hq + d + 1,
+                  write_all=True, scale=2.0)
+    for window, cap in ((0, 0.0), (17, 0.0), (100, 0.0), (0, 5.0), (50, 30.0)):
+        header(f"int2 prefill {hq}/{hkv} d{d} window={window} cap={cap}")
+        _prefill2(oracle_mod, w, window, cap)
+
+
+@pytest.mark.parametrize("scale", [1e-3, 30.0])
+def test_int2_prefill_scaled_inputs(oracle_mod, scale):
+    header(f"int2 prefill scale {scale}")
+    w = wl.custom([(40, 120), (9, 300)], 8, 2, 128, dtype=torch.float16, seed=19, write_all=True,
+                  scale=scale)
+    _prefill2(oracle_mod, w, data_scale=max(1.0, scale))
+
+
+def test_int2_prefill_last_row_matches_decode(oracle_mod):
+    """Empty sequences inside a prefill batch; the last query row of a prefill
+    equals the decode of the same token (two different kernels)."""
+    header("int2 prefill empty sequences / last row vs decode")
+    w = wl.custom([(30, 60), (0, 20), (3, 3), (40, 390)], 32, 8, 128, seed=23, write_all=True)
+    t = to_dev(w)
+    c, ref_cache = _int2_cache(oracle_mod, w, t)
+    pre = _attn2(w, t, c)
+    ref = _ref2(oracle_mod, w, ref_cache)
+    torch.cuda.synchronize()
+    assert_attention_close(pre, ref, "prefill")
+    last = sub_workload(w, [3])
+    dq = wl.Workload("last row", w.dtype, 32, 8, 128, w.num_blocks, [390], [1], [1],
+                     last.block_table, last.key, last.value, last.query[-1:], w.signs)
+    dec = _attn2(dq, to_dev(dq), c, 4)
+    torch.cuda.synchronize()
+    assert_attention_close(dec, ref[-1:], "decode of the last row")
+
+
+def test_int2_chunked_prefill_full_size_sampled(oracle_mod):
+    """The 32-sequence chunked-prefill mix (32 q / 8 KV heads, d 128) in one
+    launch; 10 sampled (sequence, query row) pairs against the oracle."""
+    w = wl.chunked_prefill(device="cuda")
+    header(f"int2 chunked prefill full size: {sum(w.query_lens)} query tokens")
+    t = to_dev(w)
+    c = torch.empty(ik.cache_shape_int2(w.num_blocks, 8, 128), dtype=torch.uint8, device="cuda")
+    _, slots = w.token_set("all")
+    ik.int2_kv_write(w.key, w.value, slots.cuda(), c, t["signs"])
+    out = _attn2(w, t, c)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(9)
+    off = w.token_offsets()
+    cuq = w.cu_seqlens_q().tolist()
+    for b in torch.randperm(w.num_seqs, generator=g)[:10].tolist():
+        ql, L = w.query_lens[b], w.kv_lens[b]
+        i = int(torch.randint(0, ql, (1,), generator=g))
+        pos = L - ql + i
+        kidx = torch.arange(off[b], off[b] + pos + 1).to(w.key.device)
+        sub = wl.Workload("row", w.dtype, 32, 8, 128, w.num_blocks, [pos + 1], [1], [1],
+                          w.block_table[[b]].clone(), w.key[kidx], w.value[kidx],
+                          w.query[cuq[b] + i:cuq[b] + i + 1], w.signs)
+        ref_cache = np.zeros(oracle_mod.cache_shape_int2(w.num_blocks, 16, 8, 128), np.uint8)
+        i2, s2 = sub.token_set("all")
+        oracle_mod.kv_write_int2(wl.bits16(sub.key[i2.to(sub.key.device)]),
+                                 wl.bits16(sub.value[i2.to(sub.key.device)]), "bf16", s2.numpy(),
+                                 ref_cache, w.signs.numpy())
+        assert_attention_close(out[cuq[b] + i:cuq[b] + i + 1], _ref2(oracle_mod, sub, ref_cache),
+                               f"seq {b} row {i}")
