@@ -711,9 +711,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
           const half8_t lb = __builtin_bit_cast(half8_t, xl);
           oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, cb, oacc[2 * e], 0, 0, 0);
           oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, cb, oacc[2 * e], 0, 0, 0);
+          // the low-bit sum enters O with weight 2v - u = 0.076 against u =
+          // 0.98: W's f16 hi part alone (2^-12 relative) keeps it far below
+          // the fp32 rounding of the rest
           oacc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, lb, oacc[2 * e + 1], 0, 0, 0);
-          oacc[2 * e + 1] =
-              __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, lb, oacc[2 * e + 1], 0, 0, 0);
         }
     } else if constexpr (Q8) {
       // phase 3 (INT8): column tile c takes byte c % 4 of the lane's dword

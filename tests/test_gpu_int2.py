@@ -172,6 +172,21 @@ def test_int2_decode_heads_window_softcap_large_values(oracle_mod, hq, hkv, d):
                                f"large values NS={ns}", data_scale=30.0)
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_int2_decode_tiny_values(oracle_mod, dtype):
+    """K/V scaled by 1e-3 over up to 3000 keys: the softmax weights times the
+    V scales reach f16's subnormal range, where the low-bit sum (taken with
+    the weights' f16 hi part only) loses relative precision."""
+    w = wl.custom([(1, 3000), (1, 700), (1, 65), (1, 1)], 32, 8, 128, dtype=dtype, seed=31,
+                  write_all=True, scale=1e-3)
+    t = to_dev(w)
+    c, ref_cache = _int2_cache(oracle_mod, w, t)
+    ref = _ref2(oracle_mod, w, ref_cache)
+    for ns in (1, 8):
+        header(f"int2 decode tiny values {dtype} NS={ns}")
+        assert_attention_close(_attn2(w, t, c, ns), ref, f"tiny values NS={ns}")
+
+
 def test_int2_decode_empty_and_zero_length(oracle_mod):
     w = wl.custom([(1, 40), (0, 20), (1, 0), (1, 9)], 8, 2, 128, seed=4, write_all=True)
     t = to_dev(w)
