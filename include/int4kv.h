@@ -9,9 +9,13 @@
  * allocates no device memory and keeps no global mutable state apart from a
  * thread-local error string and a lock-protected record of the (kernel,
  * device) pairs whose LDS limit it has raised, so it is re-entrant; buffers
- * are owned by the caller.  Device-resident metadata (slot numbers, block ids, lengths) is the
- * caller's contract and is not checked: out-of-range values there are
- * undefined behaviour.
+ * are owned by the caller.  Slot numbers are bounds-checked on the device:
+ * every write entry point stores a token only when its slot lies in
+ * [0, num_blocks * block_size) and skips it otherwise (negative slots are the
+ * pages' skip marker; larger ones would address memory past the cache).  The
+ * other device-resident metadata (block ids, lengths) is the caller's
+ * contract and is not checked: out-of-range values there are undefined
+ * behaviour.
  *
  * Citations name the page and the section that defines each operation:
  *   [report]   PR #40835 report: "[Feature] Triton INT4 per-token-head KV cache
@@ -76,7 +80,8 @@ int64_t int4kv_cache_bytes(int32_t num_blocks, int32_t block_size, int32_t num_k
  *   key, value        [num_tokens, num_kv_heads, head_size] of `dtype`; the
  *                     token stride (in elements) is given; heads are
  *                     contiguous.  Base 16-byte aligned, stride a multiple of 8.
- *   slot_mapping      int64 [num_tokens]; slot < 0 leaves the cache untouched.
+ *   slot_mapping      int64 [num_tokens]; slot < 0 (and slot >=
+ *                     num_blocks * block_size) leaves the cache untouched.
  *   kv_cache          the packed cache (layout above), written in place.
  *   rht_signs         fp32 [head_size], each exactly +1.0f or -1.0f.
  * Supported: head_size 64 or 128, block_size 16.  num_tokens == 0 is a no-op.

@@ -210,7 +210,8 @@ int4kv_status_t int4_kv_write(const void* key, int64_t key_token_stride, const v
   if (s != INT4KV_OK) return s;
   hipError_t e = int4kv::launch_write(key, key_token_stride, value, value_token_stride,
                                       dtype == INT4KV_BF16, slot_mapping, num_tokens, kv_cache,
-                                      num_kv_heads, head_size, rht_signs,
+                                      (int64_t)num_blocks * block_size, num_kv_heads, head_size,
+                                      rht_signs,
                                       reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "write launch: %s", hipGetErrorString(e));
   return ok();
@@ -245,7 +246,8 @@ int4kv_status_t int8_kv_write(const void* key, int64_t key_token_stride, const v
   if (s != INT4KV_OK) return s;
   hipError_t e = int4kv::launch_write_int8(key, key_token_stride, value, value_token_stride,
                                            dtype == INT4KV_BF16, slot_mapping, num_tokens,
-                                           kv_cache, num_kv_heads, head_size,
+                                           kv_cache, (int64_t)num_blocks * block_size,
+                                           num_kv_heads, head_size,
                                            reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "write launch: %s", hipGetErrorString(e));
   return ok();
@@ -275,7 +277,8 @@ int4kv_status_t int2_kv_write(const void* key, int64_t key_token_stride, const v
   if (s != INT4KV_OK) return s;
   hipError_t e = int4kv::launch_write_int2(key, key_token_stride, value, value_token_stride,
                                            dtype == INT4KV_BF16, slot_mapping, num_tokens,
-                                           kv_cache, num_kv_heads, head_size, rht_signs,
+                                           kv_cache, (int64_t)num_blocks * block_size,
+                                           num_kv_heads, head_size, rht_signs,
                                            reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "write launch: %s", hipGetErrorString(e));
   return ok();
@@ -425,10 +428,11 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
   if (s != INT4KV_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool bf16 = dtype == INT4KV_BF16;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
   if (max_seqlen_q == 0) {  // nothing to attend: the write alone
     hipError_t e = int4kv::launch_write(key_new, key_token_stride, value_new, value_token_stride,
-                                        bf16, slot_mapping, num_seqs, kv_cache, num_kv_heads,
-                                        head_size, rht_signs, st);
+                                        bf16, slot_mapping, num_seqs, kv_cache, num_slots,
+                                        num_kv_heads, head_size, rht_signs, st);
     if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "write launch: %s", hipGetErrorString(e));
     return ok();
   }
@@ -445,11 +449,12 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
     a.value_new = value_new;
     a.value_new_stride = value_token_stride;
     a.slot_new = slot_mapping;
+    a.num_slots = num_slots;
     e = int4kv::launch_decode_lds(a, st);
   } else {  // the same result as two calls: the write, then the attention
     e = int4kv::launch_write(key_new, key_token_stride, value_new, value_token_stride, bf16,
-                             slot_mapping, num_seqs, kv_cache, num_kv_heads, head_size,
-                             rht_signs, st);
+                             slot_mapping, num_seqs, kv_cache, num_slots, num_kv_heads,
+                             head_size, rht_signs, st);
     if (e == hipSuccess)
       e = max_seqlen_q == 1 ? int4kv::launch_decode(a, st) : int4kv::launch_prefill(a, st);
   }

@@ -367,10 +367,14 @@ __global__ __launch_bounds__(512) void decode_kernel(
             const uint32_t y = (nib < 4) ? ylo[i] : yhi[i];
             vb[i] = nib_pair_f16(y >> (4 * (nib & 3)));
           }
-          oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, __builtin_bit_cast(half8_t, vb),
-                                                           oacc[c], 0, 0, 0);
-          oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, __builtin_bit_cast(half8_t, vb),
-                                                           oacc[c], 0, 0, 0);
+          // the tile's products from zero, tiles summed in fp32 on the vector
+          // ALU: the matrix cores keep only about 15 bits of an incoming
+          // accumulator below the instruction's largest product
+          float4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              wop, __builtin_bit_cast(half8_t, vb), float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, __builtin_bit_cast(half8_t, vb), t,
+                                                     0, 0, 0);
+          oacc[c] += t;
         }
       }
   };

@@ -28,9 +28,13 @@
 //    keys' dwords, zero-extended into f16 halves, is the subnormal pair
 //    (low + 16 high) * 2^-24, and masked to 0x000F000F the low nibbles alone;
 //    per byte one column tile takes the whole bytes and one the low nibbles,
-//    the high nibble's column is their difference / 16.  Products and sums
-//    stay exact in fp32; the 2^24 (2^20) is applied per output column at the
-//    end.
+//    the high nibble's column is their difference / 16.  Single products
+//    are exact; the matrix cores sum a dot product's products in a window
+//    anchored at the largest operand exponents (a subnormal operand's leading
+//    zeros spend part of it) and keep only the top bits of an incoming
+//    accumulator that the products outweigh, so each tile's products are
+//    summed from zero and the tiles are accumulated in fp32 on the vector
+//    ALU.  The 2^24 (2^20) is applied per output column at the end.
 //  * The next tile's scores are computed on the matrix cores while the
 //    current tile's softmax runs; the softmax reference maximum moves only
 //    when a logit exceeds it by 4 (base-2 units, a factor 16 in probability),
@@ -97,11 +101,13 @@ __device__ __forceinline__ float max16(float x) {
 // Compile-time geometry of the LDS image of one tile (two cache blocks).
 // INT2 mode: the 4-level Lloyd-Max quantizer of N(0, 1) (Max, 1960, N = 4)
 // has levels -b, -a, a, b for codes 0..3.  With the code's bits (hi, lo),
-// level + b = (a + b) hi + (b - a) lo = u code + (2v - u) lo, u = (a + b)/2,
-// 2v = b - a: linear in bits, which is what the matrix cores take.
+// level + b = (a + b) hi + (b - a) lo (the scores: unsigned bit planes on
+// the exact int8 matrix cores, b leaving through the query-sum term), and
+// level = u sigma + v tau with the signed planes sigma = 2 hi - 1,
+// tau = 2 lo - 1, u = (a + b)/2, v = (b - a)/2 (P.V: centred operands).
 constexpr float kLmA = 0.4527800346f, kLmB = 1.5104176085f;
 constexpr float kLm2u = kLmA + kLmB, kLm2v = kLmB - kLmA;
-constexpr float kLmU = 0.5f * kLm2u, kLmW = kLm2v - kLmU;
+constexpr float kLmU = 0.5f * kLm2u, kLmV = 0.5f * kLm2v;
 
 template <int D, int HPW, bool Q8 = false, bool Q2 = false>
 struct Geo {
@@ -165,7 +171,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     float* __restrict__ segm_max, float* __restrict__ segm_sum,
     const uint16_t* __restrict__ key_new, int64_t key_new_stride,
     const uint16_t* __restrict__ value_new, int64_t value_new_stride,
-    const int64_t* __restrict__ slot_new, int32_t window, float cap2, float inv_cap2) {
+    const int64_t* __restrict__ slot_new, int64_t num_slots, int32_t window, float cap2,
+    float inv_cap2) {
   using GG = Geo<D, HPW, Q8, Q2>;
   using WG = WGeo<G>;
   using LY = Lay<D, G, HPW, Q8, Q2>;
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int DWG = DW / 4;    // code dwords per lane group in the score operand
   constexpr int NCK = Q2 ? D / 32 : D / 64;  // int8 MFMA k-chunks (INT2: two bit planes)
   constexpr int NCOL = D / 16;   // P.V column tiles (INT2: elements per lane)
-  constexpr int NACC = Q2 ? 2 * NCOL : NCOL;  // P.V accumulators
+  constexpr int NACC = NCOL;  // P.V accumulators
   constexpr int RPG = G <= 4 ? 1 : G / 4;
   constexpr int EPL = G * D / 64;
   constexpr int LPQ = 64 / G;
@@ -213,7 +220,9 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   bool store_pending = false;  // this wave stored rows whose completion is still to be awaited
   if (!Q8 && !Q2 && slot_new != nullptr) {  // (the INT8 and INT2 modes have no fused step)
     const int64_t slot = slot_new[b];
-    if (slot >= 0 && L > 0 && ((L - 1) / kBlockSize - blo) / per == seg) {  // uniform over the workgroup
+    // (slots outside [0, num_slots) are not stored, as in the cache write)
+    if ((uint64_t)slot < (uint64_t)num_slots && L > 0 &&
+        ((L - 1) / kBlockSize - blo) / per == seg) {  // uniform over the workgroup
       constexpr int WE = 16, WLPR = D / WE, WRPW = kWave / WLPR;  // rows of 8 or 4 lanes
       if (wave * WRPW < 2 * HPW) {
         const int r = wave * WRPW + lane / WLPR;  // row kv * HPW + head of the group
@@ -352,16 +361,19 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
     for (int m = 1; m < LPQ; m <<= 1) mx = fmaxf(mx, shfl_xor_rt(mx, m));
     const int ex = mx > 0.f ? ilogbf(mx) + 1 : 0;  // |q'| * 2^-ex < 1
-    // |v| < 2^22: the centred planes p0, p1 in [-128, 127] then leave the top
-    // plane p2 within [-65, 65], so no value is ever clamped
-    // (INT2: below 2^21, so the bit-plane weights, < 2, keep it below 2^22)
-    constexpr int QB = Q2 ? 21 : 22;
+    // |v| <= 2^22: the centred planes p0, p1 in [-128, 127] then leave the top
+    // plane p2 within [-65, 65], so no value is ever clamped.  INT2 stages the
+    // unrounded x * 2^(22 - ex) instead: each bit plane's weight (< 1.97) is
+    // applied before the one rounding, so weighted values stay below
+    // 1.97 * 2^22 < 127 * 65536 + 127 * 257 and p2 within [-127, 127]
+    constexpr int QB = 22;
     const float nrm = ldexpf(1.0f, QB - ex);
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      const float v = rintf(x[e] * nrm);
-      q24[i * D + s * EPL + e] = (int)v;
+      const float xs = x[e] * nrm;  // exact: a power-of-two scaling
+      const float v = rintf(xs);
+      q24[i * D + s * EPL + e] = Q2 ? __builtin_bit_cast(int, xs) : (int)v;
       sum += v;  // < 2^29 in magnitude; its rounding is far below the score's
     }
 #pragma unroll
@@ -411,7 +423,9 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
             // (rho, beta) is element 4 beta + rho of that dword
             const int j = (k / 2 + g) % DWG;
             const int d = 16 * (g * DWG + j) + 4 * beta + rho;
-            v = ok ? (int)rintf((float)q24[qh * D + d] * ((k & 1) ? kLm2v : kLm2u)) : 0;
+            v = ok ? (int)rintf(__builtin_bit_cast(float, q24[qh * D + d]) *
+                                ((k & 1) ? kLm2v : kLm2u))
+                   : 0;
           } else {
             const int j = Q8 ? (4 * k + rho + g) % DWG : (2 * k + (rho >> 1) + g) % DWG;
             const int d = Q8 ? 4 * (g * DWG + j) + beta : 8 * (g * DWG + j) + 2 * beta + (rho & 1);
@@ -457,10 +471,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // tile holds whole codes offset by 128
   auto o_of = [&](int c, int v) -> float {
     if constexpr (Q8) return oacc[c][v] * 16777216.0f;  // 2^24
-    if constexpr (Q2) {  // element c: u * sum W code + (2v - u) * sum W low bit, scaled by 4^k
-      const float sc = 16777216.0f / (float)(1 << (2 * (c & 3)));
-      return fmaf(kLmU, oacc[2 * c][v], kLmW * oacc[2 * c + 1][v]) * sc;
-    }
+    if constexpr (Q2) return oacc[c][v];  // element c: sum W level
     return (c & 1) ? (oacc[c][v] - oacc[c - 1][v]) * 1048576.0f  // 2^20
                    : oacc[c][v] * 16777216.0f;                   // 2^24
   };
@@ -616,12 +627,13 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       kval[n] = (tb + n < b1) && key < L && key >= lo;
       // INT4: zero point in the scale word's low 4 bits; INT8: a plain fp32
       // scale, no K zero point, and V codes offset by 128 (see the V operands)
-      // INT2: plain fp32 scales; the planes give sum q (level + b), so b
-      // leaves through the zero-point terms (K and V alike)
+      // INT2: plain fp32 scales; the score planes give sum q (level + b), so
+      // b leaves through the query-sum term; the V operands are centred (no
+      // V zero point)
       const float sK = as_float((Q8 || Q2) ? cw.kw[n] : cw.kw[n] & 0xFFFFFFF0u);
       const float zK = Q8 ? 0.f : Q2 ? kLmB : (float)(cw.kw[n] & 0xFu);
       sV[n] = kval[n] ? as_float((Q8 || Q2) ? cw.vw[n] : cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked: 0
-      zV[n] = Q8 ? 128.f : Q2 ? kLmB : (float)(cw.vw[n] & 0xFu);
+      zV[n] = Q8 ? 128.f : Q2 ? 0.f : (float)(cw.vw[n] & 0xFu);
       const uint32_t keep = kval[n] ? 0xFFFFFFFFu : 0u;
       const uint32_t ninf = kval[n] ? 0u : 0xFF800000u;
 #pragma unroll
@@ -655,7 +667,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
         m_run[v] = up ? tmax : m_run[v];
         thr[v] = m_run[v] + kLazy;
         l_run[v] *= alpha;
-        corr[v] *= alpha;
+        if constexpr (!Q2) corr[v] *= alpha;  // INT2 has no V zero-point term
 #pragma unroll
         for (int c = 0; c < NACC; ++c) oacc[c][v] *= alpha;
       }
@@ -674,7 +686,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       wl[0] = (_Float16)(w0 - (float)wh[0]);
       wl[1] = (_Float16)(w1 - (float)wh[1]);
       l_run[v] += p0 + p1;
-      corr[v] = fmaf(w1, zV[1], fmaf(w0, zV[0], corr[v]));
+      if constexpr (!Q2) corr[v] = fmaf(w1, zV[1], fmaf(w0, zV[0], corr[v]));
       *reinterpret_cast<half2_t*>(wt + wr_off[v]) = wh;
       *reinterpret_cast<half2_t*>(wt + WG::WLO + wr_off[v]) = wl;
     }
@@ -684,11 +696,31 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
     const half8_t wop_lo = *reinterpret_cast<const half8_t*>(wt + rd_lo);
     phase_end(1, kb, nxt);
+    // acc += W B for one column tile.  The tile's products are summed on the
+    // matrix cores from zero (hi, then lo on top) and tiles are accumulated
+    // in fp32 on the vector ALU: the matrix cores align an incoming
+    // accumulator to the largest product of the instruction and keep only
+    // about 15 bits of it below that product, so a running sum that a later,
+    // heavier key outweighs would lose its low bits there.
+    auto pv_tile = [&](const half8_t& bop) {
+      const float4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          wop, bop, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, bop, t, 0, 0, 0);
+    };
+    auto pv = [&](float4_t& acc, const half8_t& bop) { acc += pv_tile(bop); };
 
     if constexpr (Q2) {
       // phase 3 (INT2): byte bl of the lane's dword of two slot keys, zero-
-      // extended into f16 halves; element 4 bl + k takes the code (mask
-      // 3 << 2k) and its low bit (mask 1 << 2k), subnormals scaled by 4^k
+      // extended into f16 halves; element 4 bl + k enters as the signed
+      // planes sigma = 2 hi - 1 and tau = 2 lo - 1, each +-1.0 (the bit
+      // shifted into the sign position, inverted and merged with the
+      // magnitude in one bitop3).  Centred, normal operands: the matrix cores
+      // sum a dot product's products in a window anchored at the largest
+      // operand exponents and cut off below it, and a subnormal operand's
+      // leading zeros spend that window, so 2-bit codes as subnormals would
+      // lose the smaller weights' products; and unsigned codes with the
+      // offset b taken out in fp32 afterwards would turn such losses into an
+      // offset common to every rotated element (output element 0).
       uint32_t vx2[NCOL / 4][4];
 #pragma unroll
       for (int bl = 0; bl < NCOL / 4; ++bl)
@@ -701,20 +733,21 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int e = 4 * bl + k;
-          u32x4_t xc, xl;
+          constexpr uint32_t mag = 0x3C003C00u;  // 1.0 in both halves
+          u32x4_t xs, xt;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            xc[i] = vx2[bl][i] & (0x00030003u << (2 * k));
-            xl[i] = vx2[bl][i] & (0x00010001u << (2 * k));
+            // (~shifted & sign bits) | magnitude: sign set where the bit is 0
+            xs[i] = __builtin_amdgcn_bitop3_b32(vx2[bl][i] << (14 - 2 * k), 0x80008000u, mag, 0xAE);
+            xt[i] = __builtin_amdgcn_bitop3_b32(vx2[bl][i] << (15 - 2 * k), 0x80008000u, mag, 0xAE);
           }
-          const half8_t cb = __builtin_bit_cast(half8_t, xc);
-          const half8_t lb = __builtin_bit_cast(half8_t, xl);
-          oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, cb, oacc[2 * e], 0, 0, 0);
-          oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, cb, oacc[2 * e], 0, 0, 0);
-          // the low-bit sum enters O with weight 2v - u = 0.076 against u =
-          // 0.98: W's f16 hi part alone (2^-12 relative) keeps it far below
-          // the fp32 rounding of the rest
-          oacc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, lb, oacc[2 * e + 1], 0, 0, 0);
+          const half8_t sb = __builtin_bit_cast(half8_t, xs);
+          const half8_t tb = __builtin_bit_cast(half8_t, xt);
+          // one accumulator per element: O_e += u (W sigma) + v (W tau), the
+          // planes combined in fp32 per tile
+          const float4_t ts = pv_tile(sb), tt = pv_tile(tb);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[e][r] = fmaf(kLmV, tt[r], fmaf(kLmU, ts[r], oacc[e][r]));
         }
     } else if constexpr (Q8) {
       // phase 3 (INT8): column tile c takes byte c % 4 of the lane's dword
@@ -733,14 +766,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       phase_end(2, kb, nxt);
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) {
-        const half8_t xb = __builtin_bit_cast(half8_t, vx8[c]);
-        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, xb, oacc[c], 0, 0, 0);
-        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, xb, oacc[c], 0, 0, 0);
+        pv(oacc[c], __builtin_bit_cast(half8_t, vx8[c]));
       }
     } else {
     // phase 3: V operands.  Byte beta of the lane's dword of two slot keys,
     // each zero-extended into an f16 half: the subnormal (low + 16 * high) *
-    // 2^-24, exact in the products.
+    // 2^-24; single products are exact.
     uint32_t vx[NCOL / 2][4];
 #pragma unroll
     for (int bb = 0; bb < NCOL / 2; ++bb)
@@ -756,14 +787,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       u32x4_t vl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) vl[i] = vx[bb][i] & 0x000F000Fu;
-      const half8_t xb = __builtin_bit_cast(half8_t, vx[bb]);
-      const half8_t lb = __builtin_bit_cast(half8_t, vl);
-      float4_t& ol = oacc[2 * bb];
-      float4_t& ox = oacc[2 * bb + 1];
-      ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, xb, ox, 0, 0, 0);
-      ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, xb, ox, 0, 0, 0);
-      ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, lb, ol, 0, 0, 0);
-      ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, lb, ol, 0, 0, 0);
+      pv(oacc[2 * bb + 1], __builtin_bit_cast(half8_t, vx[bb]));
+      pv(oacc[2 * bb], __builtin_bit_cast(half8_t, vl));
     }
     }
     // the remaining score groups of tile t+1 share this region: one MFMA per
@@ -771,7 +796,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
     for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
 #pragma unroll
-    for (int j = 0; j < 2 * NACC + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
+    for (int j = 0; j < (Q2 ? 4 : 2) * NACC + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
@@ -810,10 +835,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     l_run[v] += shfl_xor<2>(l_run[v]);
     l_run[v] += shfl_xor<4>(l_run[v]);
     l_run[v] += shfl_xor<8>(l_run[v]);
-    corr[v] += shfl_xor<1>(corr[v]);
-    corr[v] += shfl_xor<2>(corr[v]);
-    corr[v] += shfl_xor<4>(corr[v]);
-    corr[v] += shfl_xor<8>(corr[v]);
+    if constexpr (!Q2) {
+      corr[v] += shfl_xor<1>(corr[v]);
+      corr[v] += shfl_xor<2>(corr[v]);
+      corr[v] += shfl_xor<4>(corr[v]);
+      corr[v] += shfl_xor<8>(corr[v]);
+    }
   }
   // column tile c holds element dof(c) of this lane
   auto dof = [&](int c) -> int {
@@ -901,7 +928,7 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
                      scale_log2, a.signs, a.num_segments, a.segm_out, a.segm_max, a.segm_sum,
                      reinterpret_cast<const uint16_t*>(a.key_new), a.key_new_stride,
                      reinterpret_cast<const uint16_t*>(a.value_new), a.value_new_stride,
-                     a.slot_new, a.window, cap2, cap2 > 0.f ? 1.0f / cap2 : 0.f);
+                     a.slot_new, a.num_slots, a.window, cap2, cap2 > 0.f ? 1.0f / cap2 : 0.f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_segments == 1) return e;
   return launch_reduce(a, stream);

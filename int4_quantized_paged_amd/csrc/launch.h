@@ -1,4 +1,7 @@
 // Host-side launchers of the INT4 KV-cache kernels (internal to the library).
+// The write kernels store a token only when its slot lies in [0, num_slots),
+// num_slots = num_blocks * block_size: negative slots are the pages' "skip"
+// marker, and larger ones would address memory past the cache.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,21 +11,23 @@ namespace int4kv {
 
 hipError_t launch_write(const void* key, int64_t key_stride, const void* value,
                         int64_t value_stride, bool bf16, const int64_t* slot_mapping,
-                        int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
-                        int32_t head_size, const float* signs, hipStream_t stream);
+                        int32_t num_tokens, uint8_t* cache, int64_t num_slots,
+                        int32_t num_kv_heads, int32_t head_size, const float* signs,
+                        hipStream_t stream);
 
 // INT8 per-token-head mode: rows of head_size int8 codes and an fp32 scale
 hipError_t launch_write_int8(const void* key, int64_t key_stride, const void* value,
                              int64_t value_stride, bool bf16, const int64_t* slot_mapping,
-                             int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
-                             int32_t head_size, hipStream_t stream);
+                             int32_t num_tokens, uint8_t* cache, int64_t num_slots,
+                             int32_t num_kv_heads, int32_t head_size, hipStream_t stream);
 
 // INT2 Lloyd-Max mode: rows of head_size / 4 code bytes and an fp32 scale,
 // over the INT4 mode's rotation
 hipError_t launch_write_int2(const void* key, int64_t key_stride, const void* value,
                              int64_t value_stride, bool bf16, const int64_t* slot_mapping,
-                             int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
-                             int32_t head_size, const float* signs, hipStream_t stream);
+                             int32_t num_tokens, uint8_t* cache, int64_t num_slots,
+                             int32_t num_kv_heads, int32_t head_size, const float* signs,
+                             hipStream_t stream);
 
 struct AttnArgs {
   const void* q;
@@ -62,6 +67,9 @@ struct AttnArgs {
   const void* value_new = nullptr;
   int64_t value_new_stride = 0;
   const int64_t* slot_new = nullptr;
+  // slots of the cache (num_blocks * block_size): a new token whose slot is
+  // outside [0, num_slots) is not stored
+  int64_t num_slots = 0;
 };
 
 // Raises a kernel's dynamic LDS limit above the 64 KiB default, once per

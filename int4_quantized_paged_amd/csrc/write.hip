@@ -33,7 +33,8 @@ template <bool BF16, int D, int E>
 __global__ __launch_bounds__(256) void write_kernel(
     const uint16_t* __restrict__ key, int64_t key_stride, const uint16_t* __restrict__ value,
     int64_t value_stride, const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
-    uint8_t* __restrict__ cache, int32_t num_kv_heads, const float* __restrict__ signs) {
+    uint8_t* __restrict__ cache, int64_t num_slots, int32_t num_kv_heads,
+    const float* __restrict__ signs) {
   constexpr int LPR = D / E;             // lanes per row
   constexpr int RPW = kWave / LPR;       // rows per wave
   constexpr int R = D / 2 + 4;           // packed row bytes
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void write_kernel(
     const uint32_t word = encode_piece<E, LPR>(x, sub, packed);
 
     const int64_t slot = slot_mapping[t];
-    if (in_range && slot >= 0) {
+    if (in_range && (uint64_t)slot < (uint64_t)num_slots) {  // skips slot < 0 too
       const int64_t blk = slot / kBlockSize, off = slot % kBlockSize;
       uint8_t* dst = cache + (((blk * 2 + kv) * kBlockSize + off) * num_kv_heads + h) * R;
       uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + (E / 2) * sub);  // rows are 4-byte aligned
@@ -109,7 +110,8 @@ __global__ __launch_bounds__(256) void write_kernel(
 
 hipError_t launch_write(const void* key, int64_t key_stride, const void* value,
                         int64_t value_stride, bool bf16, const int64_t* slot_mapping,
-                        int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
+                        int32_t num_tokens, uint8_t* cache, int64_t num_slots,
+                        int32_t num_kv_heads,
                         int32_t head_size, const float* signs, hipStream_t stream) {
   const int64_t rows = (int64_t)num_tokens * 2 * num_kv_heads;
   // 64 elements per lane once there are enough rows for every SIMD to hold
@@ -125,7 +127,7 @@ hipError_t launch_write(const void* key, int64_t key_stride, const void* value,
   auto v16 = reinterpret_cast<const uint16_t*>(value);
 #define INT4KV_W(BF, DD, EE)                                                                  \
   hipLaunchKernelGGL((write_kernel<BF, DD, EE>), grid, block, 0, stream, k16, key_stride, v16, \
-                     value_stride, slot_mapping, num_tokens, cache, num_kv_heads, signs)
+                     value_stride, slot_mapping, num_tokens, cache, num_slots, num_kv_heads, signs)
 #define INT4KV_WE(BF, DD) \
   do {                    \
     if (bulk)             \

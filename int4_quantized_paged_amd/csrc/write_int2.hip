@@ -32,7 +32,8 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(256) void write_int2_kernel(
     const uint16_t* __restrict__ key, int64_t key_stride, const uint16_t* __restrict__ value,
     int64_t value_stride, const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
-    uint8_t* __restrict__ cache, int32_t num_kv_heads, const float* __restrict__ signs) {
+    uint8_t* __restrict__ cache, int64_t num_slots, int32_t num_kv_heads,
+    const float* __restrict__ signs) {
 #pragma clang fp contract(off)
   constexpr int E = 16;
   constexpr int LPR = D / E;        // lanes per row
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void write_int2_kernel(
       word |= code << (2 * e);
     }
     const int64_t slot = slot_mapping[t];
-    if (ok && slot >= 0) {
+    if (ok && (uint64_t)slot < (uint64_t)num_slots) {  // skips slot < 0 too
       const int64_t blk = slot / kBlockSize, off = slot % kBlockSize;
       uint32_t* dst = reinterpret_cast<uint32_t*>(
           cache + (((blk * 2 + kv) * kBlockSize + off) * num_kv_heads + h) * R);  // 4-byte aligned
@@ -115,7 +116,8 @@ __global__ __launch_bounds__(256) void write_int2_kernel(
 
 hipError_t launch_write_int2(const void* key, int64_t key_stride, const void* value,
                              int64_t value_stride, bool bf16, const int64_t* slot_mapping,
-                             int32_t num_tokens, uint8_t* cache, int32_t num_kv_heads,
+                             int32_t num_tokens, uint8_t* cache, int64_t num_slots,
+                        int32_t num_kv_heads,
                              int32_t head_size, const float* signs, hipStream_t stream) {
   const int64_t rows = (int64_t)num_tokens * 2 * num_kv_heads;
   const int rows_per_block = 4 * (kWave / (head_size / 16));
@@ -127,7 +129,7 @@ hipError_t launch_write_int2(const void* key, int64_t key_stride, const void* va
   auto v16 = reinterpret_cast<const uint16_t*>(value);
 #define INT2KV_W(BF, DD)                                                                         \
   hipLaunchKernelGGL((write_int2_kernel<BF, DD>), grid, block, 0, stream, k16, key_stride, v16, \
-                     value_stride, slot_mapping, num_tokens, cache, num_kv_heads, signs)
+                     value_stride, slot_mapping, num_tokens, cache, num_slots, num_kv_heads, signs)
   if (bf16) {
     if (head_size == 128) INT2KV_W(true, 128); else INT2KV_W(true, 64);
   } else {

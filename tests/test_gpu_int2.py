@@ -145,8 +145,11 @@ def test_int2_decode_ragged_lengths(oracle_mod, G, d):
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 64), (8, 1, 128), (32, 16, 128),
                                       (128, 8, 128)])
 def test_int2_decode_heads_window_softcap_large_values(oracle_mod, hq, hkv, d):
-    """(128, 8, 128) is the instance with 8 heads of 16 query heads per
-    workgroup, which keeps part of its state in scratch."""
+    """(128, 8, 128) is the instance with 16 query heads per KV head, which
+    takes 4 KV heads per workgroup.  The scale-30 batch puts outputs of size
+    30 next to elements that cancel to near zero, so an offset common to the
+    rotated elements (it lands in output element 0) shows against the
+    unscaled absolute term."""
     w = wl.custom([(1, 300), (1, 77), (1, 513), (1, 2000)], hq, hkv, d, seed=hq + hkv + d,
                   write_all=True, scale=3.0)
     t = to_dev(w)
@@ -164,19 +167,16 @@ def test_int2_decode_heads_window_softcap_large_values(oracle_mod, hq, hkv, d):
     c30, ref30 = _int2_cache(oracle_mod, w30, t30)
     for ns in (1, 7):
         header(f"int2 decode large values {hq}/{hkv} d{d} NS={ns}")
-        # K/V at scale 30: the absolute term scales with them (measured on the
-        # 128-head batch: median error 2.4e-3, the size of one output
-        # element's fp32 rounding at this scale, and rows within 5e-4 of
-        # their largest element)
+        # K/V at scale 30 (outputs ~30, near-tied logits of order 40): the
+        # bound is the unscaled one
         assert_attention_close(_attn2(w30, t30, c30, ns), _ref2(oracle_mod, w30, ref30),
-                               f"large values NS={ns}", data_scale=30.0)
+                               f"large values NS={ns}")
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_int2_decode_tiny_values(oracle_mod, dtype):
-    """K/V scaled by 1e-3 over up to 3000 keys: the softmax weights times the
-    V scales reach f16's subnormal range, where the low-bit sum (taken with
-    the weights' f16 hi part only) loses relative precision."""
+    """K/V scaled by 1e-3 over up to 3000 keys: outputs of order 1e-4, so the
+    absolute term shrinks by the same factor (an all-zero output fails)."""
     w = wl.custom([(1, 3000), (1, 700), (1, 65), (1, 1)], 32, 8, 128, dtype=dtype, seed=31,
                   write_all=True, scale=1e-3)
     t = to_dev(w)
@@ -184,7 +184,7 @@ def test_int2_decode_tiny_values(oracle_mod, dtype):
     ref = _ref2(oracle_mod, w, ref_cache)
     for ns in (1, 8):
         header(f"int2 decode tiny values {dtype} NS={ns}")
-        assert_attention_close(_attn2(w, t, c, ns), ref, f"tiny values NS={ns}")
+        assert_attention_close(_attn2(w, t, c, ns), ref, f"tiny values NS={ns}", atol_scale=1e-3)
 
 
 def test_int2_decode_empty_and_zero_length(oracle_mod):
@@ -227,13 +227,13 @@ def test_int2_decode_llama3_full_size_sampled(oracle_mod):
 MIX = [(5, 48), (16, 16), (1, 100), (33, 33), (64, 200), (7, 301), (2, 2), (1, 1)]
 
 
-def _prefill2(oracle_mod, w, window=0, softcap=0.0, data_scale=1.0):
+def _prefill2(oracle_mod, w, window=0, softcap=0.0, atol_scale=1.0):
     t = to_dev(w)
     c, ref_cache = _int2_cache(oracle_mod, w, t)
     out = _attn2(w, t, c, 1, window, softcap)
     torch.cuda.synchronize()
     assert_attention_close(out, _ref2(oracle_mod, w, ref_cache, window, softcap), w.name,
-                           data_scale=data_scale)
+                           atol_scale)
     return out
 
 
@@ -262,7 +262,7 @@ def test_int2_prefill_scaled_inputs(oracle_mod, scale):
     header(f"int2 prefill scale {scale}")
     w = wl.custom([(40, 120), (9, 300)], 8, 2, 128, dtype=torch.float16, seed=19, write_all=True,
                   scale=scale)
-    _prefill2(oracle_mod, w, data_scale=max(1.0, scale))
+    _prefill2(oracle_mod, w, atol_scale=min(1.0, scale))
 
 
 def test_int2_prefill_last_row_matches_decode(oracle_mod):

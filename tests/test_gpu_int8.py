@@ -208,12 +208,13 @@ def test_int8_decode_llama3_full_size_sampled(oracle_mod):
 MIX = [(5, 48), (16, 16), (1, 100), (33, 33), (64, 200), (7, 301), (2, 2), (1, 1)]
 
 
-def _prefill8(oracle_mod, w, window=0, softcap=0.0):
+def _prefill8(oracle_mod, w, window=0, softcap=0.0, atol_scale=1.0):
     t = to_dev(w)
     c, ref_cache = _int8_cache(oracle_mod, w, t)
     out = _attn8(w, t, c, 1, window, softcap)
     torch.cuda.synchronize()
-    assert_attention_close(out, _ref8(oracle_mod, w, ref_cache, window, softcap), w.name)
+    assert_attention_close(out, _ref8(oracle_mod, w, ref_cache, window, softcap), w.name,
+                           atol_scale)
     return out
 
 
@@ -244,7 +245,7 @@ def test_int8_prefill_scaled_inputs(oracle_mod, scale):
     header(f"int8 prefill scale {scale}")
     w = wl.custom([(40, 120), (9, 300)], 8, 2, 128, dtype=torch.float16, seed=17, write_all=True,
                   scale=scale)
-    _prefill8(oracle_mod, w)
+    _prefill8(oracle_mod, w, atol_scale=min(1.0, scale))
 
 
 def test_int8_prefill_empty_sequences_and_last_row_matches_decode(oracle_mod):

@@ -13,7 +13,7 @@ from tests.gpu_helpers import (assert_attention_close, gpu_attention, gpu_cache,
 pytestmark = pytest.mark.gpu
 
 
-def _run(oracle_mod, w):
+def _run(oracle_mod, w, atol_scale=1.0):
     header(f"prefill {w.name}")
     t = to_dev(w)
     c = gpu_cache(w)
@@ -21,7 +21,7 @@ def _run(oracle_mod, w):
     out = gpu_attention(w, t, c)
     torch.cuda.synchronize()
     ref = oracle_attention(oracle_mod, w, oracle_cache(oracle_mod, w, "all"))
-    assert_attention_close(out, ref, w.name)
+    assert_attention_close(out, ref, w.name, atol_scale)
     return out
 
 
@@ -44,7 +44,7 @@ def test_prefill_scaled_inputs(oracle_mod, scale, G, d):
     up (logits of order 10^3: the query's hi + lo split must carry them)."""
     w = wl.custom([(40, 120), (9, 300)], G * 2, 2, d, dtype=torch.float16, seed=11 + G + d,
                   write_all=True, scale=scale)
-    _run(oracle_mod, w)
+    _run(oracle_mod, w, atol_scale=min(1.0, scale))
 
 
 def test_prefill_fp16_long_prompt(oracle_mod):

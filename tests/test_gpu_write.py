@@ -139,3 +139,74 @@ def test_write_llama3_bulk_fill_sampled(oracle_mod):
     # every (block, kv, offset, head) row was written: its scale word is a valid scale
     words = got[..., 64:68].copy().view("<u4")[..., 0]
     assert ((words & 0x7F800000) != 0x7F800000).all() and (words != 0xA5A5A5A5).all()
+
+
+@pytest.mark.parametrize("mode", ["int4", "int8", "int2"])
+def test_write_skips_slots_past_the_cache(oracle_mod, mode):
+    """Slots at or beyond num_blocks * 16 are skipped like negative ones.  The
+    cache handed to the library is the first NB blocks of a larger buffer, so
+    a store that ignored the bound would land in the guard blocks behind it
+    (inside this test's own allocation) and show there."""
+    header(f"{mode} write: slots past the cache end are skipped")
+    nb, guard, hkv, d, T = 6, 3, 4, 128, 40
+    g = torch.Generator().manual_seed(91)
+    key = torch.randn((T, hkv, d), generator=g).to(torch.bfloat16)
+    value = torch.randn((T, hkv, d), generator=g).to(torch.bfloat16)
+    random.seed(91)
+    slots = torch.tensor(random.sample(range(nb * 16), T), dtype=torch.int64)
+    slots[::4] = nb * 16 + torch.arange(0, T, 4) % (guard * 16)  # inside the guard blocks
+    slots[1] = -1
+    kept = slots.clone()
+    kept[kept >= nb * 16] = -1
+    shape = {"int4": ik.cache_shape, "int8": ik.cache_shape_int8,
+             "int2": ik.cache_shape_int2}[mode](nb + guard, hkv, d)
+    big = torch.full(shape, SENTINEL, dtype=torch.uint8, device="cuda")
+    cache = big[:nb]
+    signs = wl.rht_signs(d)
+    if mode == "int4":
+        ik.int4_kv_write(key.cuda(), value.cuda(), slots.cuda(), cache, signs.cuda())
+        ref = np.full(oracle_mod.cache_shape(nb, 16, hkv, d), SENTINEL, np.uint8)
+        oracle_mod.kv_write(wl.bits16(key), wl.bits16(value), "bf16", kept.numpy(), ref,
+                            signs.numpy())
+    elif mode == "int8":
+        ik.int8_kv_write(key.cuda(), value.cuda(), slots.cuda(), cache)
+        ref = np.full(oracle_mod.cache_shape_int8(nb, 16, hkv, d), SENTINEL, np.uint8)
+        oracle_mod.kv_write_int8(wl.bits16(key), wl.bits16(value), "bf16", kept.numpy(), ref)
+    else:
+        ik.int2_kv_write(key.cuda(), value.cuda(), slots.cuda(), cache, signs.cuda())
+        ref = np.full(oracle_mod.cache_shape_int2(nb, 16, hkv, d), SENTINEL, np.uint8)
+        oracle_mod.kv_write_int2(wl.bits16(key), wl.bits16(value), "bf16", kept.numpy(), ref,
+                                 signs.numpy())
+    torch.cuda.synchronize()
+    got = big.cpu().numpy()
+    assert np.all(got[nb:] == SENTINEL), "a slot past the cache end was stored"
+    assert np.array_equal(got[:nb], ref)
+
+
+def test_decode_step_skips_slot_past_the_cache(oracle_mod):
+    """The fused decode step stores a new token only when its slot lies in
+    the cache; a slot in the guard blocks behind the cache is skipped."""
+    header("fused decode step: a slot past the cache end is skipped")
+    w = wl.custom([(1, 40), (1, 33)], 64, 8, 128, seed=17)
+    nb, guard = w.num_blocks, 2
+    big = torch.full(ik.cache_shape(nb + guard, 8, 128), SENTINEL, dtype=torch.uint8,
+                     device="cuda")
+    cache = big[:nb]
+    t = to_dev(w)
+    pidx, pslots = w.token_set("prior")
+    ik.int4_kv_write(t["key"][pidx.cuda()], t["value"][pidx.cuda()], pslots.cuda(), cache,
+                     t["signs"])
+    nidx, nslots = w.token_set("new")
+    nslots = nslots.clone()
+    nslots[0] = nb * 16 + 5
+    segs = ik.segment_buffers(2, 64, 4, 128)
+    before = big.clone()
+    ik.int4_decode_step(t["key"][nidx.cuda()], t["value"][nidx.cuda()], nslots.cuda(),
+                        t["query"], cache, t["cu"], t["su"], 1, w.max_seqlen_k,
+                        t["block_table"], w.softmax_scale, t["signs"], num_segments=4,
+                        segm_output=segs[0], segm_max=segs[1], segm_expsum=segs[2])
+    torch.cuda.synchronize()
+    assert torch.equal(big[nb:], before[nb:]), "a slot past the cache end was stored"
+    # sequence 1's new token was stored: its slot's rows changed
+    s1 = int(nslots[1])
+    assert not torch.equal(big[s1 // 16, :, s1 % 16], before[s1 // 16, :, s1 % 16])
