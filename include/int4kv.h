@@ -162,6 +162,39 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
                                      void* stream);
 
 /*
+ * int4_paged_attention_noalloc: int4_paged_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments minus the three
+ * segment buffers, the same kernels and the same result bit for bit.
+ *
+ * The decode path's split-K partials ([S, Hq, NS, d] outputs, then [S, Hq, NS]
+ * maxima and exp-sums, fp32, each rounded up to 256 bytes) live in a fixed
+ * device array of INT4KV_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  A call whose partials would not fit
+ * returns INT4KV_ERR_WORKSPACE before anything is enqueued; cfg sizes: 64
+ * segments of 4 sequences x 64 query heads x 128 take 8.5 MB.  The call makes
+ * no hipMalloc or hipFree and uses no allocating library routine; the first
+ * call on a device looks up that device's copy of the array once.  Nothing
+ * in the array has to start at zero (every partial that the reduction reads
+ * is written by the same call).  Calls that overlap on one GPU (different
+ * streams, or threads) share the array and race: serialise them.  With
+ * max_seqlen_q > 1 or num_segments == 1 no partials are used.
+ */
+#define INT4KV_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int4kv_status_t int4_paged_attention_noalloc(const void* q, int64_t q_token_stride, void* out,
+                                             int4kv_dtype_t dtype, const uint8_t* kv_cache,
+                                             int32_t num_blocks, int32_t block_size,
+                                             int32_t num_kv_heads, int32_t head_size,
+                                             int32_t num_q_heads, const int32_t* cu_seqlens_q,
+                                             const int32_t* seqused_k, int32_t num_seqs,
+                                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                             const int32_t* block_table,
+                                             int32_t block_table_stride, float softmax_scale,
+                                             int32_t sliding_window, float softcap,
+                                             const float* rht_signs, int32_t num_segments,
+                                             void* stream);
+
+/*
  * int4_decode_step: int4_kv_write of one new token per sequence followed by
  * int4_paged_attention, in one launch on the decode path.
  * (The write half and the read half above, in the order a decode step runs

@@ -19,7 +19,8 @@ import os
 import torch
 
 __all__ = [
-    "int4_kv_write", "int4_paged_attention", "int4_decode_step", "int4kv_decode_num_segments",
+    "int4_kv_write", "int4_paged_attention", "int4_paged_attention_noalloc", "int4_decode_step",
+    "int4kv_decode_num_segments", "NOALLOC_SCRATCH_BYTES",
     "int4kv_cache_bytes", "int4kv_status_string",
     "int4kv_last_error", "Int4KVError", "cache_shape", "empty_cache", "segment_buffers",
     "library_path", "load_library",
@@ -66,6 +67,10 @@ def load_library():
                                          i32, i32, i32, P, i32, ctypes.c_float, i32,
                                          ctypes.c_float, P, i32, P, P, P, P]
     lib.int4_paged_attention.restype = ctypes.c_int
+    lib.int4_paged_attention_noalloc.argtypes = [P, i64, P, ctypes.c_int, P, i32, i32, i32, i32,
+                                                 i32, P, P, i32, i32, i32, P, i32, ctypes.c_float,
+                                                 i32, ctypes.c_float, P, i32, P]
+    lib.int4_paged_attention_noalloc.restype = ctypes.c_int
     lib.int2_paged_attention.argtypes = lib.int4_paged_attention.argtypes
     lib.int2_paged_attention.restype = ctypes.c_int
     lib.int4_decode_step.argtypes = [P, i64, P, i64, P, P, i64, P, ctypes.c_int, P, i32, i32, i32,
@@ -271,6 +276,41 @@ def int8_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: 
         int(sliding_window), float(softcap), int(num_segments), _ptr(segm_output),
         _ptr(segm_max), _ptr(segm_expsum), _stream(q.device)))
     return out
+
+
+def int4_paged_attention_noalloc(q: torch.Tensor, kv_cache: torch.Tensor,
+                                 cu_seqlens_q: torch.Tensor, seqused_k: torch.Tensor,
+                                 max_seqlen_q: int, max_seqlen_k: int, block_table: torch.Tensor,
+                                 softmax_scale: float, rht_signs: torch.Tensor,
+                                 out: torch.Tensor, num_segments: int = 1,
+                                 sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
+    """int4_paged_attention with the split-K partials in the library's fixed device
+    buffer (NOALLOC_SCRATCH_BYTES per GPU): nothing is allocated, ``out`` included."""
+    lib = load_library()
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [Tq, Hq, d] with contiguous heads")
+    Tq, hq, d = q.shape
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous with q's shape and dtype")
+    nb, two, bs, hkv, _ = kv_cache.shape
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k),
+                    ("block_table", block_table)):
+        if t.dtype != torch.int32 or not t.is_contiguous() and t is not block_table:
+            raise ValueError(f"{name} must be contiguous int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [S, max_blocks] with unit column stride")
+    if not rht_signs.is_contiguous():
+        raise ValueError("rht_signs must be contiguous")
+    S = seqused_k.shape[0]
+    _check(lib.int4_paged_attention_noalloc(
+        _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype), _ptr(kv_cache), nb, bs, hkv, d, hq,
+        _ptr(cu_seqlens_q), _ptr(seqused_k), S, int(max_seqlen_q), int(max_seqlen_k),
+        _ptr(block_table), block_table.stride(0), float(softmax_scale), int(sliding_window),
+        float(softcap), _ptr(rht_signs), int(num_segments), _stream(q.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # INT4KV_NOALLOC_SCRATCH_BYTES of include/int4kv.h
 
 
 def int4_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,

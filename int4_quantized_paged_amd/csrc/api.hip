@@ -14,6 +14,37 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+// Split-K partials of int4_paged_attention_noalloc: a fixed device array,
+// one copy per GPU, held until the process ends.  Host code never passes its
+// name to a kernel (on the host it is only a stand-in symbol): the device
+// address is looked up once per device with hipGetSymbolAddress.
+constexpr size_t kNoallocScratchFloats = INT4KV_NOALLOC_SCRATCH_BYTES / sizeof(float);
+static __device__ __align__(256) float scratch[kNoallocScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (nullptr and an error on failure).
+hipError_t scratch_for_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// floats of each split-K partials array rounded up to 64 (256 bytes)
+int64_t round64(int64_t n) { return (n + 63) / 64 * 64; }
+
 int4kv_status_t fail(int4kv_status_t s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -100,7 +131,7 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
                                 int32_t block_size, float softmax_scale, int32_t sliding_window,
                                 float softcap, const float* rht_signs, int32_t num_segments,
                                 float* segm_output, float* segm_max, float* segm_expsum,
-                                int4kv::AttnArgs& a) {
+                                int4kv::AttnArgs& a, bool internal_workspace = false) {
   if (!q || !out || !cu_seqlens_q || !seqused_k || !block_table)
     return fail(INT4KV_ERR_INVALID_ARG, "null q, out, cu_seqlens_q, seqused_k or block_table");
   if (num_q_heads < 1 || num_q_heads % num_kv_heads)
@@ -125,7 +156,8 @@ int4kv_status_t check_attention(const void* q, int64_t q_token_stride, void* out
     return fail(INT4KV_ERR_INVALID_ARG, "softcap must be finite, and > 0 only with a finite "
                 "reciprocal");
   const bool decode = max_seqlen_q == 1;
-  if (decode && num_segments > 1 && (!segm_output || !segm_max || !segm_expsum))
+  if (decode && num_segments > 1 && !internal_workspace &&
+      (!segm_output || !segm_max || !segm_expsum))
     return fail(INT4KV_ERR_WORKSPACE, "num_segments %d > 1 needs the three segment buffers",
                 num_segments);
   if (num_segments > 65535) return fail(INT4KV_ERR_INVALID_ARG, "num_segments too large");
@@ -397,6 +429,61 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
   const bool decode = max_seqlen_q == 1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = decode ? int4kv::launch_decode(a, st) : int4kv::launch_prefill(a, st);
+  if (e != hipSuccess)
+    return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int4kv_status_t int4_paged_attention_noalloc(const void* q, int64_t q_token_stride, void* out,
+                                             int4kv_dtype_t dtype, const uint8_t* kv_cache,
+                                             int32_t num_blocks, int32_t block_size,
+                                             int32_t num_kv_heads, int32_t head_size,
+                                             int32_t num_q_heads, const int32_t* cu_seqlens_q,
+                                             const int32_t* seqused_k, int32_t num_seqs,
+                                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                             const int32_t* block_table,
+                                             int32_t block_table_stride, float softmax_scale,
+                                             int32_t sliding_window, float softcap,
+                                             const float* rht_signs, int32_t num_segments,
+                                             void* stream) {
+  int4kv_status_t s =
+      check_common(kv_cache, num_blocks, block_size, num_kv_heads, head_size, rht_signs);
+  if (s != INT4KV_OK) return s;
+  if (dtype != INT4KV_F16 && dtype != INT4KV_BF16)
+    return fail(INT4KV_ERR_INVALID_ARG, "dtype %d is neither F16 nor BF16", (int)dtype);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(INT4KV_ERR_INVALID_ARG, "negative num_seqs / max_seqlen_q / max_seqlen_k");
+  if (num_seqs == 0 || max_seqlen_q == 0) return ok();
+  int4kv::AttnArgs a;
+  s = check_attention(q, q_token_stride, out, dtype, kv_cache, num_kv_heads, head_size,
+                      num_q_heads, cu_seqlens_q, seqused_k, num_seqs, max_seqlen_q, max_seqlen_k,
+                      block_table, block_table_stride, block_size, softmax_scale, sliding_window,
+                      softcap, rht_signs, num_segments, nullptr, nullptr, nullptr, a,
+                      /*internal_workspace=*/true);
+  if (s != INT4KV_OK) return s;
+  const bool split = max_seqlen_q == 1 && num_segments > 1;
+  // partials: [S, Hq, NS, d] outputs, then [S, Hq, NS] maxima and exp-sums
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * (num_segments > 0 ? num_segments : 1);
+  const int64_t need = split ? round64(rows * head_size) + 2 * round64(rows) : 0;
+  if (need > (int64_t)kNoallocScratchFloats)
+    return fail(INT4KV_ERR_WORKSPACE,
+                "split-K partials of %lld bytes exceed the library's fixed %lld-byte buffer "
+                "(num_seqs * num_q_heads * num_segments * (head_size + 2) floats); use fewer "
+                "segments or int4_paged_attention with caller-owned buffers",
+                (long long)(need * 4), (long long)INT4KV_NOALLOC_SCRATCH_BYTES);
+  if (split) {
+    float* base = nullptr;
+    hipError_t e = scratch_for_current_device(&base);
+    if (e != hipSuccess)
+      return fail(INT4KV_ERR_LAUNCH, "device scratch lookup: %s", hipGetErrorString(e));
+    a.segm_out = base;
+    a.segm_max = base + round64(rows * head_size);
+    a.segm_sum = a.segm_max + round64(rows);
+  } else {
+    a.segm_out = a.segm_max = a.segm_sum = nullptr;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = max_seqlen_q == 1 ? int4kv::launch_decode(a, st) : int4kv::launch_prefill(a, st);
   if (e != hipSuccess)
     return fail(INT4KV_ERR_LAUNCH, "attention launch: %s", hipGetErrorString(e));
   return ok();
