@@ -14,10 +14,11 @@ in the 256 MB Infinity Cache.
 Steps are plain library calls: the host enqueues a step in about a fifth of
 its GPU time, and HIP-graph replays of the same calls (`--graph`, checked bit
 for bit against plain calls) measured a few microseconds slower per step.
-The default warm-up (2000 steps, about 0.2 s) lets the GPU reach its steady
-clock and address-translation state: after 100 warm-up steps the next 200
-still ran about 4% slower than they do after 2000 (106.5-108 against
-101.8-103.5 us per step on one box), and the first tens run about 15% slower.
+Before the warm-up steps, about 0.3 s of untimed steps bring the GPU to its
+steady clock and address-translation state (the first tens of steps on a
+fresh process run up to 15% slower); the JSON line reports how many.  Every
+timed step and attention call sits between two HIP events on the launch
+stream, and the line carries their first five, median, mean and last five.
 Prints one JSON line: decode
 effective KV GB/s (packed K+V bytes of every key attended, once per KV head,
 over the step time), the bulk cache-write rate (tokens/s, from a timed
@@ -190,6 +191,47 @@ def _median_event_us(fn, reps, rounds=5):
     return ts[len(ts) // 2]
 
 
+def settle(run, nbufs: int, seconds: float = 0.3, max_steps: int = 5000) -> dict:
+    """Untimed steps until the GPU reaches its steady clock and address-
+    translation state (about 0.3 s of the same work): the first tens of steps
+    on a fresh process run up to 15% slower.  Done before the warm-up steps."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_steps:
+        for _ in range(50):
+            run[n % nbufs]()
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return {"steps": n, "seconds": round(time.perf_counter() - t0, 3)}
+
+
+def timed_calls(run, nbufs: int, n: int):
+    """n calls, each between two HIP events recorded on the current stream (the
+    stream the library launches on).  Returns (wall seconds around the n calls,
+    bracketed by synchronisation, per-call event milliseconds)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(n):
+        run[i % nbufs]()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def call_stats(ms):
+    """First 5, median, mean and last 5 of per-call times (microseconds)."""
+    us = [x * 1e3 for x in ms]
+    srt = sorted(us)
+    return {"first5_us": [round(x, 2) for x in us[:5]], "median_us": round(srt[len(srt) // 2], 2),
+            "mean_us": round(sum(us) / len(us), 2), "last5_us": [round(x, 2) for x in us[-5:]],
+            "min_us": round(srt[0], 2), "max_us": round(srt[-1], 2)}
+
+
 def _graph_us(fn, n):
     """Per-call time of `n` calls of fn captured in one HIP graph and replayed
     (median of five rounds of 5 replays): the GPU's time for the calls without
@@ -222,6 +264,7 @@ def _attention_setup(w, dev, ns, ncaches=1):
         ik.int4_paged_attention(w.query, c, cu, su, w.max_seqlen_q, w.max_seqlen_k, bt,
                                 w.softmax_scale, signs, out=out, num_segments=ns,
                                 segm_output=segs[0], segm_max=segs[1], segm_expsum=segs[2])
+    call.caches, call.signs = caches, signs
     return call
 
 
@@ -239,14 +282,33 @@ def other_rows(dev):
             call()
         us = _median_event_us(call, 10)
         fl = w.attention_flops()
+        # the mix's step as a whole: write its new tokens (sum of q_b), then attend
+        idx_n, slots_n = w.token_set("new")
+        kn, vn = w.key[idx_n.to(dev)].contiguous(), w.value[idx_n.to(dev)].contiguous()
+        sn = slots_n.to(dev)
+        cache0, sg = call.caches[0], call.signs
+
+        def write_new():
+            ik.int4_kv_write(kn, vn, sn, cache0, sg)
+
+        def write_and_attend():
+            write_new()
+            call()
+        for _ in range(3):
+            write_and_attend()
+        us_w = _median_event_us(write_new, 10)
+        us_wa = _median_event_us(write_and_attend, 10)
         rows[f"prefill_d{d}"] = {
             "workload": f"chunked-prefill mix: 32 seqs, {sum(w.query_lens)} query tokens, "
                         f"{sum(w.kv_lens)} keys, 32 q / 8 KV heads, d {d}",
             "us": round(us, 2), "tflops": round(fl / us / 1e6, 1),
             "mfma_frac": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
             "algorithmic_gflop": round(fl / 1e9, 2),
-            "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
-        del w, call
+            "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1),
+            "write_new_tokens": int(idx_n.numel()), "write_us": round(us_w, 2),
+            "write_GBps": round(w.write_bytes("new") / us_w / 1e3, 1),
+            "write_plus_attention_us": round(us_wa, 2)}
+        del w, call, kn, vn
     # the same mix over the INT8 per-token-head cache (d 128)
     w = wl.chunked_prefill(device=dev, head_size=128)
     c8 = torch.empty(ik.cache_shape_int8(w.num_blocks, w.num_kv_heads, 128), dtype=torch.uint8,
@@ -499,7 +561,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-rows", action="store_true",
                     help="skip the prefill and Llama-3-shaped decode measurements")
@@ -551,24 +613,19 @@ def main():
         run = [lambda b=b: step_fn(b) for b in bufs]
         run_attn = [lambda b=b: attend(b) for b in bufs]
 
+    settled = settle(run, nbufs)
     for i in range(args.warmup):
         run[i % nbufs]()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run[i % nbufs]()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, step_ms = timed_calls(run, nbufs, args.steps)
     ms_per_step = wall * 1e3 / args.steps
 
-    # attention call alone: HIP events on the launch stream around back-to-back calls
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
+    # the attention call alone (decode + segment reduction), warmed up the same
+    # way; HIP events on the launch stream around each call
+    for i in range(args.warmup):
         run_attn[i % nbufs]()
-    e1.record()
-    e1.synchronize()
-    attn_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    _, attn_ms = timed_calls(run_attn, nbufs, args.steps)
+    attn_s = sum(attn_ms) / len(attn_ms) / 1e3
 
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_s * 1e6:.2f} us")
     wr_tps, wr_t, wr_T = measure_bulk_write(bufs[0])
@@ -578,7 +635,7 @@ def main():
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16 mfma/f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8 mfma (scores) + f16 mfma (P.V), f32 accumulate",
         "data": "synthetic",
         "config": {"workload": "long-context decode: 4 seqs x 131072 tokens, 64 q / 8 KV heads, "
                                "head_size 128, bf16 K/V/Q N(0,1), block_size 16, split-K 64 "
@@ -586,7 +643,10 @@ def main():
                    "step_call": ("int4_kv_write + int4_paged_attention" if args.separate_calls
                                  else "int4_decode_step (write fused into the decode launch)"),
                    "global_batch": 4, "seq_len": 131072, "parallelism": "none (1 GPU)",
-                   "launch": "hip graph replay" if args.graph else "plain calls"},
+                   "launch": "hip graph replay" if args.graph else "plain calls",
+                   "settle": settled},
+        "step_events": call_stats(step_ms),
+        "attention_call_events": call_stats(attn_ms),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "num_segments_library_choice": ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads,
                                                                      w.max_seqlen_k),
@@ -594,6 +654,9 @@ def main():
         "write_bulk": {"tokens": wr_T, "seconds": wr_t,
                        "GB_per_s": round(w.write_bytes("all") / wr_t / 1e9, 1)},
         "roofline": {"kernel": "decode_lds_kernel + reduce_wave_kernel (one int4_paged_attention call)",
+                     "timing": "mean of per-call HIP event times over the timed attention calls "
+                               "(decode kernel, segment reduction and the dispatch gap between "
+                               "them)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kv_bytes,

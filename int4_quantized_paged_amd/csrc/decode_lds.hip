@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   constexpr int DWG = DW / 4;    // code dwords per lane group in the score operand
   constexpr int NCK = Q2 ? D / 32 : D / 64;  // int8 MFMA k-chunks (INT2: two bit planes)
   constexpr int NCOL = D / 16;   // P.V column tiles (INT2: elements per lane)
-  constexpr int NACC = NCOL;  // P.V accumulators
+  constexpr int NACC = Q2 ? 2 * NCOL : NCOL;  // P.V accumulators (INT2: sigma and tau sums)
   constexpr int RPG = G <= 4 ? 1 : G / 4;
   constexpr int EPL = G * D / 64;
   constexpr int LPQ = 64 / G;
@@ -465,13 +465,19 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
 #pragma unroll
   for (int c = 0; c < NACC; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // INT4 / INT8: the P.V sums of the last tile, added to oacc at the start
+  // of the next step (the matrix cores' latency is then covered)
+  float4_t pend[NACC];
+#pragma unroll
+  for (int c = 0; c < NACC; ++c) pend[c] = float4_t{0.f, 0.f, 0.f, 0.f};
   const int noff = (D == 64) ? 4 * (col >> 3) : 0;  // nibble offset of this lane's V dword
   // O (rotated domain, zero point not yet removed) of column tile c: the low
   // nibble directly, the high nibble as (byte - low) / 16 (INT4); INT8: every
   // tile holds whole codes offset by 128
   auto o_of = [&](int c, int v) -> float {
     if constexpr (Q8) return oacc[c][v] * 16777216.0f;  // 2^24
-    if constexpr (Q2) return oacc[c][v];  // element c: sum W level
+    if constexpr (Q2)  // element c: u * sum W sigma + v * sum W tau = sum W level
+      return fmaf(kLmU, oacc[2 * c][v], kLmV * oacc[2 * c + 1][v]);
     return (c & 1) ? (oacc[c][v] - oacc[c - 1][v]) * 1048576.0f  // 2^20
                    : oacc[c][v] * 16777216.0f;                   // 2^24
   };
@@ -616,6 +622,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     k_operands(sn, kb);
     tile_words(sn, nw);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!Q2) {  // tile t-1's P.V sums, under the reference they were taken with
+#pragma unroll
+      for (int c = 0; c < NACC; c += Q8 ? 1 : 2) oacc[c] += pend[c];
+    }
 
     // phase 1: logits z = c0 sK (S - zK sum(q')) in base-2 units
     bool kval[2];
@@ -696,18 +706,19 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
     const half8_t wop = *reinterpret_cast<const half8_t*>(wt + rd_off);
     const half8_t wop_lo = *reinterpret_cast<const half8_t*>(wt + rd_lo);
     phase_end(1, kb, nxt);
-    // acc += W B for one column tile.  The tile's products are summed on the
-    // matrix cores from zero (hi, then lo on top) and tiles are accumulated
-    // in fp32 on the vector ALU: the matrix cores align an incoming
-    // accumulator to the largest product of the instruction and keep only
-    // about 15 bits of it below that product, so a running sum that a later,
-    // heavier key outweighs would lose its low bits there.
+    // acc += W B for one column tile of subnormal codes (INT4, INT8).  The
+    // tile's products are summed on the matrix cores from zero (hi, then lo
+    // on top) and tiles are accumulated in fp32 on the vector ALU: the matrix
+    // cores cut a dot product off about 24 bits below the largest operand
+    // exponents, where a subnormal code counts as 2^-14, so an incoming
+    // running sum that a heavier key's products outweigh keeps only about 15
+    // bits there.
     auto pv_tile = [&](const half8_t& bop) {
       const float4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           wop, bop, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       return __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, bop, t, 0, 0, 0);
     };
-    auto pv = [&](float4_t& acc, const half8_t& bop) { acc += pv_tile(bop); };
+    auto pv = [&](float4_t& dst, const half8_t& bop) { dst = pv_tile(bop); };
 
     if constexpr (Q2) {
       // phase 3 (INT2): byte bl of the lane's dword of two slot keys, zero-
@@ -743,11 +754,13 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
           }
           const half8_t sb = __builtin_bit_cast(half8_t, xs);
           const half8_t tb = __builtin_bit_cast(half8_t, xt);
-          // one accumulator per element: O_e += u (W sigma) + v (W tau), the
-          // planes combined in fp32 per tile
-          const float4_t ts = pv_tile(sb), tt = pv_tile(tb);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[e][r] = fmaf(kLmV, tt[r], fmaf(kLmU, ts[r], oacc[e][r]));
+          // the +-1.0 operands are normal numbers, so the matrix cores'
+          // running sums keep fp32 precision across tiles: no per-tile flush
+          oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, sb, oacc[2 * e], 0, 0, 0);
+          oacc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, sb, oacc[2 * e], 0, 0, 0);
+          oacc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, tb, oacc[2 * e + 1], 0, 0, 0);
+          oacc[2 * e + 1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, tb, oacc[2 * e + 1], 0, 0, 0);
         }
     } else if constexpr (Q8) {
       // phase 3 (INT8): column tile c takes byte c % 4 of the lane's dword
@@ -766,7 +779,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       phase_end(2, kb, nxt);
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) {
-        pv(oacc[c], __builtin_bit_cast(half8_t, vx8[c]));
+        pv(pend[c], __builtin_bit_cast(half8_t, vx8[c]));
       }
     } else {
     // phase 3: V operands.  Byte beta of the lane's dword of two slot keys,
@@ -787,8 +800,17 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       u32x4_t vl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) vl[i] = vx[bb][i] & 0x000F000Fu;
-      pv(oacc[2 * bb + 1], __builtin_bit_cast(half8_t, vx[bb]));
-      pv(oacc[2 * bb], __builtin_bit_cast(half8_t, vl));
+      // whole bytes straight into the running sums: their columns reach the
+      // output only through the high nibble, (bytes - low) / 16, which
+      // scales a truncated running sum down by 16; the low nibbles, whose
+      // sums are the output as they are, go through the per-tile flush
+      {
+        const half8_t xb = __builtin_bit_cast(half8_t, vx[bb]);
+        float4_t& ox = oacc[2 * bb + 1];
+        ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, xb, ox, 0, 0, 0);
+        ox = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop_lo, xb, ox, 0, 0, 0);
+      }
+      pv(pend[2 * bb], __builtin_bit_cast(half8_t, vl));
     }
     }
     // the remaining score groups of tile t+1 share this region: one MFMA per
@@ -796,7 +818,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
     for (int i = 3; i < NGROUP; ++i) score_group(i, kb, nxt);
 #pragma unroll
-    for (int j = 0; j < (Q2 ? 4 : 2) * NACC + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
+    for (int j = 0; j < 2 * NACC + 3 * (NGROUP > 3 ? NGROUP - 3 : 0); ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
@@ -827,6 +849,10 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   }
   if (t < ntile) step(t, accA, accB, wA, wB);
   wait_vmem<0>();  // drain the clamped look-ahead copies
+  if constexpr (!Q2) {  // the last tile's P.V sums
+#pragma unroll
+    for (int c = 0; c < NACC; c += Q8 ? 1 : 2) oacc[c] += pend[c];
+  }
 
   // ---- finalise: sums over the 16 lanes of a group
 #pragma unroll
