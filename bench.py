@@ -530,31 +530,100 @@ def other_rows(dev):
     return rows
 
 
-def cpu_baseline(b):
-    """The oracle (plain single-threaded C) on the same workload: all 524288
-    tokens encoded into the packed cache, then one decode query of all 64
-    heads attended for each of the 4 sequences (textbook fp64 attention)."""
+def _first_sequences(w, n):
+    """The first n sequences of a workload as a workload of their own (same
+    cache ids): their K/V tokens, query rows and block-table rows."""
+    off = w.token_offsets()
+    cuq = w.cu_seqlens_q().tolist()
+    dev = w.key.device
+    return wl.Workload(w.name + f" first {n}", w.dtype, w.num_q_heads, w.num_kv_heads,
+                       w.head_size, w.num_blocks, w.kv_lens[:n], w.query_lens[:n],
+                       w.write_lens[:n], w.block_table[:n].clone(), w.key[:off[n]],
+                       w.value[:off[n]], w.query[:cuq[n]], w.signs)
+
+
+def _oracle_case(w, which_write="all"):
+    """Host inputs of one workload for the oracle: raw bits, slots, metadata."""
+    idx, slots = w.token_set(which_write)
+    dev_idx = idx.to(w.key.device)
+    return dict(kb=wl.bits16(w.key[dev_idx]), vb=wl.bits16(w.value[dev_idx]),
+                qb=wl.bits16(w.query), slots=slots.numpy(), T=int(idx.numel()),
+                dt="bf16" if w.dtype == torch.bfloat16 else "f16",
+                cu=w.cu_seqlens_q().numpy(), su=w.seqused_k().numpy(),
+                bt=w.block_table.numpy(), signs=w.signs.numpy(), w=w)
+
+
+def _oracle_times(oracle, c, reps):
+    """Median of `reps` runs of the oracle's write (all tokens of the case) and of
+    its plain attention, seconds."""
+    w = c["w"]
+    tw, ta = [], []
+    for _ in range(reps):
+        cache = np.zeros(oracle.cache_shape(w.num_blocks, 16, w.num_kv_heads, w.head_size),
+                         np.uint8)
+        t0 = time.perf_counter()
+        oracle.kv_write(c["kb"], c["vb"], c["dt"], c["slots"], cache, c["signs"])
+        tw.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        oracle.attention_plain(c["qb"], c["dt"], cache, c["cu"], c["su"], c["bt"],
+                               w.softmax_scale, c["signs"], w.num_q_heads)
+        ta.append(time.perf_counter() - t0)
+    return sorted(tw)[len(tw) // 2], sorted(ta)[len(ta) // 2]
+
+
+def cpu_baseline(b, dev):
+    """The oracle (plain C: fp32 encoding steps, textbook fp64 attention over the
+    decoded cache) timed on this host: the long-context workload on one core
+    (a bounded sample) and with OpenMP on every core this process may use
+    (the whole workload), plus every other configuration with OpenMP.
+    Median of three runs each; host inputs already in memory."""
     import oracle
     oracle._load()
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    omp = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
     w = b["w"]
     key, value, _ = b["bulk"]
-    kb, vb = wl.bits16(key), wl.bits16(value)
-    qb = wl.bits16(w.query)
-    _, slots = w.token_set("all")
-    cache = np.zeros(oracle.cache_shape(w.num_blocks, 16, w.num_kv_heads, w.head_size), np.uint8)
-    t0 = time.perf_counter()
-    oracle.kv_write(kb, vb, "bf16", slots.numpy(), cache, w.signs.numpy())
-    t_write = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.attention_plain(qb, "bf16", cache, w.cu_seqlens_q().numpy(), w.seqused_k().numpy(),
-                           w.block_table.numpy(), w.softmax_scale, w.signs.numpy(), w.num_q_heads)
-    t_attn = time.perf_counter() - t0
+    full = dict(kb=wl.bits16(key), vb=wl.bits16(value), qb=wl.bits16(w.query),
+                slots=w.token_set("all")[1].numpy(), dt="bf16", cu=w.cu_seqlens_q().numpy(),
+                su=w.seqused_k().numpy(), bt=w.block_table.numpy(), signs=w.signs.numpy(), w=w)
     kv = w.kv_bytes_attended()
-    return {"value": round(kv / t_attn / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole workload (4 x 131072 keys, 8 KV heads, 64 query heads): plain "
-                      f"fp64 attention {t_attn:.2f} s; its cache write of 524288 tokens "
-                      f"{t_write:.2f} s",
-            "write_tokens_per_s": round(key.shape[0] / t_write, 1)}
+    # one core: sequence 0 of the four (131072 keys), written and attended
+    one = wl.Workload(w.name + " seq 0", w.dtype, w.num_q_heads, w.num_kv_heads, w.head_size,
+                      w.num_blocks, w.kv_lens[:1], w.query_lens[:1], w.write_lens[:1],
+                      w.block_table[:1].clone(), key[:w.kv_lens[0]], value[:w.kv_lens[0]],
+                      w.query[:1], w.signs)
+    c1 = _oracle_case(one)
+    oracle.set_num_threads(1)
+    tw1, ta1 = _oracle_times(oracle, c1, 3)
+    kv1 = one.kv_bytes_attended()
+    oracle.set_num_threads(omp)
+    twn, tan = _oracle_times(oracle, full, 3)
+    res = {"value": round(kv / tan / 1e9, 4), "unit": "GB/s", "cores": omp, "kind": "oracle",
+           "sample": f"the whole long-context workload (4 x 131072 keys, 8 KV heads, 64 query "
+                     f"heads) on {omp} OpenMP threads: plain fp64 attention {tan:.3f} s, its "
+                     f"cache write of {key.shape[0]} tokens {twn:.3f} s (median of 3)",
+           "write_tokens_per_s": round(key.shape[0] / twn, 1),
+           "single_core": {"value": round(kv1 / ta1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                           "sample": f"sequence 0 of the workload (131072 keys): attention "
+                                     f"{ta1:.3f} s, write {tw1:.3f} s (median of 3)",
+                           "write_tokens_per_s": round(one.kv_lens[0] / tw1, 1)},
+           "host_cpus": cores}
+    # the other configurations, OpenMP, median of 3 (the chunked-prefill mix on a
+    # sample of its first 4 sequences: its plain attention is the longest)
+    per = {}
+    for name, wk in (("tiny_causal", wl.tiny()), ("gqa_decode", wl.gqa_decode()),
+                     ("llama3_8b_decode", wl.llama3_8b_decode(device=dev)),
+                     ("chunked_prefill_d128_first4",
+                      _first_sequences(wl.chunked_prefill(device=dev), 4))):
+        c = _oracle_case(wk)
+        tw, ta = _oracle_times(oracle, c, 3)
+        per[name] = {"write_tokens": c["T"], "write_s": round(tw, 4),
+                     "write_tokens_per_s": round(c["T"] / tw, 1),
+                     "attention_s": round(ta, 4),
+                     "attention_kv_GBps": round(wk.kv_bytes_attended() / ta / 1e9, 4)}
+        del c, wk
+    res["configs"] = per
+    return res
 
 
 def main():
@@ -666,7 +735,7 @@ def main():
         res["other_rows"] = other_rows(dev)
         log("other rows measured")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(bufs[0])
+        res["cpu_baseline"] = cpu_baseline(bufs[0], dev)
         log("oracle baseline timed")
     else:
         res["cpu_baseline"] = None

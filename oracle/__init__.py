@@ -21,7 +21,10 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZED=1 loads the AddressSanitizer/UBSan build (liboracle_san.so;
+# the process must preload the ASan runtime)
+_SANITIZED = os.environ.get("ORACLE_SANITIZED") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if _SANITIZED else "liboracle.so")
 _lib = None
 
 _DT = {"f16": 0, "bf16": 1}
@@ -33,7 +36,7 @@ def _load():
         return _lib
     if not os.path.exists(_LIB_PATH):
         from . import build as _b  # compile on first use (gcc is everywhere)
-        _b.build()
+        _b.build(sanitized=_SANITIZED)
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
@@ -62,8 +65,20 @@ def _load():
     lib.oracle_decode_row_int2.argtypes = [P, i32, P, P]
     lib.oracle_attention_plain_int2.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i32,
                                                 P, P, i32, P, i32, f64, P, i32, f64, P]
+    lib.oracle_set_num_threads.argtypes = [i32]
+    lib.oracle_max_threads.restype = i32
     _lib = lib
     return lib
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the write and plain-attention loops (timing only: the
+    results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:

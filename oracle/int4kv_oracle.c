@@ -55,6 +55,9 @@
  *           and this is the usual tanh soft cap.)
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -215,7 +218,12 @@ void oracle_kv_write(const uint16_t* key, int64_t key_stride, const uint16_t* va
                      int num_tokens, uint8_t* cache, int num_blocks, int block_size,
                      int num_kv_heads, int d, const float* signs) {
   (void)num_blocks;
+  /* tokens are independent (each writes its own rows), so OpenMP threads may
+   * take them in any order; every row is computed exactly as with one thread */
+#pragma omp parallel
+  {
   float* y = (float*)malloc(sizeof(float) * (size_t)d);
+#pragma omp for schedule(static)
   for (int t = 0; t < num_tokens; ++t) {
     int64_t slot = slot_mapping[t];
     if (slot < 0) continue;
@@ -238,6 +246,7 @@ void oracle_kv_write(const uint16_t* key, int64_t key_stride, const uint16_t* va
     }
   }
   free(y);
+  }
 }
 
 static uint32_t or_row_word(const uint8_t* row, int d) {
@@ -285,11 +294,16 @@ void oracle_attention_plain(const uint16_t* q, int64_t q_stride, int dtype,
                             double softcap, double* out) {
   (void)num_blocks;
   int G = num_q_heads / num_kv_heads;
-  for (int b = 0; b < num_seqs; ++b) {
+  /* (sequence, kv head) pairs are independent (each writes its own output
+   * rows), so OpenMP threads may take them in any order; every output is
+   * computed exactly as with one thread */
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < num_seqs * num_kv_heads; ++bh) {
+    const int b = bh / num_kv_heads, h = bh % num_kv_heads;
     int q0 = cu_seqlens_q[b], qlen = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
     int64_t L = seqused_k[b];
     if (qlen <= 0 || L <= 0) continue;
-    for (int h = 0; h < num_kv_heads; ++h) {
+    {
       /* decode every key and value of this (sequence, kv head) once */
       double* K = (double*)malloc(sizeof(double) * (size_t)(L * d));
       double* V = (double*)malloc(sizeof(double) * (size_t)(L * d));
@@ -813,4 +827,22 @@ void oracle_attention_plain_int2(const uint16_t* q, int64_t q_stride, int dtype,
       free(V);
     }
   }
+}
+
+/* Threads the OpenMP loops above use (the timing harness only; results do not
+ * depend on it).  Without OpenMP everything runs on one thread. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
