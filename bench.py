@@ -175,6 +175,30 @@ def measure_bulk_write(b, reps: int = 5):
     return T / t, t, T
 
 
+def measure_stream_ceiling(read_bytes: int, write_bytes: int, reps: int = 5):
+    """A plain streaming kernel with the bulk write's read:write byte mix (no
+    arithmetic beyond XOR), timed like the write: the bandwidth an HBM pass of
+    that mix attains, which the write is compared against."""
+    read_bytes -= read_bytes % 16
+    write_bytes -= write_bytes % 16
+    src = torch.empty(read_bytes, dtype=torch.uint8, device="cuda").random_(0, 256)
+    dst = torch.empty(write_bytes, dtype=torch.uint8, device="cuda")
+    ik.int4kv_stream_rw(src, read_bytes, dst, write_bytes)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ik.int4kv_stream_rw(src, read_bytes, dst, write_bytes)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    times.sort()
+    t = times[len(times) // 2]
+    del src, dst
+    return t, read_bytes, write_bytes
+
+
 def _median_event_us(fn, reps, rounds=5):
     """Per-call time of `reps` back-to-back calls between two HIP events on the
     launch stream (as the headline attention figure), median of `rounds`."""
@@ -703,6 +727,10 @@ def main():
 
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_s * 1e6:.2f} us")
     wr_tps, wr_t, wr_T = measure_bulk_write(bufs[0])
+    bk, bv, bslots = bufs[0]["bulk"]
+    wr_read = bk.numel() * bk.element_size() + bv.numel() * bv.element_size() + bslots.numel() * 8
+    wr_written = w.write_bytes("all") - wr_read  # write_bytes counts the inputs read too
+    st_t, st_r, st_w = measure_stream_ceiling(wr_read, wr_written)
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = kv_bytes / attn_s / 1e9
     traffic = _traffic_from_profiles(_kernel_hash())
@@ -726,7 +754,13 @@ def main():
                                                                      w.max_seqlen_k),
         "write_tokens_per_s": round(wr_tps, 1),
         "write_bulk": {"tokens": wr_T, "seconds": wr_t,
-                       "GB_per_s": round(w.write_bytes("all") / wr_t / 1e9, 1)},
+                       "bytes_read": wr_read, "bytes_written": wr_written,
+                       "GB_per_s": round(wr_written / wr_t / 1e9, 1),
+                       "read_plus_write_GB_per_s": round((wr_read + wr_written) / wr_t / 1e9, 1),
+                       "stream_same_mix": {
+                           "seconds": st_t, "bytes_read": st_r, "bytes_written": st_w,
+                           "read_plus_write_GB_per_s": round((st_r + st_w) / st_t / 1e9, 1),
+                           "write_time_over_stream_time": round(wr_t / st_t, 4)}},
         "roofline": {"kernel": "decode_lds_kernel + reduce_wave_kernel (one int4_paged_attention call)",
                      "timing": "mean of per-call HIP event times over the timed attention calls "
                                "2..K (decode kernel, segment reduction, the dispatch gaps)",

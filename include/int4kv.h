@@ -162,6 +162,21 @@ int4kv_status_t int4_paged_attention(const void* q, int64_t q_token_stride, void
                                      void* stream);
 
 /*
+ * int4kv_stream_rw: a plain streaming kernel that reads read_bytes from src and
+ * writes write_bytes to dst, for measuring the bandwidth an HBM pass with a
+ * given read:write mix attains on the device: the ceiling the cache write
+ * (inputs read, packed rows written) is compared against.  Not a step of the
+ * method.  In 16-byte units, with nr read and nw written units, written unit w
+ * is the XOR of the read units w, w + nw, w + 2 nw, ... below nr (so no read
+ * is dead); accesses are coalesced.  Byte counts must be multiples of 16 and
+ * pointers 16-byte aligned; reads with write_bytes 0 are rejected
+ * (INT4KV_ERR_INVALID_ARG); write_bytes 0 with read_bytes 0 is a no-op.  The
+ * launch is asynchronous on the given stream (NULL: the default stream).
+ */
+int4kv_status_t int4kv_stream_rw(const void* src, int64_t read_bytes, void* dst,
+                                 int64_t write_bytes, void* stream);
+
+/*
  * int4_paged_attention_noalloc: int4_paged_attention for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same arguments minus the three

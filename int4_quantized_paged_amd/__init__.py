@@ -71,6 +71,8 @@ def load_library():
                                                  i32, P, P, i32, i32, i32, P, i32, ctypes.c_float,
                                                  i32, ctypes.c_float, P, i32, P]
     lib.int4_paged_attention_noalloc.restype = ctypes.c_int
+    lib.int4kv_stream_rw.argtypes = [P, i64, P, i64, P]
+    lib.int4kv_stream_rw.restype = ctypes.c_int
     lib.int2_paged_attention.argtypes = lib.int4_paged_attention.argtypes
     lib.int2_paged_attention.restype = ctypes.c_int
     lib.int4_decode_step.argtypes = [P, i64, P, i64, P, P, i64, P, ctypes.c_int, P, i32, i32, i32,
@@ -311,6 +313,17 @@ def int4_paged_attention_noalloc(q: torch.Tensor, kv_cache: torch.Tensor,
 
 
 NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # INT4KV_NOALLOC_SCRATCH_BYTES of include/int4kv.h
+
+
+def int4kv_stream_rw(src: torch.Tensor, read_bytes: int, dst: torch.Tensor, write_bytes: int):
+    """Plain streaming pass (calibration of the write path's attainable bandwidth):
+    reads ``read_bytes`` of ``src``, writes ``write_bytes`` of ``dst``."""
+    lib = load_library()
+    if read_bytes > src.numel() * src.element_size() or \
+            write_bytes > dst.numel() * dst.element_size():
+        raise ValueError("byte counts exceed the buffers")
+    _check(lib.int4kv_stream_rw(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes),
+                                _stream(src.device)))
 
 
 def int4_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,

@@ -489,6 +489,21 @@ int4kv_status_t int4_paged_attention_noalloc(const void* q, int64_t q_token_stri
   return ok();
 }
 
+int4kv_status_t int4kv_stream_rw(const void* src, int64_t read_bytes, void* dst,
+                                 int64_t write_bytes, void* stream) {
+  if (read_bytes < 0 || write_bytes < 0 || (read_bytes % 16) || (write_bytes % 16))
+    return fail(INT4KV_ERR_INVALID_ARG, "byte counts must be non-negative multiples of 16");
+  if ((read_bytes && (!src || !aligned16(src))) || (write_bytes && (!dst || !aligned16(dst))))
+    return fail(INT4KV_ERR_INVALID_ARG, "src and dst must be non-null and 16-byte aligned");
+  if (read_bytes > 0 && write_bytes == 0)
+    return fail(INT4KV_ERR_INVALID_ARG, "reads need at least one written unit to land in");
+  if (write_bytes == 0) return ok();
+  hipError_t e = int4kv::launch_stream_rw(src, read_bytes, dst, write_bytes,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "stream launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
                                  const void* value_new, int64_t value_token_stride,
                                  const int64_t* slot_mapping, const void* q,

@@ -11,8 +11,9 @@
 // here), so the bytes are reproducible bit for bit:
 //   * the signs are applied as bit flips of the 16-bit inputs (exact),
 //   * clamp-then-round equals round-then-clamp for the integer bounds 0 and
-//     15, and rounding to nearest-even is an fp32 add of 1.5 * 2^23, after
-//     which the code sits in the low 4 bits of the sum.
+//     15, and the rounding to nearest even is the float-to-byte conversion
+//     (v_cvt_pk_u8_f32, round-to-nearest-even mode), which also places the
+//     code in its byte.
 #pragma once
 
 #include "device_common.h"
@@ -111,8 +112,7 @@ __device__ __forceinline__ void cross_fmac8(int m, float (&x)[E], int e, float c
 // fl(stored * (sigma * inv)) = fl(y * inv)).
 //
 // Codes: t = fl(fl(y * inv) + zp) is clamped to [0, 15] and rounded to
-// nearest even by adding 1.5 * 2^23, after which the code sits in the low 4
-// bits of the sum.
+// nearest even by the float-to-byte conversion; two codes share a byte.
 template <int E, int LPR>
 __device__ __forceinline__ uint32_t encode_piece(float (&x)[E], int sub,
                                                  uint32_t (&packed)[E / 8]) {
@@ -167,22 +167,25 @@ __device__ __forceinline__ uint32_t encode_piece(float (&x)[E], int sub,
   const float inv = __fdiv_rn(1.0f, s_t);
   const float zpf = fminf(fmaxf(rintf(__fmul_rn(-mn, inv)), 0.0f), 15.0f);
   const float invs = LPR > 1 ? sigma * inv : inv;  // exact
-  constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
 
 #pragma unroll
   for (int q = 0; q < E / 8; ++q) {
-    uint32_t b[4];
+    // codes 8q .. 8q+7 as bytes [c1 c0 c3 c2] of w[0] and [c5 c4 c7 c6] of
+    // w[1] (each code < 16), so that (w << 12) | w holds c0 | c1 << 4 in byte
+    // 1 and c2 | c3 << 4 in byte 3
+    uint32_t w[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 8 * q + 2 * j;
-      const float t0 = enc_med3(__fadd_rn(__fmul_rn(x[e], invs), zpf), 0.0f, 15.0f);
-      const float t1 = enc_med3(__fadd_rn(__fmul_rn(x[e + 1], invs), zpf), 0.0f, 15.0f);
-      const float c0 = __fadd_rn(t0, kMagic), c1 = __fadd_rn(t1, kMagic);
-      b[j] = (as_uint(c1) << 4) | as_uint(c0);  // byte 0 = code_lo | code_hi << 4
+    for (int hf = 0; hf < 2; ++hf) {
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 8 * q + 4 * hf + j;
+        const float t = enc_med3(__fadd_rn(__fmul_rn(x[e], invs), zpf), 0.0f, 15.0f);
+        acc = __builtin_amdgcn_cvt_pk_u8_f32(t, j ^ 1, acc);  // round to nearest even
+      }
+      w[hf] = (acc << 12) | acc;
     }
-    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // [b0.0 b1.0 0 0]
-    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
-    packed[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);            // [lo.0 lo.1 hi.0 hi.1]
+    packed[q] = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u);  // bytes 1, 3 of w[0], w[1]
   }
   return as_uint(s_t) | (uint32_t)zpf;
 }

@@ -83,4 +83,8 @@ bool decode_lds_supported(const AttnArgs& a);
 hipError_t launch_decode_lds(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
 
+// plain streaming kernel: reads read_bytes, writes write_bytes (16-byte units)
+hipError_t launch_stream_rw(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                            hipStream_t stream);
+
 }  // namespace int4kv

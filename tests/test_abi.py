@@ -276,3 +276,17 @@ def test_int2_attention_rejects_invalid_host_arguments(kw, status):
 def test_int2_attention_empty_batch_is_a_no_op():
     assert _a2(S=0) == 0
     assert _a2(mq=0) == 0
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, 32, FAKE, 0), (FAKE, 24, FAKE, 16), (FAKE, 16, FAKE, 8), (FAKE + 4, 16, FAKE, 16),
+    (None, 16, FAKE, 16), (FAKE, 16, None, 16), (FAKE, -16, FAKE, 16),
+])
+def test_stream_rw_rejects_invalid_host_arguments(args):
+    src, nr, dst, nw = args
+    assert ik.load_library().int4kv_stream_rw(src, nr, dst, nw, None) == 1
+    assert ik.int4kv_last_error() != ""
+
+
+def test_stream_rw_empty_is_a_no_op():
+    assert ik.load_library().int4kv_stream_rw(None, 0, None, 0, None) == 0

@@ -46,7 +46,7 @@ def test_write_page_grid_bit_exact(oracle_mod, T, hkv, d, dtype):
 @pytest.mark.parametrize("T", [4000, 4100])
 def test_write_both_lane_layouts(oracle_mod, T, d):
     """8 KV heads: 4000 tokens (64000 rows) take the 16-elements-per-lane
-    layout, 4100 tokens (65600 rows) the 64-elements-per-lane one; both bit
+    layout, 4100 tokens (65600 rows) the 32-elements-per-lane one; both bit
     for bit over the whole cache."""
     header(f"write lane layouts T={T} d={d}")
     random.seed(T + d)
@@ -88,6 +88,29 @@ def test_write_degenerate_rows(oracle_mod, d):
         T = xx.shape[0]
         slots = torch.arange(T, dtype=torch.int64) * 3
         got, ref = _write_both(oracle_mod, xx, -xx, slots, (3 * T) // 16 + 1, 1, d, wl.rht_signs(d))
+        assert np.array_equal(got, ref), dtype
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_write_degenerate_rows_bulk_layout(oracle_mod, d):
+    """The degenerate rows above (plus exact half-integer grids) repeated over
+    4100 tokens x 8 heads, so that they take the bulk lane layout."""
+    header(f"write degenerate rows, bulk layout d={d}")
+    g = torch.Generator().manual_seed(d)
+    base = [torch.zeros(d), torch.full((d,), 3.0), torch.full((d,), -0.5),
+            torch.nn.functional.one_hot(torch.tensor(0), d).float() * 7,
+            torch.arange(d).float() / 8, torch.randn(d, generator=g) * 1e4,
+            torch.randn(d, generator=g) * 1e-5, torch.round(torch.randn(d, generator=g) * 4) / 2,
+            torch.full((d,), 6e-8), torch.round(torch.randn(d, generator=g) * 8) / 4]
+    T, hkv = 4100, 8
+    idx = torch.randint(0, len(base), (T, hkv), generator=g)
+    rows = torch.stack(base)[idx] * torch.where(torch.rand(T, hkv, 1, generator=g) < 0.5, -1.0, 1.0)
+    for dtype in (torch.float16, torch.bfloat16):
+        xx = rows.to(dtype)
+        nb = (T + 15) // 16 + 2
+        slots = torch.randperm(nb * 16, generator=g)[:T].to(torch.int64)
+        got, ref = _write_both(oracle_mod, xx, xx.flip(-1).contiguous(), slots, nb, hkv, d,
+                               wl.rht_signs(d))
         assert np.array_equal(got, ref), dtype
 
 
@@ -210,3 +233,20 @@ def test_decode_step_skips_slot_past_the_cache(oracle_mod):
     # sequence 1's new token was stored: its slot's rows changed
     s1 = int(nslots[1])
     assert not torch.equal(big[s1 // 16, :, s1 % 16], before[s1 // 16, :, s1 % 16])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nr,nw", [(4 * 1000 + 3, 1000), (77, 300), (0, 64), (16 * 1024 * 1024 + 5, 262144)])
+def test_stream_rw_definition(nr, nw):
+    """The write-bandwidth comparator: written unit w is the XOR of the read
+    units w, w + nw, ... below nr (16-byte units), checked on the host."""
+    g = torch.Generator().manual_seed(nr * 7 + nw)
+    src = torch.randint(0, 2**31 - 1, (nr * 4 + 4,), dtype=torch.int32, generator=g)
+    dst = torch.full((nw * 4,), -1, dtype=torch.int32, device="cuda")
+    ik.int4kv_stream_rw(src.cuda(), nr * 16, dst, nw * 16)
+    units = src[: nr * 4].view(nr, 4)
+    want = torch.zeros(nw, 4, dtype=torch.int32)
+    for j in range((nr + nw - 1) // nw if nr else 0):
+        part = units[j * nw: (j + 1) * nw]
+        want[: part.shape[0]] ^= part
+    assert torch.equal(dst.cpu().view(nw, 4), want)
