@@ -16,9 +16,11 @@ its GPU time, and HIP-graph replays of the same calls (`--graph`, checked bit
 for bit against plain calls) measured a few microseconds slower per step.
 Before the warm-up steps, about 0.3 s of untimed steps bring the GPU to its
 steady clock and address-translation state (the first tens of steps on a
-fresh process run up to 15% slower); the JSON line reports how many.  Every
-timed step and attention call sits between two HIP events on the launch
-stream, and the line carries their first five, median, mean and last five.
+fresh process run up to 15% slower); the JSON line reports how many.  The
+timed steps run back to back (an event recorded between two calls is a
+queue packet of its own and costs each call 2-3 us); a second pass of the
+same steps, and of the attention calls, with an event after each call gives
+the per-call first five, median, mean and last five.
 Prints one JSON line: decode
 effective KV GB/s (packed K+V bytes of every key attended, once per KV head,
 over the step time), the bulk cache-write rate (tokens/s, from a timed
@@ -249,6 +251,24 @@ def timed_calls(run, nbufs: int, n: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, [ev[i].elapsed_time(ev[i + 1]) for i in range(n - 1)]
+
+
+def timed_block(run, nbufs: int, n: int):
+    """n calls with nothing between them, bracketed by synchronisation: the
+    wall seconds, and the milliseconds between two HIP events recorded on the
+    launch stream right before the first call and right after the last one.
+    (An event recorded between calls is a packet of its own in the queue and
+    costs the calls 2-3 us each, so the per-call statistics come from a
+    separate pass of the same calls.)"""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(n):
+        run[i % nbufs]()
+    e1.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1)
 
 
 def call_stats(ms):
@@ -715,15 +735,18 @@ def main():
     for i in range(args.warmup):
         run[i % nbufs]()
     torch.cuda.synchronize()
-    wall, step_ms = timed_calls(run, nbufs, args.steps)
+    wall, step_ev_ms = timed_block(run, nbufs, args.steps)
     ms_per_step = wall * 1e3 / args.steps
+    # per-step statistics: the same steps again, an event after each
+    _, step_ms = timed_calls(run, nbufs, args.steps)
 
     # the attention call alone (decode + segment reduction), warmed up the same
-    # way; HIP events on the launch stream around each call
+    # way; HIP events on the launch stream before the first and after the last
     for i in range(args.warmup):
         run_attn[i % nbufs]()
-    attn_wall, attn_ms = timed_calls(run_attn, nbufs, args.steps)
-    attn_s = sum(attn_ms) / len(attn_ms) / 1e3 if attn_ms else attn_wall / args.steps
+    attn_wall, attn_ev_ms = timed_block(run_attn, nbufs, args.steps)
+    attn_s = attn_ev_ms / 1e3 / args.steps
+    _, attn_ms = timed_calls(run_attn, nbufs, args.steps)
 
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_s * 1e6:.2f} us")
     wr_tps, wr_t, wr_T = measure_bulk_write(bufs[0])
@@ -747,8 +770,13 @@ def main():
                    "global_batch": 4, "seq_len": 131072, "parallelism": "none (1 GPU)",
                    "launch": "hip graph replay" if args.graph else "plain calls",
                    "settle": settled},
+        "timed_region_event_us_per_step": round(step_ev_ms * 1e3 / args.steps, 2),
         "step_events": call_stats(step_ms) if step_ms else None,
         "attention_call_events": call_stats(attn_ms) if attn_ms else None,
+        "per_call_events_note": "step_events / attention_call_events: a second pass of the same "
+                                "K calls with an event after each (those events cost the calls "
+                                "2-3 us each); ms_per_step and roofline come from passes with "
+                                "events only before the first and after the last call",
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "num_segments_library_choice": ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads,
                                                                      w.max_seqlen_k),
@@ -762,8 +790,9 @@ def main():
                            "read_plus_write_GB_per_s": round((st_r + st_w) / st_t / 1e9, 1),
                            "write_time_over_stream_time": round(wr_t / st_t, 4)}},
         "roofline": {"kernel": "decode_lds_kernel + reduce_wave_kernel (one int4_paged_attention call)",
-                     "timing": "mean of per-call HIP event times over the timed attention calls "
-                               "2..K (decode kernel, segment reduction, the dispatch gaps)",
+                     "timing": "HIP events on the launch stream before the first and after the "
+                               "last of K back-to-back attention calls, / K (decode kernel, "
+                               "segment reduction, the dispatch gaps)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kv_bytes,
