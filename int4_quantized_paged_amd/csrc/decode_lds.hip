@@ -212,12 +212,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   // ---- fused decode step: the new token of sequence b (its last key, at
   // position L - 1) is encoded exactly as the cache write does and stored by
   // the workgroup whose segment holds that key's block, before any copy of
-  // the block is issued.  The writing waves' stores complete (vmcnt 0) before
-  // a barrier that precedes that copy: the barrier right here when the
+  // the block is issued.  The writing waves' stores complete before a barrier
+  // that precedes that copy: the barrier right here (vmcnt 0) when the
   // block's tile is among the first S - 1 (copied before the loop), else the
-  // barrier at which tile 0 has landed.  The block is read only by this
-  // workgroup, through L2.
-  bool store_pending = false;  // this wave stored rows whose completion is still to be awaited
+  // wait for tile 0 ahead of the loop's first barrier, as vector memory
+  // operations retire in issue order and the stores precede tile 0's
+  // copies.  The block is read only by this workgroup, through L2.
   if (!Q8 && !Q2 && slot_new != nullptr) {  // (the INT8 and INT2 modes have no fused step)
     const int64_t slot = slot_new[b];
     // (slots outside [0, num_slots) are not stored, as in the cache write)
@@ -253,9 +253,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       if (ntile <= S - 1) {
         wait_vmem<0>();  // the stores have reached L2
         __syncthreads();
-      } else {
-        store_pending = wave * WRPW < 2 * HPW;
-      }
+      }  // else the wait for tile 0 before the loop's first barrier covers them
     }
   }
   if (qlen <= 0) return;  // uniform over the workgroup
@@ -832,7 +830,6 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
   TileWords wA, wB;
   if (ntile > 0) {
     wait_tiles(std::integral_constant<int, S - 2>());  // tile 0
-    if (store_pending) wait_vmem<0>();  // this wave's stores of the new token, too
     __syncthreads();
     issue(0, S - 1);  // the staged query has been read by every wave
     load_ids(0, S);
