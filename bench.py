@@ -14,9 +14,10 @@ in the 256 MB Infinity Cache.
 Steps are plain library calls: the host enqueues a step in about a fifth of
 its GPU time, and HIP-graph replays of the same calls (`--graph`, checked bit
 for bit against plain calls) measured a few microseconds slower per step.
-Before the warm-up steps, about 0.3 s of untimed steps bring the GPU to its
-steady clock and address-translation state (the first tens of steps on a
-fresh process run up to 15% slower); the JSON line reports how many.  The
+Before the warm-up steps, about 1 s of untimed steps bring the GPU to its
+steady clock and address-translation state (the first few hundred steps on
+a fresh process run up to 15% slower, and the launch time eases by another
+2-3% over the next half second); the JSON line reports how many.  The
 timed steps run back to back (an event recorded between two calls is a
 queue packet of its own and costs each call 2-3 us); a second pass of the
 same steps, and of the attention calls, with an event after each call gives
@@ -217,10 +218,12 @@ def _median_event_us(fn, reps, rounds=5):
     return ts[len(ts) // 2]
 
 
-def settle(run, nbufs: int, seconds: float = 0.3, max_steps: int = 5000) -> dict:
+def settle(run, nbufs: int, seconds: float = 1.0, max_steps: int = 20000) -> dict:
     """Untimed steps until the GPU reaches its steady clock and address-
-    translation state (about 0.3 s of the same work): the first tens of steps
-    on a fresh process run up to 15% slower.  Done before the warm-up steps."""
+    translation state (about 1 s of the same work): on a fresh process the
+    first few hundred decode launches run up to 15% slower, and the launch
+    time keeps easing by 2-3% over the next half second.  Done before the
+    warm-up steps."""
     t0 = time.perf_counter()
     n = 0
     while n < max_steps:
