@@ -7,9 +7,11 @@
  * enqueuing anything when they are invalid; on success the work is enqueued on
  * `stream` and the call returns at once (no synchronisation).  The library
  * allocates no device memory and keeps no global mutable state apart from a
- * thread-local error string and a lock-protected record of the (kernel,
- * device) pairs whose LDS limit it has raised, so it is re-entrant; buffers
- * are owned by the caller.  Slot numbers are bounds-checked on the device:
+ * thread-local error string, a lock-protected record of the (kernel, device)
+ * pairs whose LDS limit it has raised, and the fixed per-device array that
+ * int4_paged_attention_noalloc keeps its split-K partials in (with the
+ * looked-up address of each device's copy); every other entry point is
+ * re-entrant, and its buffers are owned by the caller.  Slot numbers are bounds-checked on the device:
  * every write entry point stores a token only when its slot lies in
  * [0, num_blocks * block_size) and skips it otherwise (negative slots are the
  * pages' skip marker; larger ones would address memory past the cache).  The
