@@ -202,6 +202,29 @@ def measure_stream_ceiling(read_bytes: int, write_bytes: int, reps: int = 5):
     return t, read_bytes, write_bytes
 
 
+def gather_only(bufs, n: int):
+    """The attention call's block gather on its own (int4kv_stream_blocks): the
+    same blocks in the same order over the same workgroups (one per sequence
+    and segment) and the same LDS ring, nothing computed; n back-to-back calls
+    alternating the caches, HIP events around them.  Microseconds per call:
+    the rate the decode kernel's access pattern attains by itself."""
+    runs = []
+    for b in bufs:
+        w = b["w"]
+        nblk = {(L + 15) // 16 for L in w.kv_lens}
+        assert len(nblk) == 1, "one block count for every sequence"
+        nblk = nblk.pop()
+        assert nblk % NUM_SEGMENTS == 0 and (nblk // NUM_SEGMENTS) % 2 == 0
+        ids = b["bt"][:, :nblk].contiguous().view(-1)
+        block_bytes = 2 * 16 * w.num_kv_heads * (w.head_size // 2 + 4)
+        runs.append(lambda b=b, ids=ids, bb=block_bytes, nwg=w.num_seqs * NUM_SEGMENTS:
+                    ik.int4kv_stream_blocks(b["cache"], bb, ids, nwg))
+    for i in range(2 * len(runs)):
+        runs[i % len(runs)]()
+    _, ms = timed_block(runs, len(runs), n)
+    return ms * 1e3 / n
+
+
 def _median_event_us(fn, reps, rounds=5):
     """Per-call time of `reps` back-to-back calls between two HIP events on the
     launch stream (as the headline attention figure), median of `rounds`."""
@@ -751,7 +774,9 @@ def main():
     attn_s = attn_ev_ms / 1e3 / args.steps
     _, attn_ms = timed_calls(run_attn, nbufs, args.steps)
 
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_s * 1e6:.2f} us")
+    gather_us = gather_only(bufs, args.steps)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_s * 1e6:.2f} us; "
+        f"its gather alone {gather_us:.2f} us")
     wr_tps, wr_t, wr_T = measure_bulk_write(bufs[0])
     bk, bv, bslots = bufs[0]["bulk"]
     wr_read = bk.numel() * bk.element_size() + bv.numel() * bv.element_size() + bslots.numel() * 8
@@ -799,7 +824,15 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kv_bytes,
-                     "avg_launch_us": round(attn_s * 1e6, 2)},
+                     "avg_launch_us": round(attn_s * 1e6, 2),
+                     "gather_only": {
+                         "call": "int4kv_stream_blocks: the attention call's block gather alone "
+                                 "(same blocks, order, workgroups and LDS ring, nothing "
+                                 "computed), timed like the attention call",
+                         "us": round(gather_us, 2),
+                         "GB_per_s": round(kv_bytes / gather_us / 1e3, 1),
+                         "frac_of_peak": round(kv_bytes / gather_us / 1e3 / HBM_PEAK_GBS, 4),
+                         "attention_call_over_gather": round(attn_s * 1e6 / gather_us, 4)}},
     }
     if not args.no_other_rows:
         res["other_rows"] = other_rows(dev)

@@ -179,6 +179,28 @@ int4kv_status_t int4kv_stream_rw(const void* src, int64_t read_bytes, void* dst,
                                  int64_t write_bytes, void* stream);
 
 /*
+ * int4kv_stream_blocks: the decode path's block gather on its own, for
+ * measuring the rate its access pattern attains: cache blocks listed in
+ * `block_ids` (device, int32, num_ids entries) are copied HBM -> LDS with the
+ * same instructions and ring discipline as the decode kernel (two blocks per
+ * tile, 1 KiB units over 8 waves, a 4-stage ring, a barrier per tile) and
+ * nothing is computed or written.  Not a step of the method.  Workgroup g of
+ * num_workgroups copies ids [2 g T, 2 (g + 1) T), T = num_ids / (2 *
+ * num_workgroups), in order (as a decode workgroup copies its segment's
+ * blocks; the decode call's own gather is its block table's rows,
+ * concatenated, with one workgroup per segment of each sequence).  Block b
+ * occupies bytes [b * block_bytes, (b + 1) * block_bytes) of `cache` (16-byte
+ * aligned); block_bytes must be a multiple of 1024 in [1024, 20480] (an INT4
+ * block of 8 KV heads: 2 * 16 * 8 * (head_size / 2 + 4) bytes), num_ids a
+ * positive multiple of 2 * num_workgroups (INT4KV_ERR_INVALID_ARG otherwise;
+ * num_ids 0 is a no-op).  Ids are the caller's contract: each must lie in
+ * [0, number of blocks in the cache).  Asynchronous on `stream`.
+ */
+int4kv_status_t int4kv_stream_blocks(const uint8_t* cache, int64_t block_bytes,
+                                     const int32_t* block_ids, int64_t num_ids,
+                                     int32_t num_workgroups, void* stream);
+
+/*
  * int4_paged_attention_noalloc: int4_paged_attention for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same arguments minus the three

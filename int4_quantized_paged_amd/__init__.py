@@ -23,7 +23,7 @@ __all__ = [
     "int4kv_decode_num_segments", "NOALLOC_SCRATCH_BYTES",
     "int4kv_cache_bytes", "int4kv_status_string",
     "int4kv_last_error", "Int4KVError", "cache_shape", "empty_cache", "segment_buffers",
-    "library_path", "load_library",
+    "library_path", "load_library", "int4kv_stream_rw", "int4kv_stream_blocks",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +73,8 @@ def load_library():
     lib.int4_paged_attention_noalloc.restype = ctypes.c_int
     lib.int4kv_stream_rw.argtypes = [P, i64, P, i64, P]
     lib.int4kv_stream_rw.restype = ctypes.c_int
+    lib.int4kv_stream_blocks.argtypes = [P, i64, P, i64, i32, P]
+    lib.int4kv_stream_blocks.restype = ctypes.c_int
     lib.int2_paged_attention.argtypes = lib.int4_paged_attention.argtypes
     lib.int2_paged_attention.restype = ctypes.c_int
     lib.int4_decode_step.argtypes = [P, i64, P, i64, P, P, i64, P, ctypes.c_int, P, i32, i32, i32,
@@ -324,6 +326,22 @@ def int4kv_stream_rw(src: torch.Tensor, read_bytes: int, dst: torch.Tensor, writ
         raise ValueError("byte counts exceed the buffers")
     _check(lib.int4kv_stream_rw(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes),
                                 _stream(src.device)))
+
+
+def int4kv_stream_blocks(cache: torch.Tensor, block_bytes: int, block_ids: torch.Tensor,
+                         num_workgroups: int):
+    """The decode path's block gather on its own (calibration): copies the cache
+    blocks listed in ``block_ids`` (int32, contiguous, on the cache's device)
+    into LDS as the decode kernel does, computing and writing nothing.  Every
+    id must lie in [0, cache bytes / block_bytes) (not checked: reading the
+    ids back would synchronise the stream)."""
+    lib = load_library()
+    if block_ids.dtype != torch.int32 or not block_ids.is_contiguous() or \
+            block_ids.device != cache.device:
+        raise ValueError("block_ids must be a contiguous int32 tensor on the cache's device")
+    _check(lib.int4kv_stream_blocks(_ptr(cache), int(block_bytes), _ptr(block_ids),
+                                    int(block_ids.numel()), int(num_workgroups),
+                                    _stream(cache.device)))
 
 
 def int4_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,

@@ -504,6 +504,29 @@ int4kv_status_t int4kv_stream_rw(const void* src, int64_t read_bytes, void* dst,
   return ok();
 }
 
+int4kv_status_t int4kv_stream_blocks(const uint8_t* cache, int64_t block_bytes,
+                                     const int32_t* block_ids, int64_t num_ids,
+                                     int32_t num_workgroups, void* stream) {
+  if (num_ids < 0 || num_workgroups < 1)
+    return fail(INT4KV_ERR_INVALID_ARG, "num_ids (%lld) must be >= 0 and num_workgroups (%d) >= 1",
+                (long long)num_ids, num_workgroups);
+  if (block_bytes < 1024 || block_bytes > 20480 || block_bytes % 1024)
+    return fail(INT4KV_ERR_INVALID_ARG,
+                "block_bytes %lld must be a multiple of 1024 in [1024, 20480]",
+                (long long)block_bytes);
+  if (num_ids == 0) return ok();
+  if (num_ids % (2 * (int64_t)num_workgroups))
+    return fail(INT4KV_ERR_INVALID_ARG,
+                "num_ids %lld must be a multiple of 2 * num_workgroups (%d)",
+                (long long)num_ids, 2 * num_workgroups);
+  if (!cache || !aligned16(cache) || !block_ids)
+    return fail(INT4KV_ERR_INVALID_ARG, "cache (16-byte aligned) and block_ids must be non-null");
+  hipError_t e = int4kv::launch_stream_blocks(cache, block_bytes, block_ids, num_ids,
+                                              num_workgroups, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(INT4KV_ERR_LAUNCH, "stream launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
                                  const void* value_new, int64_t value_token_stride,
                                  const int64_t* slot_mapping, const void* q,

@@ -87,4 +87,10 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_stream_rw(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
                             hipStream_t stream);
 
+// The decode path's block gather into LDS without its arithmetic (calibration):
+// block_bytes a multiple of 1024 in [1024, 20480], num_ids a multiple of
+// 2 * num_workgroups (checked by the caller).
+hipError_t launch_stream_blocks(const uint8_t* cache, int64_t block_bytes, const int32_t* ids,
+                                int64_t num_ids, int32_t num_workgroups, hipStream_t stream);
+
 }  // namespace int4kv

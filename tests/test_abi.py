@@ -290,3 +290,24 @@ def test_stream_rw_rejects_invalid_host_arguments(args):
 
 def test_stream_rw_empty_is_a_no_op():
     assert ik.load_library().int4kv_stream_rw(None, 0, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, 17408, FAKE, 64, 0),          # no workgroups
+    (FAKE, 17408, FAKE, -2, 1),          # negative count
+    (FAKE, 1000, FAKE, 64, 4),           # block size not a multiple of 1024
+    (FAKE, 0, FAKE, 64, 4),              # empty blocks
+    (FAKE, 21504, FAKE, 64, 4),          # blocks past the ring's stage size
+    (FAKE, 17408, FAKE, 66, 4),          # not whole tiles per workgroup
+    (FAKE + 4, 17408, FAKE, 64, 4),      # misaligned cache
+    (None, 17408, FAKE, 64, 4),          # null cache
+    (FAKE, 17408, None, 64, 4),          # null ids
+])
+def test_stream_blocks_rejects_invalid_host_arguments(args):
+    cache, bb, ids, n, wg = args
+    assert ik.load_library().int4kv_stream_blocks(cache, bb, ids, n, wg, None) == 1
+    assert ik.int4kv_last_error() != ""
+
+
+def test_stream_blocks_empty_is_a_no_op():
+    assert ik.load_library().int4kv_stream_blocks(None, 17408, None, 0, 4, None) == 0

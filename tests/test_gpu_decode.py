@@ -173,3 +173,22 @@ def test_decode_other_kv_head_counts(oracle_mod, hq, hkv, d):
     (3, 12)."""
     w = wl.custom([(1, 45), (1, 300), (1, 16)], hq, hkv, d, seed=hq + hkv + d, write_all=True)
     _run_both(oracle_mod, w, [1, 4])
+
+
+@pytest.mark.parametrize("hkv,d,nwg", [(8, 128, 4), (8, 64, 2), (16, 64, 1)])
+def test_stream_blocks_copies_and_writes_nothing(hkv, d, nwg):
+    """The decode gather's calibration pass (int4kv_stream_blocks) over a real
+    block list: it completes, and leaves the cache and every other buffer as
+    they were (it only copies into LDS)."""
+    header(f"stream_blocks hkv={hkv} d={d} workgroups={nwg}")
+    nb = 96
+    block_bytes = 2 * 16 * hkv * (d // 2 + 4)
+    assert block_bytes % 1024 == 0
+    g = torch.Generator().manual_seed(hkv * d + nwg)
+    cache = torch.randint(0, 256, (nb * block_bytes,), dtype=torch.uint8, generator=g).cuda()
+    before = cache.clone()
+    ids = torch.randperm(nb, generator=g)[: 2 * nwg * 9].to(torch.int32).cuda()
+    import int4_quantized_paged_amd as ik
+    ik.int4kv_stream_blocks(cache, block_bytes, ids, nwg)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, before)
