@@ -95,3 +95,18 @@ def test_chunked_prefill_full_size_sampled(oracle_mod, d):
                           w.value[kidx], w.query[cuq[b] + i:cuq[b] + i + 1], w.signs)
         ref = oracle_attention(oracle_mod, sub, oracle_cache(oracle_mod, sub, "all"))
         assert_attention_close(out[cuq[b] + i:cuq[b] + i + 1], ref, f"seq {b} row {i}")
+
+
+def test_prefill_many_groups_long_context(oracle_mod):
+    """The workgroups' launch ranking beyond one pass of its 512 threads: 163
+    sequences (652 (sequence, query tile) groups at 32 q / 8 KV heads, many of
+    them empty), and contexts past 1,022 key tiles, where the ranking scales
+    the tile counts into its buckets; every output row checked."""
+    g = torch.Generator().manual_seed(77)
+    lens = []
+    for _ in range(160):
+        q = int(torch.randint(1, 101, (1,), generator=g))
+        lens.append((q, q + int(torch.randint(0, 201, (1,), generator=g))))
+    lens += [(2, 40000), (33, 36000), (128, 128)]
+    w = wl.custom(lens, 32, 8, 128, dtype=torch.bfloat16, seed=78, write_all=True)
+    _run(oracle_mod, w)
