@@ -145,6 +145,7 @@ struct PGeo {
 // Called by all 512 threads at the start of the kernel; uses the first
 // (kRankBuckets + 516) ints of LDS and ends with a barrier.
 constexpr int kRankBuckets = 1024;
+constexpr int64_t kPrefillCUs = 256;  // MI355X: one prefill workgroup per CU at a time
 
 template <int TQ>
 __device__ int ranked_group(int rank, int num_seqs, int tiles_per_seq,
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ seqused_k,
     const int32_t* __restrict__ block_table, int32_t bt_stride, float scale_log2,
     const float* __restrict__ signs, int32_t num_seqs, int32_t tiles_per_seq, int32_t window,
-    float cap2, float inv_cap2, int32_t max_tiles) {
+    float cap2, float inv_cap2, int32_t max_tiles, int32_t rank_groups) {
   using PG = PGeo<D, G, Q8, Q2>;
   constexpr int R = PG::R, RW = PG::RW, DW = PG::DW, NIB = PG::NIB;
   constexpr int NCH = D / 32;   // f16 MFMA k-chunks of the score
@@ -259,8 +260,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int h = rr % num_kv_heads;
   const int rank = (rr / num_kv_heads) * 8 + (id & 7);
   if (rank >= num_seqs * tiles_per_seq) return;  // uniform over the workgroup
-  const int grp = ranked_group<TQ>(rank, num_seqs, tiles_per_seq, cu_seqlens_q, seqused_k,
-                                   window, max_tiles, reinterpret_cast<int*>(smem));
+  // (a launch whose workgroups all fit on the CUs at once needs no order)
+  const int grp = rank_groups ? ranked_group<TQ>(rank, num_seqs, tiles_per_seq, cu_seqlens_q,
+                                                 seqused_k, window, max_tiles,
+                                                 reinterpret_cast<int*>(smem))
+                              : rank;
   if (grp < 0) return;  // uniform: past the last non-empty group
   const int b = grp / tiles_per_seq;
   const int qt = grp - b * tiles_per_seq;
@@ -864,7 +868,7 @@ hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t stream) {
                      reinterpret_cast<uint16_t*>(a.out), a.cache, a.num_kv_heads, a.num_q_heads,
                      a.cu_seqlens_q, a.seqused_k, a.block_table, a.bt_stride, scale_log2, a.signs,
                      a.num_seqs, tiles_per_seq, a.window, cap2, cap2 > 0.f ? 1.0f / cap2 : 0.f,
-                     (a.max_seqlen_k + 31) / 32);
+                     (a.max_seqlen_k + 31) / 32, nwg > kPrefillCUs ? 1 : 0);
   return hipGetLastError();
 }
 
