@@ -454,6 +454,51 @@ def other_rows(dev):
         "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
     del w, cache, gstep
 
+    # serving stand-in: 100 prompts of 512 tokens written (timed), then one
+    # decode step per sequence at a context in [512, 640] (int4_decode_step)
+    w = wl.serving_standin(device=dev)
+    cache = ik.empty_cache(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)
+    signs = w.signs.to(dev)
+    off = w.token_offsets()
+    P = 512
+    pos = torch.arange(P, dtype=torch.int64)
+    pidx = torch.cat([pos + off[b] for b in range(w.num_seqs)]).to(dev)
+    pslots = torch.cat([w.slots_of(b, pos) for b in range(w.num_seqs)]).to(dev)
+    kp, vp = w.key[pidx].contiguous(), w.value[pidx].contiguous()
+    pwrite = lambda: ik.int4_kv_write(kp, vp, pslots, cache, signs)  # noqa: E731
+    for _ in range(3):
+        pwrite()
+    pw_us = _median_event_us(pwrite, 10)
+    mid = [(torch.arange(P, L - 1, dtype=torch.int64), b) for b, L in enumerate(w.kv_lens) if L - 1 > P]
+    midx = torch.cat([m + off[b] for m, b in mid]).to(dev)
+    mslots = torch.cat([w.slots_of(b, m) for m, b in mid]).to(dev)
+    ik.int4_kv_write(w.key[midx], w.value[midx], mslots, cache, signs)
+    idx_n, slots_n = w.token_set("new")
+    kn, vn, sn = w.key[idx_n.to(dev)].contiguous(), w.value[idx_n.to(dev)].contiguous(), slots_n.to(dev)
+    ns = ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads, w.max_seqlen_k)
+    segs = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns, w.head_size, dev) if ns > 1 else \
+        (None, None, None)
+    cu, su, bt = w.cu_seqlens_q().to(dev), w.seqused_k().to(dev), w.block_table.to(dev)
+    out = torch.empty_like(w.query)
+    sstep = lambda: ik.int4_decode_step(kn, vn, sn, w.query, cache, cu, su, 1, w.max_seqlen_k,  # noqa: E731
+                                        bt, w.softmax_scale, signs, out=out, num_segments=ns,
+                                        segm_output=segs[0], segm_max=segs[1],
+                                        segm_expsum=segs[2])
+    for _ in range(20):
+        sstep()
+    us = _graph_us(sstep, 20)
+    rows["serving_standin"] = {
+        "workload": f"{w.num_seqs} seqs: {w.num_seqs * P} prompt tokens written, then one decode "
+                    f"step each at contexts {min(w.kv_lens)}..{max(w.kv_lens)} "
+                    f"({sum(w.kv_lens)} keys), 32 q / 8 KV heads, d 128",
+        "prompt_write_us": round(pw_us, 2),
+        "prompt_write_tokens_per_s": round(w.num_seqs * P / pw_us * 1e6, 1),
+        "num_segments": ns, "decode_step_us": round(us, 2),
+        "timing": "prompt write: 10 back-to-back calls between events, per call; decode step: "
+                  "20 steps replayed from one HIP graph, per step",
+        "kv_GBps": round(w.kv_bytes_attended() / us / 1e3, 1)}
+    del w, cache, sstep, kp, vp
+
     w = wl.llama3_8b_decode(device=dev)
     # its bulk cache fill (262144 tokens) and a decode step's write (64 tokens)
     cache = ik.empty_cache(w.num_blocks, w.num_kv_heads, w.head_size, device=dev)

@@ -60,14 +60,21 @@ int4kv_status_t ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Split-count heuristic of the decode path: enough segments that the grid has
-// a workgroup per CU (256 on MI355X), but no segment shorter than 2 tiles of
-// 32 keys.  Large batches are limited by the first rule (the long-context and
-// Llama-3-shaped decodes get 64 and 4 segments, the fastest measured); short
-// batches with few workgroups by the second: 8 sequences of up to 909 keys
-// took 36.5 us at 1 segment, 15 us at 8 and 14 us at 16.
-constexpr int64_t kDecodeTargetWorkgroups = 256;
+// Split-count heuristic of the decode path.  A decode workgroup holds a whole
+// CU (256 on MI355X), so a grid of W workgroups runs in ceil(W / 256) rounds,
+// each as long as one workgroup: a fixed start (the query prologue and the
+// ring's first copies, about 3 tiles' time) plus its segment's tiles; a split
+// adds the segment reduction (about 3 tiles' time).  The count minimises
+//   rounds(ns) * (3 + tiles / ns) + (ns > 1 ? 3 : 0)
+// over ns in [1, tiles / 2] (no segment shorter than 2 tiles of 32 keys),
+// ties to the smaller count.  It picks the fastest measured counts: 64 for
+// the long-context decode, 4 for the Llama-3-shaped one (2 with the INT8
+// kernel's 4-head workgroups), 16 for 8 sequences of up to 1024 keys (36.5 us
+// at 1 segment, 15 at 8, 14 at 16), and 2 rather than 3 for 100 sequences of
+// 512-640 keys (3 segments make 300 workgroups: a second round of 44).
+constexpr int64_t kDecodeCUs = 256;
 constexpr int64_t kDecodeMinTilesPerSegment = 2;
+constexpr double kDecodeStartTiles = 3.0, kDecodeReduceTiles = 3.0;
 
 // the split-count rule for workgroups of up to `hpw_cap` KV heads (8 for the
 // INT4 decode kernel, 4 for the INT8 one)
@@ -82,13 +89,21 @@ int32_t decode_num_segments(int32_t num_seqs, int32_t num_kv_heads, int32_t max_
   else if (hkv % hpw_cap != 0)
     while (hkv % hpw) hpw >>= 1;
   const int64_t wgs = (int64_t)num_seqs * (hkv / hpw);  // workgroups per segment index
-  const int64_t fill = (kDecodeTargetWorkgroups + wgs - 1) / wgs;
   const int64_t tiles = ((int64_t)max_seqlen_k + 31) / 32;  // 32-key tiles of the longest sequence
-  const int64_t cap = tiles / kDecodeMinTilesPerSegment;
-  int64_t ns = fill < cap ? fill : cap;
-  if (ns < 1) ns = 1;
-  if (ns > 256) ns = 256;
-  return (int32_t)ns;
+  int64_t cap = tiles / kDecodeMinTilesPerSegment;
+  if (cap > 256) cap = 256;
+  int64_t best = 1;
+  double best_cost = 0.0;
+  for (int64_t ns = 1; ns <= (cap > 1 ? cap : 1); ++ns) {
+    const double rounds = (double)((ns * wgs + kDecodeCUs - 1) / kDecodeCUs);
+    const double cost = rounds * (kDecodeStartTiles + (double)tiles / (double)ns) +
+                        (ns > 1 ? kDecodeReduceTiles : 0.0);
+    if (ns == 1 || cost < best_cost) {
+      best = ns;
+      best_cost = cost;
+    }
+  }
+  return (int32_t)best;
 }
 
 int4kv_status_t check_common(const void* cache, int32_t num_blocks, int32_t block_size,

@@ -235,6 +235,28 @@ def long_context_decode(device="cpu", seed: int = 3, num_seqs: int = 4,
                     d, NB, [ctx] * S, [1] * S, [1] * S, bt, key, value, query, rht_signs(d))
 
 
+def serving_standin(device="cpu", seed: int = 5) -> Workload:
+    """Serving stand-in: 100 sequences whose 512-token prompts are written,
+    then one decode step each at a context uniform in [512, 640] (its last key
+    is the step's new token; the keys between the prompt and it are written
+    beforehand); 32 q / 8 KV heads, d 128, bf16 N(0,1), disjoint random
+    blocks."""
+    gc = torch.Generator().manual_seed(seed)
+    S, Hq, Hkv, d = 100, 32, 8, 128
+    kv_lens = torch.randint(512, 641, (S,), generator=gc).tolist()
+    nbl = [(L + BLOCK_SIZE - 1) // BLOCK_SIZE for L in kv_lens]
+    NB = sum(nbl)
+    bt = _disjoint_tables(nbl, NB, gc)
+    g = gc if str(device) == "cpu" else _gen(seed, device)
+    N = sum(kv_lens)
+    key = _normal((N, Hkv, d), g, torch.bfloat16, device)
+    value = _normal((N, Hkv, d), g, torch.bfloat16, device)
+    query = _normal((S, Hq, d), g, torch.bfloat16, device)
+    return Workload("serving stand-in 100x512 prompts, decode at 512..640 32q/8kv d128 bf16",
+                    torch.bfloat16, Hq, Hkv, d, NB, kv_lens, [1] * S, [1] * S, bt, key, value,
+                    query, rht_signs(d))
+
+
 def chunked_prefill(device="cpu", seed: int = 4, head_size: int = 128,
                     num_seqs: int = 32) -> Workload:
     """Chunked-prefill mixed batch: 32 sequences, query lengths

@@ -149,18 +149,31 @@ def test_decode_step_empty_batch_is_a_no_op():
 @pytest.mark.parametrize("S,hkv,L,ns", [
     (4, 8, 131072, 64),  # long-context decode: one workgroup per CU
     (64, 8, 4096, 4),    # Llama-3-8B-shaped decode: 256 workgroups
+    (100, 8, 640, 2),    # serving stand-in: 3 segments would need a second round of 44
     (1, 8, 40, 1),       # shorter than two minimum segments
-    (1, 8, 100, 2),      # capped by the 2-tile minimum segment
+    (1, 8, 100, 1),      # 4 tiles: a split saves less than the reduction costs
     (8, 8, 1024, 16),    # GQA decode: capped by the minimum segment
-    (32, 3, 5000, 3),    # register-path head count (one head per workgroup)
+    (32, 3, 5000, 8),    # register-path head count (one head per workgroup)
     (2, 16, 65536, 64),  # two workgroups per segment index
     (1, 1, 10 ** 7, 256),
 ])
 def test_decode_num_segments_heuristic(S, hkv, L, ns):
-    """Enough segments for one workgroup per CU, none shorter than 2 tiles of
-    32 keys, at most 256; the two large benchmark shapes get the split counts
-    that measured fastest (64 and 4)."""
+    """The count with the fewest rounds of workgroups times (start + tiles per
+    segment), plus the reduction for a split; none shorter than 2 tiles of 32
+    keys, at most 256.  The benchmark shapes get the split counts that
+    measured fastest (64, 4, 16 and 2)."""
     assert ik.int4kv_decode_num_segments(S, hkv, L) == ns
+
+
+def test_decode_num_segments_fills_one_round_when_it_pays():
+    """A split never makes a partial second round of workgroups for a batch
+    whose sequences are short (the start and the reduction outweigh the
+    shorter segments), and grows with the context once one round is full."""
+    for S in (40, 64, 100, 128, 200):
+        ns = ik.int4kv_decode_num_segments(S, 8, 640)
+        assert ns * S <= 256 or ns == 1, (S, ns)
+    grow = [ik.int4kv_decode_num_segments(4, 8, L) for L in (2048, 8192, 32768, 131072)]
+    assert grow == sorted(grow) and grow[-1] == 64
 
 
 def test_decode_num_segments_degenerate_inputs():
@@ -221,7 +234,7 @@ def test_int8_attention_empty_batch_is_a_no_op():
     (64, 8, 4096, 2),    # Llama-3-8B-shaped: 4-head workgroups, 128 per segment index
     (4, 8, 131072, 32),
     (8, 8, 1024, 16),
-    (1, 2, 100, 2),
+    (1, 2, 100, 1),
 ])
 def test_int8_decode_num_segments(S, hkv, L, ns):
     assert ik.int8kv_decode_num_segments(S, hkv, L) == ns
