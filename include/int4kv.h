@@ -274,8 +274,11 @@ int4kv_status_t int4_decode_step(const void* key_new, int64_t key_token_stride,
 /*
  * int4kv_decode_num_segments: the split-K segment count the library's decode
  * kernels run best with for a decode batch (max_seqlen_q == 1) of `num_seqs`
- * sequences whose longest has `max_seqlen_k` keys: enough segments for one
- * workgroup per CU of MI355X, none shorter than 64 keys.  Host only; never
+ * sequences whose longest has `max_seqlen_k` keys.  A decode workgroup holds
+ * a whole CU of MI355X (256), so a grid runs in rounds of 256 workgroups; the
+ * count minimises rounds x (a fixed start of about 3 key tiles + the tiles
+ * of one segment), plus about 3 tiles for the segment reduction when split,
+ * with no segment shorter than 64 keys (2 tiles of 32).  Host only; never
  * fails (returns >= 1).  The caller sizes the segment buffers of
  * int4_paged_attention / int4_decode_step with it and passes it as
  * num_segments.  (The pages' attention test sizes its segment buffers from a
