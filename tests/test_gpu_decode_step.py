@@ -109,3 +109,20 @@ def test_decode_step_prefill_batch_falls_back(oracle_mod):
     w = wl.custom([(1, 50), (5, 90), (1, 17)], 32, 8, 128, seed=13)
     header("decode step with a prefill row")
     _both(w, 1)
+
+
+def test_decode_step_serving_batch(oracle_mod):
+    """100 sequences of 514-640 keys at the library's split count (2): the
+    fused step against the two calls bit for bit, and 10 sampled sequences
+    against the oracle."""
+    w = wl.serving_standin()
+    ns = ik.int4kv_decode_num_segments(w.num_seqs, w.num_kv_heads, w.max_seqlen_k)
+    assert ns == 2
+    header(f"decode step serving batch NS={ns}")
+    out = _both(w, ns)
+    g = torch.Generator().manual_seed(12)
+    picks = torch.randperm(w.num_seqs, generator=g)[:10].tolist()
+    from tests.gpu_helpers import sub_workload
+    ws = sub_workload(w, picks)
+    ref = oracle_attention(oracle_mod, ws, oracle_cache(oracle_mod, ws, "all"))
+    assert_attention_close(out[picks], ref, "serving batch, sampled sequences")
