@@ -110,3 +110,24 @@ def test_prefill_many_groups_long_context(oracle_mod):
     lens += [(2, 40000), (33, 36000), (128, 128)]
     w = wl.custom(lens, 32, 8, 128, dtype=torch.bfloat16, seed=78, write_all=True)
     _run(oracle_mod, w)
+
+
+def test_prefill_batch_invariance():
+    """A sequence's prefill output does not depend on the rest of the batch or
+    on the launch order: the chunked-prefill mix (3,328 workgroups, ranked
+    longest first) against four of its sequences run alone (few workgroups,
+    launched in index order), bit for bit."""
+    from tests.gpu_helpers import sub_workload
+    w = wl.chunked_prefill(device="cuda")
+    header("prefill batch invariance")
+    t = to_dev(w)
+    c = gpu_cache(w)
+    gpu_write(w, t, c, "all")
+    out = gpu_attention(w, t, c)
+    cuq = w.cu_seqlens_q().tolist()
+    for b in (0, 4, 7, 19):  # (query lengths 20, 372, 114, 4: all prefill rows)
+        ws = sub_workload(w, [b])
+        ts = to_dev(ws)
+        o1 = gpu_attention(ws, ts, c)  # same cache ids, one sequence
+        torch.cuda.synchronize()
+        assert torch.equal(o1, out[cuq[b]:cuq[b + 1]]), f"sequence {b}"
