@@ -55,6 +55,11 @@ __global__ __launch_bounds__(256) void write_kernel(
   // sign bits of the lane's E elements, as flips of 16-bit pairs
   uint32_t flip[E / 2];
   row_flips<E>(signs, sub, flip);
+  // kept in registers: left visible, the compiler re-derives them from the
+  // signs inside the row loop (reloading the signs and redoing the sign tests
+  // for every pair of rows)
+#pragma unroll
+  for (int p = 0; p < E / 2; ++p) flip[p] = opaque(flip[p]);
 
   // Row coordinates, slot and raw 16-bit inputs of one row.  Rows are
   // software-pipelined in two buffers that take turns (the loads of one row
