@@ -55,6 +55,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 4.0f;  // headroom of the softmax reference maximum (log2 units)
+// the reference of a row that has seen no key: finite, so such a row (or a key
+// group that got only masked keys) gives p = 2^(-inf) = 0, never 2^(-inf + inf)
+constexpr float kNoRef = -1e30f;
 constexpr int kStages = 8;
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -406,16 +409,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     for (int i = 0; i < NIB; ++i) dma4(p, goff[i], sb + (uint32_t)i * 256);
   };
 
-  float m_run[2][4], thr[2][4], l_run[2][4], corr[2][4];
+  float m_run[2][4], l_run[2][4], corr[2][4];
+  bool all_ref = false;  // every row of the wave holds a reference (uniform)
   float4_t oacc[2][NCOL];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      // a finite floor instead of -inf: a row that has seen no key (or a group
-      // that got only masked keys) then gives p = 0, never 2^(-inf + inf)
-      m_run[i][v] = -1e30f;
-      thr[i][v] = -1e30f;
+      m_run[i][v] = kNoRef;
       l_run[i][v] = 0.f;
       corr[i][v] = 0.f;
     }
@@ -578,62 +579,97 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       sV[n] = as_float((Q8 || Q2) ? vw[n] : vw[n] & 0xFFFFFFF0u);
       zV[n] = Q8 ? 128.f : Q2 ? 0.f : (float)(vw[n] & 0xFu);
     }
-    // logits in base-2 units; the reference maximum m of a row only moves
-    // when a logit exceeds it by more than kLazy (so p = 2^(z - m) <= 2^kLazy),
-    // which is detected per logit against thr = m + kLazy; the row maxima are
-    // only reduced on the rare tiles where that happens
+    // logits in base-2 units, kept relative to the row's reference m:
+    // d = z - m.  m only moves when a logit exceeds it by more than kLazy (so
+    // p = 2^d <= 2^kLazy), and the row maxima are only reduced on the rare
+    // tiles where that happens.  Once every row holds a reference, d is one
+    // fma per logit from the score; while some row has none yet (its first
+    // keys) and under a soft cap, the logit is formed first.
     float z[2][4][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) z[i][v][n] = fmaf(-zK[n], qsum[i][v], sacc[i][n][v]) * sKc[n];
-    if (cap2 > 0.f) {  // uniform: soft cap before the mask, so masked keys stay -inf
+    auto mask_all = [&]() {  // the causal / window mask
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int n = 0; n < 2; ++n) z[i][v][n] = soft_cap(z[i][v][n], cap2, inv_cap2);
-    }
-    bool over = false;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          float zz = z[i][v][n];
-          if (masked) {
+          for (int n = 0; n < 2; ++n) {
             const int key = 32 * t + 16 * n + col;
-            zz = (key <= pos[i][v] && (window <= 0 || key > pos[i][v] - window)) ? zz : -INFINITY;
+            const bool in = key <= pos[i][v] && (window <= 0 || key > pos[i][v] - window);
+            z[i][v][n] = in ? z[i][v][n] : -INFINITY;
           }
-          z[i][v][n] = zz;
-          over |= zz > thr[i][v];
-        }
-    if (__any(over)) {  // bring l, corr and O to the new references first
+    };
+    if (!all_ref || cap2 > 0.f) {  // uniform
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) z[i][v][n] = fmaf(-zK[n], qsum[i][v], sacc[i][n][v]) * sKc[n];
+      if (cap2 > 0.f) {  // soft cap before the mask, so masked keys stay -inf
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) z[i][v][n] = soft_cap(z[i][v][n], cap2, inv_cap2);
+      }
+      if (masked) mask_all();
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
+          // a row without a reference takes its maximum as one (its l, corr
+          // and O are still zero); one whose keys are all masked keeps none
           const float tmax = max16(fmaxf(z[i][v][0], z[i][v][1]));
-          const bool up = tmax > thr[i][v];
-          const float alpha = up ? __builtin_amdgcn_exp2f(m_run[i][v] - tmax) : 1.0f;
-          m_run[i][v] = up ? tmax : m_run[i][v];
-          thr[i][v] = m_run[i][v] + kLazy;
+          if (m_run[i][v] == kNoRef && tmax > kNoRef) m_run[i][v] = tmax;
+          z[i][v][0] -= m_run[i][v];
+          z[i][v][1] -= m_run[i][v];
+        }
+      bool none = false;  // a row of this wave still without a reference
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) none |= m_run[i][v] == kNoRef;
+      all_ref = !__any(none);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            z[i][v][n] = fmaf(fmaf(-zK[n], qsum[i][v], sacc[i][n][v]), sKc[n], -m_run[i][v]);
+      if (masked) mask_all();
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, fmaxf(z[i][v][0], z[i][v][1]));
+    if (__any(mx > kLazy)) {  // move the references of the rows that outgrew theirs
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float dmax = max16(fmaxf(z[i][v][0], z[i][v][1]));
+          const float mnew = dmax > kLazy ? m_run[i][v] + dmax : m_run[i][v];
+          const float shift = mnew - m_run[i][v];  // 0 for a row that keeps its reference
+          const float alpha = __builtin_amdgcn_exp2f(-shift);
+          m_run[i][v] = mnew;
           l_run[i][v] *= alpha;
           corr[i][v] *= alpha;
 #pragma unroll
           for (int c = 0; c < NCOL; ++c) oacc[i][c][v] *= alpha;
+          z[i][v][0] -= shift;
+          z[i][v][1] -= shift;
         }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p0 = __builtin_amdgcn_exp2f(z[i][v][0] - m_run[i][v]);
-        const float p1 = __builtin_amdgcn_exp2f(z[i][v][1] - m_run[i][v]);
+        const float p0 = __builtin_amdgcn_exp2f(z[i][v][0]);
+        const float p1 = __builtin_amdgcn_exp2f(z[i][v][1]);
         const float w0 = p0 * sV[0], w1 = p1 * sV[1];
         half2_t wh, wl;  // W = p sV as f16 hi + lo (22 significant bits)
         wh[0] = (_Float16)w0;
