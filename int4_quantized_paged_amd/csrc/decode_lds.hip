@@ -642,18 +642,27 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
       const float zK = Q8 ? 0.f : Q2 ? kLmB : (float)(cw.kw[n] & 0xFu);
       sV[n] = kval[n] ? as_float((Q8 || Q2) ? cw.vw[n] : cw.vw[n] & 0xFFFFFFF0u) : 0.f;  // masked: 0
       zV[n] = Q8 ? 128.f : Q2 ? 0.f : (float)(cw.vw[n] & 0xFu);
-      const uint32_t keep = kval[n] ? 0xFFFFFFFFu : 0u;
-      const uint32_t ninf = kval[n] ? 0u : 0xFF800000u;
 #pragma unroll
       for (int v = 0; v < RPG; ++v) {
         const float sf = fmaf((float)acc[n][2][v], 65536.0f,
                               (float)((acc[n][1][v] << 8) + acc[n][0][v]));
         const float tt = fmaf(-zK, qsf[v], sf);  // sum_i q_i (code_i - zp)
-        float zz = tt * (sK * c0[v]);
-        if (cap2 > 0.f) zz = soft_cap(zz, cap2, inv_cap2);  // uniform
-        // masked keys become -inf through a bitwise select (never a branch)
-        z[v][n] = as_float(and_or(as_uint(zz), keep, ninf));
+        z[v][n] = tt * (sK * c0[v]);
       }
+    }
+    if (cap2 > 0.f) {  // uniform; one branch for the tile
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int v = 0; v < RPG; ++v) z[v][n] = soft_cap(z[v][n], cap2, inv_cap2);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      // masked keys become -inf through a bitwise select (never a branch)
+      const uint32_t keep = kval[n] ? 0xFFFFFFFFu : 0u;
+      const uint32_t ninf = kval[n] ? 0u : 0xFF800000u;
+#pragma unroll
+      for (int v = 0; v < RPG; ++v) z[v][n] = as_float(and_or(as_uint(z[v][n]), keep, ninf));
     }
     phase_end(0, kb, nxt);
 
