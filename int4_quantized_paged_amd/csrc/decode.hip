@@ -284,7 +284,7 @@ __global__ __launch_bounds__(512) void decode_kernel(
   #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int key = tb * kBlockSize + 16 * n + col;
-        kval[n] = (tb + n < b1) && key < L && key >= lo;
+        kval[n] = (tb + n < b1) & (key < L) & (key >= lo);  // no short circuit: no branch
         sK[n] = as_float(cur.ks[n] & 0xFFFFFFF0u);
         zK[n] = (float)(cur.ks[n] & 0xFu);
         sV[n] = as_float(cur.vs[n] & 0xFFFFFFF0u);

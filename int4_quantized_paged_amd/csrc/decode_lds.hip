@@ -632,7 +632,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_lds_kernel(
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int key = tb * kBlockSize + 16 * n + col;
-      kval[n] = (tb + n < b1) && key < L && key >= lo;
+      kval[n] = (tb + n < b1) & (key < L) & (key >= lo);  // no short circuit: no branch
       // INT4: zero point in the scale word's low 4 bits; INT8: a plain fp32
       // scale, no K zero point, and V codes offset by 128 (see the V operands)
       // INT2: plain fp32 scales; the score planes give sum q (level + b), so
