@@ -476,7 +476,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     load_id(t0 + 2 * (kPairs - 1) + kg);
   }
 
-  for (int sidx = 0; sidx < nsteps; ++sidx) {
+  // One step of the key group.  `fastc`: every row of the wave holds a
+  // reference maximum and there is no soft cap, so the logits enter the
+  // softmax in one fused step; the steps before that (the rows' first keys)
+  // and all steps under a soft cap take the general path.  The two kinds of
+  // step are separate loops, so neither carries the other's registers.
+  auto step = [&](const int sidx, auto fastc) {
+    constexpr bool kFast = decltype(fastc)::value;
     const int t = t0 + 2 * sidx + kg;
     wait_vmem<(kPairs - 2) * NIB>();  // this wave's copies of tile t have landed
     __syncthreads();                  // ... and everyone's; everyone is done with step s-1
@@ -598,7 +604,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
             z[i][v][n] = in ? z[i][v][n] : -INFINITY;
           }
     };
-    if (!all_ref || cap2 > 0.f) {  // uniform
+    if constexpr (!kFast) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -771,7 +777,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         oacc[i][2 * bb] += tl;
       }
     }
-  }
+  };
+  int sidx = 0;
+  for (; sidx < nsteps && (!all_ref || cap2 > 0.f); ++sidx) step(sidx, std::false_type{});
+  for (; sidx < nsteps; ++sidx) step(sidx, std::true_type{});
   wait_vmem<0>();  // drain the clamped look-ahead copies
 
   // ---- merge the odd-tile group into the even one (same rows, wave q + 4 ->
