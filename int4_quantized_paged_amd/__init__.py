@@ -23,7 +23,7 @@ __all__ = [
     "int4kv_decode_num_segments", "NOALLOC_SCRATCH_BYTES",
     "int4kv_cache_bytes", "int4kv_status_string",
     "int4kv_last_error", "Int4KVError", "cache_shape", "empty_cache", "segment_buffers",
-    "library_path", "load_library", "int4kv_stream_rw", "int4kv_stream_blocks",
+    "library_path", "load_library", "int4kv_stream_rw", "int4kv_stream_blocks", "DecodeStepPlan",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -443,19 +443,12 @@ def int2_paged_attention(q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: 
     return out
 
 
-def int4_decode_step(key_new: torch.Tensor, value_new: torch.Tensor, slot_mapping: torch.Tensor,
-                     q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
-                     seqused_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
-                     block_table: torch.Tensor, softmax_scale: float, rht_signs: torch.Tensor,
-                     out: torch.Tensor | None = None, num_segments: int = 1,
-                     segm_output: torch.Tensor | None = None,
-                     segm_max: torch.Tensor | None = None,
-                     segm_expsum: torch.Tensor | None = None,
-                     sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
-    """``int4_kv_write`` of one new token per sequence (``key_new``/``value_new``
-    [S, Hkv, d], token b is sequence b's last key, at ``slot_mapping[b]``), then
-    ``int4_paged_attention``; one launch on the decode path.  Returns ``out``."""
-    lib = load_library()
+def _decode_step_args(key_new, value_new, slot_mapping, q, kv_cache, cu_seqlens_q, seqused_k,
+                      max_seqlen_q, max_seqlen_k, block_table, softmax_scale, rht_signs,
+                      out=None, num_segments=1, segm_output=None, segm_max=None,
+                      segm_expsum=None, sliding_window=0, softcap=0.0):
+    """Checks int4_decode_step's arguments; returns the C call's arguments
+    without the stream, and ``out``."""
     S = seqused_k.shape[0]
     if key_new.dim() != 3 or value_new.shape != key_new.shape or key_new.shape[0] != S:
         raise ValueError("key_new and value_new must both be [S, Hkv, d], one token per sequence")
@@ -482,12 +475,62 @@ def int4_decode_step(key_new: torch.Tensor, value_new: torch.Tensor, slot_mappin
             raise ValueError(f"{name} must be int32")
     if block_table.dim() != 2 or block_table.stride(1) != 1:
         raise ValueError("block_table must be [S, max_blocks] with unit column stride")
-    _check(lib.int4_decode_step(
-        _ptr(key_new), key_new.stride(0), _ptr(value_new), value_new.stride(0),
-        _ptr(slot_mapping.contiguous()), _ptr(q), q.stride(0), _ptr(out), _dtype_code(q.dtype),
-        _ptr(kv_cache), nb, bs, hkv, d, hq, _ptr(cu_seqlens_q.contiguous()),
-        _ptr(seqused_k.contiguous()), S, int(max_seqlen_q), int(max_seqlen_k), _ptr(block_table),
-        block_table.stride(0), float(softmax_scale), int(sliding_window), float(softcap),
-        _ptr(rht_signs.contiguous()), int(num_segments), _ptr(segm_output), _ptr(segm_max),
-        _ptr(segm_expsum), _stream(q.device)))
+    args = (_ptr(key_new), key_new.stride(0), _ptr(value_new), value_new.stride(0),
+            _ptr(slot_mapping.contiguous()), _ptr(q), q.stride(0), _ptr(out),
+            _dtype_code(q.dtype), _ptr(kv_cache), nb, bs, hkv, d, hq,
+            _ptr(cu_seqlens_q.contiguous()), _ptr(seqused_k.contiguous()), S, int(max_seqlen_q),
+            int(max_seqlen_k), _ptr(block_table), block_table.stride(0), float(softmax_scale),
+            int(sliding_window), float(softcap), _ptr(rht_signs.contiguous()), int(num_segments),
+            _ptr(segm_output), _ptr(segm_max), _ptr(segm_expsum))
+    return args, out
+
+
+def int4_decode_step(key_new: torch.Tensor, value_new: torch.Tensor, slot_mapping: torch.Tensor,
+                     q: torch.Tensor, kv_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                     seqused_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                     block_table: torch.Tensor, softmax_scale: float, rht_signs: torch.Tensor,
+                     out: torch.Tensor | None = None, num_segments: int = 1,
+                     segm_output: torch.Tensor | None = None,
+                     segm_max: torch.Tensor | None = None,
+                     segm_expsum: torch.Tensor | None = None,
+                     sliding_window: int = 0, softcap: float = 0.0) -> torch.Tensor:
+    """``int4_kv_write`` of one new token per sequence (``key_new``/``value_new``
+    [S, Hkv, d], token b is sequence b's last key, at ``slot_mapping[b]``), then
+    ``int4_paged_attention``; one launch on the decode path.  Returns ``out``."""
+    args, out = _decode_step_args(key_new, value_new, slot_mapping, q, kv_cache, cu_seqlens_q,
+                                  seqused_k, max_seqlen_q, max_seqlen_k, block_table,
+                                  softmax_scale, rht_signs, out, num_segments, segm_output,
+                                  segm_max, segm_expsum, sliding_window, softcap)
+    _check(load_library().int4_decode_step(*args, _stream(q.device)))
     return out
+
+
+class DecodeStepPlan:
+    """``int4_decode_step`` with its arguments checked and converted once, for
+    a loop that runs the same step on the same buffers again and again (their
+    contents change between calls; their storage, shapes and the other
+    arguments do not).  Calling the plan launches the step on the current
+    stream of the query's device and returns ``out``; the result is the plain
+    call's, bit for bit.  The plan keeps its tensors alive."""
+
+    def __init__(self, key_new, value_new, slot_mapping, q, kv_cache, cu_seqlens_q, seqused_k,
+                 max_seqlen_q, max_seqlen_k, block_table, softmax_scale, rht_signs, out=None,
+                 num_segments=1, segm_output=None, segm_max=None, segm_expsum=None,
+                 sliding_window=0, softcap=0.0):
+        slot_mapping, cu_seqlens_q, seqused_k, rht_signs = (
+            t.contiguous() for t in (slot_mapping, cu_seqlens_q, seqused_k, rht_signs))
+        args, out = _decode_step_args(key_new, value_new, slot_mapping, q, kv_cache,
+                                      cu_seqlens_q, seqused_k, max_seqlen_q, max_seqlen_k,
+                                      block_table, softmax_scale, rht_signs, out, num_segments,
+                                      segm_output, segm_max, segm_expsum, sliding_window,
+                                      softcap)
+        self._fn = load_library().int4_decode_step
+        self._args = tuple(ty(v) for ty, v in zip(self._fn.argtypes, args))
+        self._keep = (key_new, value_new, slot_mapping, q, kv_cache, cu_seqlens_q, seqused_k,
+                      block_table, rht_signs, segm_output, segm_max, segm_expsum)
+        self._device = q.device
+        self.out = out
+
+    def __call__(self) -> torch.Tensor:
+        _check(self._fn(*self._args, torch.cuda.current_stream(self._device).cuda_stream))
+        return self.out

@@ -126,3 +126,46 @@ def test_decode_step_serving_batch(oracle_mod):
     ws = sub_workload(w, picks)
     ref = oracle_attention(oracle_mod, ws, oracle_cache(oracle_mod, ws, "all"))
     assert_attention_close(out[picks], ref, "serving batch, sampled sequences")
+
+
+def test_decode_step_plan_matches_plain_call(oracle_mod):
+    """DecodeStepPlan (arguments checked once) launches the same step: the
+    same cache bytes and output bits as int4_decode_step, on repeated calls,
+    after the buffers' contents change, and on a non-default stream."""
+    w = wl.custom(LENS, 64, 8, 128, seed=9)
+    t = to_dev(w)
+    base, kn, vn, slots = _split(w, t)
+    ns = 8
+    segs = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns, w.head_size, device="cuda")
+    ca, cb = base.clone(), base.clone()
+    out_a, out_b = torch.empty_like(t["query"]), torch.empty_like(t["query"])
+    plan = ik.DecodeStepPlan(kn, vn, slots, t["query"], cb, t["cu"], t["su"], w.max_seqlen_q,
+                             w.max_seqlen_k, t["block_table"], w.softmax_scale, t["signs"],
+                             out=out_b, num_segments=ns, segm_output=segs[0], segm_max=segs[1],
+                             segm_expsum=segs[2])
+    segs_a = ik.segment_buffers(w.num_seqs, w.num_q_heads, ns, w.head_size, device="cuda")
+
+    def plain():
+        ik.int4_decode_step(kn, vn, slots, t["query"], ca, t["cu"], t["su"], w.max_seqlen_q,
+                            w.max_seqlen_k, t["block_table"], w.softmax_scale, t["signs"],
+                            out=out_a, num_segments=ns, segm_output=segs_a[0],
+                            segm_max=segs_a[1], segm_expsum=segs_a[2])
+    for rnd in range(3):
+        header(f"decode step plan, round {rnd}")
+        if rnd == 1:  # new contents in the same buffers
+            t["query"].mul_(-0.5)
+            kn.mul_(2.0)
+            vn.add_(0.25)
+        if rnd == 2:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                plain()
+                assert plan() is out_b
+            torch.cuda.current_stream().wait_stream(s)
+        else:
+            plain()
+            assert plan() is out_b
+        torch.cuda.synchronize()
+        assert torch.equal(ca, cb), "cache bytes differ from the plain call"
+        assert torch.equal(out_a, out_b), "output differs from the plain call"
