@@ -324,3 +324,49 @@ def test_stream_blocks_rejects_invalid_host_arguments(args):
 
 def test_stream_blocks_empty_is_a_no_op():
     assert ik.load_library().int4kv_stream_blocks(None, 17408, None, 0, 4, None) == 0
+
+
+def _plan_inputs(S=4, hkv=8, d=128, hq=32, nblk=8):
+    import torch
+    bf = torch.bfloat16
+    return dict(key_new=torch.zeros(S, hkv, d, dtype=bf), value_new=torch.zeros(S, hkv, d, dtype=bf),
+                slot_mapping=torch.zeros(S, dtype=torch.int64), q=torch.zeros(S, hq, d, dtype=bf),
+                kv_cache=torch.zeros(S * nblk, 2, 16, hkv, d // 2 + 4, dtype=torch.uint8),
+                cu_seqlens_q=torch.arange(S + 1, dtype=torch.int32),
+                seqused_k=torch.full((S,), 100, dtype=torch.int32), max_seqlen_q=1,
+                max_seqlen_k=100, block_table=torch.zeros(S, nblk, dtype=torch.int32),
+                softmax_scale=0.088, rht_signs=torch.ones(d))
+
+
+def test_decode_step_plan_converts_arguments_once():
+    """DecodeStepPlan checks and converts its arguments at construction (host
+    only: nothing is launched here): the C argument tuple has one value per
+    declared argument but the stream, and ``out`` is allocated like q."""
+    kw = _plan_inputs()
+    plan = ik.DecodeStepPlan(**kw)
+    lib = ik.load_library()
+    assert len(plan._args) == len(lib.int4_decode_step.argtypes) - 1
+    assert plan.out.shape == kw["q"].shape and plan.out.dtype == kw["q"].dtype
+    assert plan._args[0].value == kw["key_new"].data_ptr()
+
+
+@pytest.mark.parametrize("bad", [
+    dict(slot_mapping="int32"), dict(key_new="3 tokens"), dict(block_table="int64"),
+    dict(kv_cache="float"),
+])
+def test_decode_step_plan_rejects_what_the_plain_call_rejects(bad):
+    import torch
+    kw = _plan_inputs()
+    (k, v), = bad.items()
+    if k == "slot_mapping":
+        kw[k] = kw[k].to(torch.int32)
+    elif k == "key_new":
+        kw[k] = kw[k][:3]
+    elif k == "block_table":
+        kw[k] = kw[k].to(torch.int64)
+    else:
+        kw[k] = kw[k].float()
+    with pytest.raises(ValueError):
+        ik.DecodeStepPlan(**kw)
+    with pytest.raises(ValueError):
+        ik.int4_decode_step(**kw)
